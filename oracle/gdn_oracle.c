@@ -1,0 +1,438 @@
+/*
+ * gdn_oracle.c -- plain, slow, fp64 CPU oracle for the chunk-wise Gated DeltaNet
+ * intra-chunk solve.  TEST INFRASTRUCTURE ONLY: it exists so that tests, the smoke
+ * check and the CPU-baseline leg of the benchmark can check the GPU library against
+ * an independent computation.  The GPU library never links, loads or calls it, and
+ * it shares no code, header or table with the GPU library.
+ *
+ * Sources cited below (titles of the pages the method is taken from):
+ *   [GEO]  "When Good Enough Is Optimal: Multiplication-Only Matrix Inversion
+ *           Approximation for Quantized Gated DeltaNet" (technical summary, gist.science,
+ *           arXiv 2606.06034).  Sections: "Enonce du Probleme" (problem statement),
+ *           "Methodologie" SS1 (truncated low-order Neumann), SS2 (structural diagonal
+ *           mask), SS3 (parallel residual correction), "Adaptation a la Quantification".
+ *   [PSDA] "A Persistent-State Dataflow Accelerator for Memory-Bound Linear Attention
+ *           Decode on FPGA" (technical summary, gist.science, arXiv 2603.05931),
+ *           section 2.B (five-phase fused decode pipeline over the recurrent state).
+ *   The formula for A, the exact doubling product and the WY products are not printed
+ *   on those pages; they follow from the gated delta rule and are written out here
+ *   from the mathematics (each function says which reading it takes).
+ *
+ * Conventions: every matrix is dense row-major fp64; a "block" is one C x C chunk
+ * of one (batch, head).  Everything is computed with plain triple loops, with no
+ * blocking, fusion or reordering beyond what the definition states.  OpenMP only
+ * splits independent blocks / heads across threads; each block's arithmetic is
+ * sequential and identical whatever the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_version(void) { return 1; }
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* ---- small dense helpers (row-major, n x n unless stated) -------------------- */
+
+static void mat_identity(int n, double* X) {
+  memset(X, 0, sizeof(double) * (size_t)n * n);
+  for (int i = 0; i < n; ++i) X[(size_t)i * n + i] = 1.0;
+}
+
+/* Z = X * Y, all n x n.  Z must not alias X or Y. */
+static void mat_mul(int n, const double* X, const double* Y, double* Z) {
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < n; ++j) {
+      double s = 0.0;
+      for (int k = 0; k < n; ++k) s += X[(size_t)i * n + k] * Y[(size_t)k * n + j];
+      Z[(size_t)i * n + j] = s;
+    }
+}
+
+/* in-chunk gate: G_r = sum_{s<=r} gamma_s, restarting at every chunk start
+ * (reading: per-token log-gates gamma, cumulated inside the chunk only; the decay
+ * across chunks is carried by the state).  If g_cumulative, g is already G. */
+static void chunk_cumsum(int C, const double* g, int g_cumulative, double* G) {
+  double acc = 0.0;
+  for (int r = 0; r < C; ++r) {
+    if (g_cumulative) {
+      G[r] = g[r];
+    } else {
+      acc += g[r];
+      G[r] = acc;
+    }
+  }
+}
+
+/* ---- O2: A = -tril(diag(beta) (K K^T .* exp(G_i - G_j)), -1) ------------------
+ * [GEO] Enonce du Probleme: A is strictly lower-triangular; the entries are the
+ * gated delta rule's key interactions inside one chunk.
+ * K: [nb][C][dk], beta, g: [nb][C], A: [nb][C][C]. */
+void oracle_build_A(int64_t nb, int C, int dk, const double* K, const double* beta,
+                    const double* g, int g_cumulative, double* A) {
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < nb; ++b) {
+    const double* Kb = K + (size_t)b * C * dk;
+    const double* bb = beta + (size_t)b * C;
+    double* Ab = A + (size_t)b * C * C;
+    double* G = (double*)malloc(sizeof(double) * C);
+    chunk_cumsum(C, g + (size_t)b * C, g_cumulative, G);
+    for (int i = 0; i < C; ++i)
+      for (int j = 0; j < C; ++j) {
+        double v = 0.0;
+        if (i > j) {
+          double kk = 0.0;
+          for (int d = 0; d < dk; ++d) kk += Kb[(size_t)i * dk + d] * Kb[(size_t)j * dk + d];
+          v = -bb[i] * kk * exp(G[i] - G[j]);
+        }
+        Ab[(size_t)i * C + j] = v;
+      }
+    free(G);
+  }
+}
+
+/* ---- O3: forward substitution, the sequential baseline ----------------------
+ * [GEO] Enonce du Probleme: the traditional way to get T = (I - A)^-1 for a
+ * strictly lower A is forward substitution, k-1 dependent row steps.
+ * Row i of T = e_i + sum_{m<i} A_im * (row m of T). */
+void oracle_fs_inverse(int64_t nb, int C, const double* A, double* T) {
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < nb; ++b) {
+    const double* Ab = A + (size_t)b * C * C;
+    double* Tb = T + (size_t)b * C * C;
+    mat_identity(C, Tb);
+    for (int i = 1; i < C; ++i)
+      for (int m = 0; m < i; ++m) {
+        double a = Ab[(size_t)i * C + m];
+        for (int j = 0; j <= m; ++j) Tb[(size_t)i * C + j] += a * Tb[(size_t)m * C + j];
+      }
+  }
+}
+
+/* structural diagonal mask M^(N): keep entry (i,j) iff i - j <= N.
+ * [GEO] Methodologie SS2.  Entries above the diagonal (i - j < 0) are kept as they
+ * are (they are zero for every lower-triangular operand used here). */
+static void apply_band_mask(int C, int N, double* X) {
+  for (int i = 0; i < C; ++i)
+    for (int j = 0; j < C; ++j)
+      if (i - j > N) X[(size_t)i * C + j] = 0.0;
+}
+
+/* ---- O4a/O4b: truncated low-order Neumann sum, Horner form, optional mask ----
+ * [GEO] Methodologie SS1: T(0) = sum_{n=0}^{N} A^n.  Evaluated as
+ *   H_1 = I + A,  H_{k+1} = I + A H_k  (k = 1..N-1),  T(0) = H_N,
+ * i.e. N-1 matrix products.  N = 0 gives T = I.
+ * [GEO] Methodologie SS2: with mask != 0 the result is M^(N) .* T(0).  The mask is
+ * applied to the final sum only (masking A or the intermediates as well gives the
+ * same result, because every lower-triangular product's band entries depend only
+ * on band entries). */
+void oracle_neumann(int64_t nb, int C, const double* A, int N, int mask, double* T) {
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < nb; ++b) {
+    const double* Ab = A + (size_t)b * C * C;
+    double* Tb = T + (size_t)b * C * C;
+    double* H = (double*)malloc(sizeof(double) * C * C);
+    double* P = (double*)malloc(sizeof(double) * C * C);
+    mat_identity(C, H);
+    for (int k = 0; k < N; ++k) {
+      /* H <- I + A H  (first pass: H = I, so H <- I + A) */
+      mat_mul(C, Ab, H, P);
+      for (int i = 0; i < C; ++i)
+        for (int j = 0; j < C; ++j)
+          H[(size_t)i * C + j] = P[(size_t)i * C + j] + (i == j ? 1.0 : 0.0);
+    }
+    if (mask) apply_band_mask(C, N, H);
+    memcpy(Tb, H, sizeof(double) * C * C);
+    free(H);
+    free(P);
+  }
+}
+
+/* ---- O5: exact multiplication-only doubling product --------------------------
+ * T = prod_{i=0}^{m-1} (I + A^(2^i)),  m = ceil(log2 C).
+ * Valid because A is nilpotent: by Lemma 3.1 of [GEO] (Methodologie SS1), A^n is
+ * zero above its n-th subdiagonal, so A^C = 0 and the telescoping product
+ * (I - A) prod (I + A^(2^i)) = I - A^(2^m) equals I once 2^m >= C.
+ * Evaluated as P = I, X = A; repeat m times: P <- P (I + X), X <- X X. */
+void oracle_doubling(int64_t nb, int C, const double* A, double* T) {
+  int m = 0;
+  while ((1 << m) < C) ++m;
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < nb; ++b) {
+    const double* Ab = A + (size_t)b * C * C;
+    double* Tb = T + (size_t)b * C * C;
+    double* P = (double*)malloc(sizeof(double) * C * C);
+    double* X = (double*)malloc(sizeof(double) * C * C);
+    double* Y = (double*)malloc(sizeof(double) * C * C);
+    double* Z = (double*)malloc(sizeof(double) * C * C);
+    mat_identity(C, P);
+    memcpy(X, Ab, sizeof(double) * C * C);
+    for (int it = 0; it < m; ++it) {
+      /* Y = I + X;  Z = P Y;  P = Z */
+      for (size_t e = 0; e < (size_t)C * C; ++e) Y[e] = X[e];
+      for (int i = 0; i < C; ++i) Y[(size_t)i * C + i] += 1.0;
+      mat_mul(C, P, Y, Z);
+      memcpy(P, Z, sizeof(double) * C * C);
+      /* X = X X */
+      mat_mul(C, X, X, Z);
+      memcpy(X, Z, sizeof(double) * C * C);
+    }
+    memcpy(Tb, P, sizeof(double) * C * C);
+    free(P);
+    free(X);
+    free(Y);
+    free(Z);
+  }
+}
+
+/* ---- O5': parallel residual correction ---------------------------------------
+ * [GEO] Methodologie SS3: with T(0) the (masked) truncated sum,
+ *   E = I - (I - A) T(0),   T ~= T(0) * sum_{s=0}^{S} E^s.
+ * The sum of powers of E is taken in Horner form R = I + E (I + E (... )). */
+void oracle_residual(int64_t nb, int C, const double* A, int N, int mask, int S,
+                     double* T) {
+  double* T0 = (double*)malloc(sizeof(double) * (size_t)nb * C * C);
+  oracle_neumann(nb, C, A, N, mask, T0);
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < nb; ++b) {
+    const double* Ab = A + (size_t)b * C * C;
+    const double* T0b = T0 + (size_t)b * C * C;
+    double* Tb = T + (size_t)b * C * C;
+    double* IA = (double*)malloc(sizeof(double) * C * C);
+    double* E = (double*)malloc(sizeof(double) * C * C);
+    double* R = (double*)malloc(sizeof(double) * C * C);
+    double* Z = (double*)malloc(sizeof(double) * C * C);
+    for (int i = 0; i < C; ++i)
+      for (int j = 0; j < C; ++j)
+        IA[(size_t)i * C + j] = (i == j ? 1.0 : 0.0) - Ab[(size_t)i * C + j];
+    mat_mul(C, IA, T0b, Z);
+    for (int i = 0; i < C; ++i)
+      for (int j = 0; j < C; ++j)
+        E[(size_t)i * C + j] = (i == j ? 1.0 : 0.0) - Z[(size_t)i * C + j];
+    mat_identity(C, R);
+    for (int s = 0; s < S; ++s) {
+      mat_mul(C, E, R, Z);
+      for (int i = 0; i < C; ++i)
+        for (int j = 0; j < C; ++j)
+          R[(size_t)i * C + j] = Z[(size_t)i * C + j] + (i == j ? 1.0 : 0.0);
+    }
+    mat_mul(C, T0b, R, Tb);
+    free(IA);
+    free(E);
+    free(R);
+    free(Z);
+  }
+  free(T0);
+}
+
+/* ---- O6 (first half): WY products -------------------------------------------
+ * W = T diag(s) K,  U = T diag(beta) V, per block.
+ * gate_k = 0: s = beta (the stand-alone WY form);
+ * gate_k = 1: s = beta .* exp(G) (the form the chunk recurrence needs with a gated A:
+ *             A = D Ahat D^-1 with D = diag(exp(G)), so the state correction picks
+ *             up the gate on the key side).
+ * T: [nb][C][C], K: [nb][C][dk], V: [nb][C][dv], W: [nb][C][dk], U: [nb][C][dv]. */
+void oracle_wy(int64_t nb, int C, int dk, int dv, const double* T, const double* K,
+               const double* V, const double* beta, const double* g, int g_cumulative,
+               int gate_k, double* W, double* U) {
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < nb; ++b) {
+    const double* Tb = T + (size_t)b * C * C;
+    const double* Kb = K + (size_t)b * C * dk;
+    const double* Vb = V + (size_t)b * C * dv;
+    const double* bb = beta + (size_t)b * C;
+    double* Wb = W + (size_t)b * C * dk;
+    double* Ub = U + (size_t)b * C * dv;
+    double* G = (double*)malloc(sizeof(double) * C);
+    chunk_cumsum(C, g + (size_t)b * C, g_cumulative, G);
+    for (int i = 0; i < C; ++i) {
+      for (int d = 0; d < dk; ++d) {
+        double s = 0.0;
+        for (int m = 0; m < C; ++m) {
+          double sk = bb[m] * (gate_k ? exp(G[m]) : 1.0);
+          s += Tb[(size_t)i * C + m] * sk * Kb[(size_t)m * dk + d];
+        }
+        Wb[(size_t)i * dk + d] = s;
+      }
+      for (int e = 0; e < dv; ++e) {
+        double s = 0.0;
+        for (int m = 0; m < C; ++m) s += Tb[(size_t)i * C + m] * bb[m] * Vb[(size_t)m * dv + e];
+        Ub[(size_t)i * dv + e] = s;
+      }
+    }
+    free(G);
+  }
+}
+
+/* inverse of one block by the selected variant (see the functions above) */
+static void block_inverse(int C, const double* A, int inv_mode, int N, int mask,
+                          double* T) {
+  if (inv_mode == 1)
+    oracle_doubling(1, C, A, T);
+  else if (inv_mode == 2)
+    oracle_fs_inverse(1, C, A, T);
+  else
+    oracle_neumann(1, C, A, N, mask, T);
+}
+
+/* ---- O6: chunk-wise forward ----------------------------------------------------
+ * Per (b, h), chunks in order, state S (dk x dv) starting from S0 (zeros if NULL):
+ *   G  = in-chunk cumsum of the per-token log-gates
+ *   A  = -tril(diag(beta) (K K^T .* exp(G_i - G_j)), -1);  T = inverse variant of A
+ *   W  = T diag(beta .* exp(G)) K,   U = T diag(beta) V
+ *   U' = U - W S
+ *   O  = scale * ( diag(exp(G)) Q S + (Q K^T .* exp(G_i - G_j) .* [i >= j]) U' )
+ *   S  = exp(G_C) S + K^T diag(exp(G_C - G)) U'
+ * [GEO] Enonce du Probleme: the chunk-wise form needs T = (I - A)^-1 per chunk and
+ * keeps a fixed-size recurrent state across chunks.
+ * inv_mode: 0 = truncated Neumann (N, mask), 1 = exact doubling, 2 = forward
+ * substitution.  Layouts: Q, K [B][H][Tn][dk]; V, O [B][H][Tn][dv];
+ * beta, g [B][H][Tn]; S0, S_out [B][H][dk][dv].  Tn % C == 0. */
+void oracle_chunk_fwd(int Bn, int Hn, int64_t Tn, int dk, int dv, int C, const double* Q,
+                      const double* K, const double* V, const double* beta,
+                      const double* g, const double* S0, double scale, int inv_mode, int N,
+                      int mask, double* O, double* S_out) {
+  const int64_t nchunks = Tn / C;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bh = 0; bh < (int64_t)Bn * Hn; ++bh) {
+    const double* Qh = Q + (size_t)bh * Tn * dk;
+    const double* Kh = K + (size_t)bh * Tn * dk;
+    const double* Vh = V + (size_t)bh * Tn * dv;
+    const double* bh_beta = beta + (size_t)bh * Tn;
+    const double* bh_g = g + (size_t)bh * Tn;
+    double* Oh = O + (size_t)bh * Tn * dv;
+    double* S = (double*)malloc(sizeof(double) * dk * dv);
+    double* A = (double*)malloc(sizeof(double) * C * C);
+    double* T = (double*)malloc(sizeof(double) * C * C);
+    double* W = (double*)malloc(sizeof(double) * C * dk);
+    double* U = (double*)malloc(sizeof(double) * C * dv);
+    double* Up = (double*)malloc(sizeof(double) * C * dv);
+    double* G = (double*)malloc(sizeof(double) * C);
+    double* Snew = (double*)malloc(sizeof(double) * dk * dv);
+    if (S0)
+      memcpy(S, S0 + (size_t)bh * dk * dv, sizeof(double) * dk * dv);
+    else
+      memset(S, 0, sizeof(double) * dk * dv);
+    for (int64_t c = 0; c < nchunks; ++c) {
+      const double* Qc = Qh + (size_t)c * C * dk;
+      const double* Kc = Kh + (size_t)c * C * dk;
+      const double* Vc = Vh + (size_t)c * C * dv;
+      const double* bc = bh_beta + (size_t)c * C;
+      const double* gc = bh_g + (size_t)c * C;
+      double* Oc = Oh + (size_t)c * C * dv;
+      chunk_cumsum(C, gc, 0, G);
+      oracle_build_A(1, C, dk, Kc, bc, gc, 0, A);
+      block_inverse(C, A, inv_mode, N, mask, T);
+      oracle_wy(1, C, dk, dv, T, Kc, Vc, bc, gc, 0, 1, W, U);
+      /* U' = U - W S */
+      for (int i = 0; i < C; ++i)
+        for (int e = 0; e < dv; ++e) {
+          double s = 0.0;
+          for (int d = 0; d < dk; ++d) s += W[(size_t)i * dk + d] * S[(size_t)d * dv + e];
+          Up[(size_t)i * dv + e] = U[(size_t)i * dv + e] - s;
+        }
+      /* O = scale (diag(e^G) Q S + P U'),  P_ij = q_i.k_j e^{G_i - G_j} [i >= j] */
+      for (int i = 0; i < C; ++i)
+        for (int e = 0; e < dv; ++e) {
+          double qs = 0.0;
+          for (int d = 0; d < dk; ++d) qs += Qc[(size_t)i * dk + d] * S[(size_t)d * dv + e];
+          double pu = 0.0;
+          for (int j = 0; j <= i; ++j) {
+            double qk = 0.0;
+            for (int d = 0; d < dk; ++d) qk += Qc[(size_t)i * dk + d] * Kc[(size_t)j * dk + d];
+            pu += qk * exp(G[i] - G[j]) * Up[(size_t)j * dv + e];
+          }
+          Oc[(size_t)i * dv + e] = scale * (exp(G[i]) * qs + pu);
+        }
+      /* S = e^{G_C} S + K^T diag(e^{G_C - G}) U' */
+      const double GC = G[C - 1];
+      for (int d = 0; d < dk; ++d)
+        for (int e = 0; e < dv; ++e) {
+          double s = 0.0;
+          for (int j = 0; j < C; ++j)
+            s += Kc[(size_t)j * dk + d] * exp(GC - G[j]) * Up[(size_t)j * dv + e];
+          Snew[(size_t)d * dv + e] = exp(GC) * S[(size_t)d * dv + e] + s;
+        }
+      memcpy(S, Snew, sizeof(double) * dk * dv);
+    }
+    memcpy(S_out + (size_t)bh * dk * dv, S, sizeof(double) * dk * dv);
+    free(S);
+    free(A);
+    free(T);
+    free(W);
+    free(U);
+    free(Up);
+    free(G);
+    free(Snew);
+  }
+}
+
+/* ---- O7: token-by-token gated delta rule (brute force) -----------------------
+ * For t = 1..Tn, with a_t = exp(gamma_t):
+ *   S_t = a_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,   o_t = scale S_t^T q_t.
+ * Evaluated in the single-read form: r = S^T k, p = S^T q (one pass over S);
+ * u = beta (v - a r); S = a S + k u^T; o = scale (a p + (k . q) u).
+ * [PSDA] section 2.B describes the same split of one decode step: read the state
+ * once for retrieval and the partial output, apply the delta correction, write the
+ * state, then correct the output.  [GEO] Enonce du Probleme: fixed-size state. */
+void oracle_recurrence(int Bn, int Hn, int64_t Tn, int dk, int dv, const double* Q,
+                       const double* K, const double* V, const double* beta,
+                       const double* g, const double* S0, double scale, double* O,
+                       double* S_out) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bh = 0; bh < (int64_t)Bn * Hn; ++bh) {
+    double* S = (double*)malloc(sizeof(double) * dk * dv);
+    double* r = (double*)malloc(sizeof(double) * dv);
+    double* p = (double*)malloc(sizeof(double) * dv);
+    if (S0)
+      memcpy(S, S0 + (size_t)bh * dk * dv, sizeof(double) * dk * dv);
+    else
+      memset(S, 0, sizeof(double) * dk * dv);
+    for (int64_t t = 0; t < Tn; ++t) {
+      const double* q = Q + ((size_t)bh * Tn + t) * dk;
+      const double* k = K + ((size_t)bh * Tn + t) * dk;
+      const double* v = V + ((size_t)bh * Tn + t) * dv;
+      const double bt = beta[(size_t)bh * Tn + t];
+      const double a = exp(g[(size_t)bh * Tn + t]);
+      double kq = 0.0;
+      for (int d = 0; d < dk; ++d) kq += k[d] * q[d];
+      for (int e = 0; e < dv; ++e) {
+        double rs = 0.0, ps = 0.0;
+        for (int d = 0; d < dk; ++d) {
+          rs += S[(size_t)d * dv + e] * k[d];
+          ps += S[(size_t)d * dv + e] * q[d];
+        }
+        r[e] = rs;
+        p[e] = ps;
+      }
+      double* o = O + ((size_t)bh * Tn + t) * dv;
+      for (int e = 0; e < dv; ++e) {
+        const double u = bt * (v[e] - a * r[e]);
+        for (int d = 0; d < dk; ++d) S[(size_t)d * dv + e] = a * S[(size_t)d * dv + e] + k[d] * u;
+        o[e] = scale * (a * p[e] + kq * u);
+      }
+    }
+    memcpy(S_out + (size_t)bh * dk * dv, S, sizeof(double) * dk * dv);
+    free(S);
+    free(r);
+    free(p);
+  }
+}
