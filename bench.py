@@ -1,0 +1,254 @@
+"""Throughput of the GDN intra-chunk solve on one MI355X.
+
+Headline workload (one "step"): the batched 64x64 tri-inverse over B=1, H=16,
+seq 8192 -> 2048 blocks, bf16 keys (d_k = 128), fp32 beta and log-gates, A built in
+the kernel, T = band-masked truncated Neumann sum with N = 3 (the pages' method),
+T written as fp32.  value = 64x64 blocks per second.
+
+The same JSON line also carries the other inverse variants of that workload and, when
+the library has it, the full chunk-wise prefill forward (B=4, H=16, seq 8192,
+d_k = d_v = 128, C = 64) in tokens per second, each with its roofline.
+
+Inputs are seeded synthetic tensors (see synth/), resident in HBM before timing.
+Eight input/output buffer sets are rotated so that successive launches do not hit
+the 256 MB Infinity Cache.  Kernel durations come from HIP events recorded on the
+stream the kernels are launched on.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only c1|c3]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA
+N_SETS = 8
+
+
+def source_digest() -> str:
+    """Hash of the HIP sources: recorded next to counter-derived traffic figures so a
+    stale measurement is never reported for a changed kernel."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tri_inverse_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was taken
+    on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(kernel_key)
+    if not ent or ent.get("source_digest") != source_digest():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def time_launches(torch, launch, n_sets, steps, warmup):
+    """Run `launch(set_index)` `warmup` times eagerly, then capture exactly `steps`
+    launches (rotating buffer sets) in one HIP graph and time one replay with HIP
+    events on the replay stream.  Returns ms per step (= per launch).  Replaying a
+    graph keeps Python's per-call overhead out of the timed region, so back-to-back
+    kernels run without host-induced gaps."""
+    for i in range(warmup):
+        launch(i % n_sets)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for k in range(steps):
+            launch(k % n_sets)
+    graph.replay()  # untimed: first replay uploads the graph
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    graph.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    del graph
+    return ms, ms
+
+
+# ------------------------------------------------------------------ c1: tri-inverse
+
+C1 = dict(B=1, H=16, T=8192, C=64, d_k=128)
+
+
+def c1_bytes_flops(variant, t_bytes=4):
+    C, dk = C1["C"], C1["d_k"]
+    n_blocks = C1["B"] * C1["H"] * C1["T"] // C
+    per_block_bytes = C * dk * 2 + 2 * C * 4 + C * C * t_bytes
+    gram = 2 * C * C * dk
+    if variant[0] == "exact":
+        m = (C - 1).bit_length()
+        prods = 2 * (m - 1)
+    else:
+        prods = variant[1] - 1
+    flops = gram + prods * 2 * C ** 3
+    return n_blocks, n_blocks * per_block_bytes, n_blocks * flops
+
+
+def bench_c1(torch, tri, synth, steps, warmup):
+    C = C1["C"]
+    n_blocks = C1["B"] * C1["H"] * C1["T"] // C
+    sets = []
+    for s in range(N_SETS):
+        inp = synth.blocks(1 if s == 0 else 1000 + s, n_blocks, C, C1["d_k"], k_dtype="bf16")
+        sets.append({k: v.cuda() for k, v in inp.items()})
+    outs32 = [torch.empty((n_blocks, C, C), device="cuda") for _ in range(N_SETS)]
+    outs16 = [torch.empty((n_blocks, C, C), device="cuda", dtype=torch.bfloat16) for _ in range(N_SETS)]
+
+    def mk(variant, t_dtype):
+        outs = outs32 if t_dtype == torch.float32 else outs16
+
+        def launch(i):
+            x = sets[i]
+            if variant[0] == "exact":
+                tri.gdn_tri_inverse_exact(K=x["K"], beta=x["beta"], g=x["g"], C=C, compute="bf16",
+                                          out=outs[i])
+            else:
+                tri.gdn_tri_inverse_neumann(K=x["K"], beta=x["beta"], g=x["g"], C=C, N=variant[1],
+                                            mask=variant[2], compute="bf16", out=outs[i])
+        return launch
+
+    results = {}
+    variants = [("neumann", 3, True, torch.float32), ("neumann", 2, True, torch.float32),
+                ("neumann", 4, True, torch.float32), ("neumann", 2, False, torch.float32),
+                ("neumann", 3, False, torch.float32), ("neumann", 4, False, torch.float32),
+                ("exact", 0, False, torch.float32), ("exact", 0, False, torch.bfloat16),
+                ("neumann", 3, True, torch.bfloat16)]
+    for v in variants:
+        name = ("exact" if v[0] == "exact" else "N%d_%s" % (v[1], "masked" if v[2] else "unmasked"))
+        name += "_T" + ("f32" if v[3] == torch.float32 else "bf16")
+        st = steps if v == variants[0] else max(10, steps // 2)
+        ms_step, ms_kernel = time_launches(torch, mk(v, v[3]), N_SETS, st, warmup)
+        nb, by, fl = c1_bytes_flops(v, 4 if v[3] == torch.float32 else 2)
+        results[name] = {
+            "ms_per_step": ms_step, "ms_kernel": ms_kernel,
+            "blocks_per_s": nb / (ms_step * 1e-3),
+            "hbm_frac": by / (ms_kernel * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "mfma_frac": fl / (ms_kernel * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "bytes": by, "flops": fl,
+        }
+    return results
+
+
+def profile_c1(torch, tri, synth, n):
+    """Headline launch n times on rotating buffer sets, then a plain 256 MiB copy n
+    times: the copy's FETCH_SIZE / WRITE_SIZE per dispatch calibrate the counters."""
+    C = C1["C"]
+    n_blocks = C1["B"] * C1["H"] * C1["T"] // C
+    sets = [{k: v.cuda() for k, v in synth.blocks(1 if s == 0 else 1000 + s, n_blocks, C, C1["d_k"],
+                                                  k_dtype="bf16").items()} for s in range(N_SETS)]
+    outs = [torch.empty((n_blocks, C, C), device="cuda") for _ in range(N_SETS)]
+    for i in range(n):
+        x = sets[i % N_SETS]
+        tri.gdn_tri_inverse_neumann(K=x["K"], beta=x["beta"], g=x["g"], C=C, N=3, mask=True,
+                                    compute="bf16", out=outs[i % N_SETS])
+    torch.cuda.synchronize()
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(n):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def cpu_baseline_c1():
+    import oracle
+    import synth
+    n_blocks = C1["B"] * C1["H"] * C1["T"] // C1["C"]
+    inp = synth.blocks(1, n_blocks, C1["C"], C1["d_k"], k_dtype="bf16")
+    K = inp["K"].double().numpy()
+    beta = inp["beta"].double().numpy()
+    g = inp["g"].double().numpy()
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        A = oracle.build_A(K, beta, g)
+        oracle.neumann(A, 3, True)
+        reps += 1
+        if time.perf_counter() - t0 > 10.0 or reps >= 400:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": reps * n_blocks / dt, "unit": "blocks/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": "the full 2048-block workload (A build + N=3 masked Neumann, fp64), "
+                      "%d pass(es), %.1f s" % (reps, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", default="all")
+    ap.add_argument("--profile-launches", type=int, default=0,
+                    help="profiling mode: run the headline launch this many times plus a "
+                         "256 MiB device copy (counter calibration), print nothing else")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import tri_inverse_amd as tri
+
+    torch.cuda.set_device(0)
+    if args.profile_launches:
+        profile_c1(torch, tri, synth, args.profile_launches)
+        return
+    c1 = bench_c1(torch, tri, synth, args.steps, args.warmup)
+    head = c1["N3_masked_Tf32"]
+    traffic = load_traffic("inverse_kernel<4,1,128,1,0,1>")
+    roofline = {
+        "bound": "hbm",
+        "achieved": head["bytes"] / (head["ms_kernel"] * 1e-3) / 1e9,
+        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": head["bytes"] / (head["ms_kernel"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "traffic": traffic,
+    }
+    out = {
+        "metric": "64×64 tri-inverse blocks/s; GDN chunk-fwd tokens/s; % MFMA/HBM roofline",
+        "value": head["blocks_per_s"],
+        "unit": "blocks/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded unit-norm bf16 keys, U(0,1) beta, log-sigmoid gates)",
+        "config": {"workload": "batched 64x64 tri-inverse, B=1 H=16 seq=8192 (2048 blocks), "
+                               "d_k=128 bf16 K, A built in-kernel, truncated Neumann N=3 + band "
+                               "mask, fp32 accumulate, T fp32",
+                   "n_blocks": 2048, "C": 64, "d_k": 128, "N": 3, "mask": True},
+        "roofline": roofline,
+        "variants": c1,
+        "source_digest": source_digest(),
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline_c1()
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,165 @@
+/*
+ * gdn.h -- C ABI of libgdn: the chunk-wise Gated DeltaNet intra-chunk solve on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Pages the operations follow (cited by title):
+ *   [GEO]  "When Good Enough Is Optimal: Multiplication-Only Matrix Inversion
+ *           Approximation for Quantized Gated DeltaNet" (technical summary):
+ *           problem statement (per-chunk T = (I - A)^-1 with A strictly lower),
+ *           Methodologie SS1 (truncated low-order Neumann sum, Lemma 3.1),
+ *           SS2 (structural diagonal mask), SS3 (parallel residual correction),
+ *           "Adaptation a la Quantification" (low-bit ranges, N = 3).
+ *   [PSDA] "A Persistent-State Dataflow Accelerator for Memory-Bound Linear
+ *           Attention Decode on FPGA" (technical summary), section 2.B (the state
+ *           read / delta correction / state write split of one recurrence step).
+ *
+ * Notation for one block (one chunk of one (batch, head)), positions r = 0..C-1:
+ *   K [C][d_k], V [C][d_v], Q [C][d_k]; beta[C]; gamma[C] per-token log-gates (<= 0);
+ *   G = cumulative sum of gamma restarted at every chunk start;
+ *   A_ij = -beta_i (k_i . k_j) exp(G_i - G_j) for i > j, 0 otherwise   (strictly lower)
+ *   T    = (I - A)^-1 (exact), or its truncated / masked approximation.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor arguments are DEVICE pointers, row-major and contiguous, 16-byte
+ *     aligned (else GDN_ERR_BAD_ALIGNMENT).  The caller allocates and frees them.
+ *     Inputs are read-only; outputs are fully overwritten, never accumulated into.
+ *     Inputs and outputs must not overlap.
+ *   - Descriptor structs (gdn_blocks, gdn_inverse_cfg) are HOST pointers, read
+ *     during the call only.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *     enqueued on it and the call returns without synchronising.  Argument errors
+ *     and launch errors are returned synchronously; device faults surface at the
+ *     caller's next synchronisation.  No C++ exception crosses the ABI.
+ *   - The library allocates nothing, keeps no per-call state and is reentrant.
+ *   - n_blocks == 0 (or B*H == 0, T == 0) is valid and enqueues nothing.
+ *   - Supported chunk sizes C: 16, 32, 64 (all entry points), 128 and 256
+ *     (gdn_wy and the inverse entry points with compute = GDN_BF16).  d_k and d_v:
+ *     multiples of 32, at most 256.  Anything else: GDN_ERR_UNSUPPORTED.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_NULL_POINTER = 1,  /* a required pointer is NULL                          */
+  GDN_ERR_BAD_SHAPE = 2,     /* negative size, T % C != 0, N out of range, ...      */
+  GDN_ERR_BAD_DTYPE = 3,     /* dtype code not accepted for that argument           */
+  GDN_ERR_BAD_ALIGNMENT = 4, /* a tensor pointer is not 16-byte aligned             */
+  GDN_ERR_UNSUPPORTED = 5,   /* valid request this build does not implement         */
+  GDN_ERR_HIP = 6            /* the HIP runtime reported an error at launch         */
+} gdn_status;
+
+/* element types (int32 codes in every signature) */
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1, GDN_FP8_E4M3 = 2 } gdn_dtype;
+
+/* inverse variants */
+typedef enum gdn_inv_mode {
+  GDN_INV_NEUMANN = 0, /* truncated sum_{n<=N} A^n ([GEO] Methodologie SS1), optional
+                          band mask i - j <= N ([GEO] Methodologie SS2)                */
+  GDN_INV_EXACT = 1    /* prod_{i<m} (I + A^(2^i)), m = ceil(log2 C): exact because
+                          A^C = 0 (Lemma 3.1 of [GEO])                                */
+} gdn_inv_mode;
+
+/* How T is formed.  `compute` is the MFMA operand type of the power chain:
+ *   GDN_F32  fp32 operands (16x16x4 f32 MFMA)
+ *   GDN_BF16 bf16 operands, fp32 accumulation (16x16x32 bf16 MFMA)
+ *   GDN_FP8_E4M3 OCP e4m3 operands with one absmax/448 scale per block and tensor,
+ *            fp32 accumulation (16x16x32 fp8 MFMA); Neumann mode only.
+ * N is ignored for GDN_INV_EXACT. */
+typedef struct gdn_inverse_cfg {
+  int32_t mode;    /* gdn_inv_mode                  */
+  int32_t N;       /* truncation order, 1 <= N < C  */
+  int32_t mask;    /* 0 / 1: apply M^(N)            */
+  int32_t compute; /* gdn_dtype                     */
+} gdn_inverse_cfg;
+
+/* A batch of independent C x C blocks.  Either A is given (then K, beta, g are not
+ * read), or A is built on the fly from K, beta and g.
+ *   A     [n_blocks][C][C] fp32; only the strictly lower triangle is read.
+ *   K     [n_blocks][C][d_k], k_dtype GDN_BF16 or GDN_F32 (for a [B][H][T][d_k]
+ *         tensor with T % C == 0 this is the same memory with n_blocks = B*H*T/C).
+ *   beta  [n_blocks][C] fp32.
+ *   g     [n_blocks][C] fp32 per-token log-gates; if g_cumulative != 0 they are
+ *         already the in-chunk cumulative sums G. */
+typedef struct gdn_blocks {
+  const float* A;
+  const void* K;
+  int32_t k_dtype;
+  int32_t g_cumulative;
+  const float* beta;
+  const float* g;
+  int64_t n_blocks;
+  int32_t C;
+  int32_t d_k;
+} gdn_blocks;
+
+/* fp8 diagnostics, accumulated on the device by the fp8 paths (uint64_t[4]):
+ *   [0] non-finite values met when quantising
+ *   [1] saturations (|x| / scale rounds beyond 448, i.e. >= 464) under the dynamic per-block absmax scale
+ *   [2] saturations under a static per-block scale (A's scale reused for its powers
+ *       and for T): the fixed-range regime in which high powers overflow
+ *   [3] non-zero values that quantise to zero (underflow)                          */
+#define GDN_FP8_STATS_COUNT 4
+
+int gdn_abi_version(void);
+const char* gdn_status_string(int32_t status);
+
+/* A = -tril(diag(beta) (K K^T .* exp(G_i - G_j)), -1) per block ([GEO] problem
+ * statement: A strictly lower).  in->A must be NULL.  A_out [n_blocks][C][C] fp32,
+ * upper triangle and diagonal written as exact zeros. */
+gdn_status gdn_build_A(const gdn_blocks* in, float* A_out, void* stream);
+
+/* T = M^(N) .* sum_{n=0}^{N} A^n (mask != 0) or the plain truncated sum (mask == 0),
+ * evaluated as N-1 Horner products H <- I + A H ([GEO] Methodologie SS1-2).
+ * compute: GDN_F32, GDN_BF16 or GDN_FP8_E4M3.  T_out [n_blocks][C][C], t_dtype GDN_F32
+ * or GDN_BF16.  stats: device uint64_t[4] (see above) or NULL; when given it is
+ * zeroed on `stream` and then accumulated (fp8 compute only; other computes write
+ * zeros). */
+gdn_status gdn_tri_inverse_neumann(const gdn_blocks* in, int32_t N, int32_t mask,
+                                   int32_t compute, void* T_out, int32_t t_dtype,
+                                   uint64_t* stats, void* stream);
+
+/* T = prod_{i=0}^{m-1} (I + A^(2^i)), m = ceil(log2 C): the exact inverse by
+ * multiplications only.  compute GDN_F32 or GDN_BF16. */
+gdn_status gdn_tri_inverse_exact(const gdn_blocks* in, int32_t compute, void* T_out,
+                                 int32_t t_dtype, void* stream);
+
+/* WY products per block: W = T diag(s) K, U = T diag(beta) V with s = beta
+ * (gate_k == 0) or s = beta .* exp(G) (gate_k != 0, the form the gated chunk
+ * recurrence consumes).  T: if non-NULL, [n_blocks][C][C] of t_dtype (GDN_F32 or
+ * GDN_BF16), used as given; if NULL, T is formed on the fly from in (K, beta, g;
+ * in->A must be NULL) with `inv`.  V [n_blocks][C][d_v] bf16.  W_out
+ * [n_blocks][C][d_k], U_out [n_blocks][C][d_v], out_dtype GDN_F32 or GDN_BF16. */
+gdn_status gdn_wy(const gdn_blocks* in, const void* T, int32_t t_dtype,
+                  const gdn_inverse_cfg* inv, const void* V, int32_t d_v, int32_t gate_k,
+                  void* W_out, void* U_out, int32_t out_dtype, void* stream);
+
+/* Chunk-wise gated delta rule forward over whole sequences.  Per (b, h), chunks
+ * in order, state S [d_k][d_v] fp32 starting at S0 (zeros if NULL):
+ *   T from A (inv); U' = T diag(beta) (V - diag(exp(G)) K S)   (= U - W S, W gated)
+ *   O  = scale (diag(exp(G)) Q S + (Q K^T .* exp(G_i - G_j) .* [i >= j]) U')
+ *   S <- exp(G_C) S + K^T diag(exp(G_C - G)) U'
+ * Q, K [B][H][T][d_k] and V [B][H][T][d_v] in qkv_dtype (GDN_BF16); beta, g
+ * [B][H][T] fp32 (g per-token log-gates); S0, S_out [B][H][d_k][d_v] fp32;
+ * O [B][H][T][d_v] in o_dtype (GDN_BF16 or GDN_F32).  T % C == 0.  stats as for
+ * gdn_tri_inverse_neumann (fp8 compute). */
+gdn_status gdn_chunk_fwd(const void* Q, const void* K, const void* V, int32_t qkv_dtype,
+                         const float* beta, const float* g, const float* S0, void* O,
+                         int32_t o_dtype, float* S_out, int32_t B, int32_t H, int64_t T,
+                         int32_t d_k, int32_t d_v, int32_t C, float scale,
+                         const gdn_inverse_cfg* inv, uint64_t* stats, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,93 @@
+"""C-ABI checks that run without a GPU: the library loads, exports every symbol the
+header declares, and every validation path returns its documented status before any
+HIP call is made (all pointers below are fake host addresses that are never touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+tri = pytest.importorskip("tri_inverse_amd", reason="libgdn.so not built")
+lib = tri._lib
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_A-Z0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = header_functions()
+    assert "gdn_chunk_fwd" in names and "gdn_tri_inverse_neumann" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(tri.EXPORTED)
+
+
+def test_version_and_status_strings():
+    assert tri.gdn_abi_version() == 1
+    for s in range(7):
+        assert tri.gdn_status_string(s).startswith("GDN_")
+    assert "unknown" in tri.gdn_status_string(99)
+
+
+FAKE = 0x10000  # aligned, never dereferenced: validation fails or returns before use
+
+
+def blocks(**kw):
+    d = tri.gdn_blocks()
+    d.A = kw.get("A", None)
+    d.K = kw.get("K", FAKE)
+    d.k_dtype = kw.get("k_dtype", tri.GDN_BF16)
+    d.g_cumulative = 0
+    d.beta = kw.get("beta", FAKE)
+    d.g = kw.get("g", FAKE)
+    d.n_blocks = kw.get("n_blocks", 4)
+    d.C = kw.get("C", 64)
+    d.d_k = kw.get("d_k", 128)
+    return d
+
+
+def neumann(d, N=3, mask=1, compute=tri.GDN_BF16, T=FAKE, t_dtype=tri.GDN_F32, stats=None):
+    return lib.gdn_tri_inverse_neumann(ctypes.byref(d) if d is not None else None, N, mask, compute,
+                                       T, t_dtype, stats, None)
+
+
+def test_neumann_validation():
+    assert neumann(None) == 1                                   # NULL descriptor
+    assert neumann(blocks(K=None)) == 1                         # NULL K
+    assert neumann(blocks(), T=None) == 1                       # NULL output
+    assert neumann(blocks(C=48)) == 5                           # unsupported chunk
+    assert neumann(blocks(d_k=48)) == 5                         # unsupported head dim
+    assert neumann(blocks(n_blocks=-1)) == 2                    # negative size
+    assert neumann(blocks(), N=0) == 2                          # N out of range
+    assert neumann(blocks(), N=64) == 2
+    assert neumann(blocks(), mask=2) == 2
+    assert neumann(blocks(), compute=7) == 3                    # bad dtype codes
+    assert neumann(blocks(), t_dtype=tri.GDN_FP8_E4M3) == 3
+    assert neumann(blocks(k_dtype=9)) == 3
+    assert neumann(blocks(k_dtype=tri.GDN_F32)) == 5            # fp32 K only for build_A
+    assert neumann(blocks(K=FAKE + 2)) == 4                     # misaligned
+    assert neumann(blocks(), T=FAKE + 8) == 4
+    assert neumann(blocks(n_blocks=0)) == 0                     # empty batch: nothing launched
+    assert neumann(blocks(A=FAKE, K=None, beta=None, g=None, n_blocks=0)) == 0
+    assert neumann(blocks(K=None, beta=None, g=None, n_blocks=0), T=None) == 0  # NULLs allowed when empty
+    assert neumann(blocks(n_blocks=0), N=0) == 2                # sizes still validated
+
+
+def test_exact_and_build_A_validation():
+    ex = lambda d, compute=tri.GDN_BF16, T=FAKE: lib.gdn_tri_inverse_exact(
+        ctypes.byref(d), compute, T, tri.GDN_F32, None)
+    assert ex(blocks(), compute=tri.GDN_FP8_E4M3) == 5
+    assert ex(blocks(C=24)) == 5
+    assert ex(blocks(), T=None) == 1
+    assert ex(blocks(n_blocks=0)) == 0
+    bA = lambda d, out=FAKE: lib.gdn_build_A(ctypes.byref(d), out, None)
+    assert bA(blocks(A=FAKE)) == 5                               # A is the output here
+    assert bA(blocks(), out=None) == 1
+    assert bA(blocks(beta=None)) == 1
+    assert bA(blocks(n_blocks=0)) == 0
+    assert bA(blocks(n_blocks=0, k_dtype=tri.GDN_F32)) == 0

@@ -1,0 +1,167 @@
+// abi.cpp -- the C ABI of libgdn (declared in include/gdn.h): argument validation,
+// status codes, and the hand-off to the kernel launchers on the caller's stream.
+// Validation happens entirely on the host and returns before any HIP call, so every
+// error path can be exercised without a GPU.
+#include "gdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include "gdn_kernels.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool chunk_ok(int C) { return C == 16 || C == 32 || C == 64 || C == 128 || C == 256; }
+bool chunk_small(int C) { return C == 16 || C == 32 || C == 64; }
+bool head_dim_ok(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
+
+gdn_status launch_result(int rc) {
+  if (rc < 0) return GDN_ERR_UNSUPPORTED;
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+// validates a gdn_blocks descriptor; src_out: 0 = A given, 1 = K bf16, 2 = K fp32.
+// An empty batch (n_blocks == 0) only needs valid sizes: its pointers may be NULL.
+gdn_status check_blocks(const gdn_blocks* in, bool allow_A, bool allow_k_f32, int* src_out) {
+  if (!in) return GDN_ERR_NULL_POINTER;
+  if (in->n_blocks < 0 || in->C <= 0) return GDN_ERR_BAD_SHAPE;
+  if (!chunk_ok(in->C)) return GDN_ERR_UNSUPPORTED;
+  const bool empty = in->n_blocks == 0;
+  if (in->A) {
+    if (!allow_A) return GDN_ERR_UNSUPPORTED;
+    if (!aligned16(in->A)) return GDN_ERR_BAD_ALIGNMENT;
+    *src_out = 0;
+    return GDN_OK;
+  }
+  if (in->d_k <= 0) {
+    if (empty && !in->K) {  // empty batch given as A == NULL, K == NULL
+      *src_out = 0;
+      return GDN_OK;
+    }
+    return GDN_ERR_BAD_SHAPE;
+  }
+  if (!head_dim_ok(in->d_k)) return GDN_ERR_UNSUPPORTED;
+  if (in->k_dtype == GDN_BF16) {
+    *src_out = 1;
+  } else if (in->k_dtype == GDN_F32) {
+    if (!allow_k_f32) return GDN_ERR_UNSUPPORTED;
+    *src_out = 2;
+  } else {
+    return GDN_ERR_BAD_DTYPE;
+  }
+  if (empty) return GDN_OK;
+  if (!in->K || !in->beta || !in->g) return GDN_ERR_NULL_POINTER;
+  if (!aligned16(in->K) || !aligned16(in->beta) || !aligned16(in->g)) return GDN_ERR_BAD_ALIGNMENT;
+  return GDN_OK;
+}
+
+gdn::BlocksArgs to_args(const gdn_blocks* in) {
+  gdn::BlocksArgs a;
+  a.A = in->A;
+  a.K = in->K;
+  a.beta = in->beta;
+  a.g = in->g;
+  a.n_blocks = in->n_blocks;
+  a.C = in->C;
+  a.d_k = in->d_k;
+  a.g_cumulative = in->g_cumulative;
+  return a;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_status_string(int32_t s) {
+  switch (s) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_NULL_POINTER: return "GDN_ERR_NULL_POINTER: a required pointer is NULL";
+    case GDN_ERR_BAD_SHAPE: return "GDN_ERR_BAD_SHAPE: a size or order argument is out of range";
+    case GDN_ERR_BAD_DTYPE: return "GDN_ERR_BAD_DTYPE: dtype code not accepted for this argument";
+    case GDN_ERR_BAD_ALIGNMENT: return "GDN_ERR_BAD_ALIGNMENT: a tensor pointer is not 16-byte aligned";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: configuration not implemented by this build";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP: the HIP runtime reported an error at launch";
+    default: return "unknown gdn_status";
+  }
+}
+
+gdn_status gdn_build_A(const gdn_blocks* in, float* A_out, void* stream) {
+  int src = 0;
+  if (in && in->A) return GDN_ERR_UNSUPPORTED;  // A is the output here
+  gdn_status st = check_blocks(in, false, true, &src);
+  if (st != GDN_OK) return st;
+  if (!chunk_small(in->C)) return GDN_ERR_UNSUPPORTED;
+  if (in->n_blocks == 0) return GDN_OK;
+  if (!A_out) return GDN_ERR_NULL_POINTER;
+  if (!aligned16(A_out)) return GDN_ERR_BAD_ALIGNMENT;
+  return launch_result(gdn::launch_build_A(to_args(in), src, A_out, as_stream(stream)));
+}
+
+gdn_status gdn_tri_inverse_neumann(const gdn_blocks* in, int32_t N, int32_t mask, int32_t compute,
+                                   void* T_out, int32_t t_dtype, uint64_t* stats, void* stream) {
+  int src = 0;
+  gdn_status st = check_blocks(in, true, false, &src);
+  if (st != GDN_OK) return st;
+  if (N < 1 || N >= in->C) return GDN_ERR_BAD_SHAPE;
+  if (mask != 0 && mask != 1) return GDN_ERR_BAD_SHAPE;
+  if (compute != GDN_F32 && compute != GDN_BF16 && compute != GDN_FP8_E4M3) return GDN_ERR_BAD_DTYPE;
+  if (t_dtype != GDN_F32 && t_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
+  if (!chunk_small(in->C)) return GDN_ERR_UNSUPPORTED;
+  if (stats && !aligned16(stats)) return GDN_ERR_BAD_ALIGNMENT;
+  if (in->n_blocks > 0) {
+    if (!T_out) return GDN_ERR_NULL_POINTER;
+    if (!aligned16(T_out)) return GDN_ERR_BAD_ALIGNMENT;
+  }
+  hipStream_t s = as_stream(stream);
+  auto* st64 = reinterpret_cast<unsigned long long*>(stats);
+  if (st64) {
+    gdn::launch_zero_stats(st64, s);
+    if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;
+  }
+  if (in->n_blocks == 0) return GDN_OK;
+  return launch_result(gdn::launch_neumann(to_args(in), src, N, mask, compute, T_out,
+                                           t_dtype == GDN_BF16, st64, s));
+}
+
+gdn_status gdn_tri_inverse_exact(const gdn_blocks* in, int32_t compute, void* T_out,
+                                 int32_t t_dtype, void* stream) {
+  int src = 0;
+  gdn_status st = check_blocks(in, true, false, &src);
+  if (st != GDN_OK) return st;
+  if (compute == GDN_FP8_E4M3) return GDN_ERR_UNSUPPORTED;
+  if (compute != GDN_F32 && compute != GDN_BF16) return GDN_ERR_BAD_DTYPE;
+  if (t_dtype != GDN_F32 && t_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
+  if (!chunk_small(in->C)) return GDN_ERR_UNSUPPORTED;
+  if (in->n_blocks == 0) return GDN_OK;
+  if (!T_out) return GDN_ERR_NULL_POINTER;
+  if (!aligned16(T_out)) return GDN_ERR_BAD_ALIGNMENT;
+  return launch_result(gdn::launch_exact(to_args(in), src, compute, T_out, t_dtype == GDN_BF16,
+                                         as_stream(stream)));
+}
+
+gdn_status gdn_wy(const gdn_blocks* in, const void* T, int32_t t_dtype, const gdn_inverse_cfg* inv,
+                  const void* V, int32_t d_v, int32_t gate_k, void* W_out, void* U_out,
+                  int32_t out_dtype, void* stream) {
+  (void)in; (void)T; (void)t_dtype; (void)inv; (void)V; (void)d_v; (void)gate_k;
+  (void)W_out; (void)U_out; (void)out_dtype; (void)stream;
+  return GDN_ERR_UNSUPPORTED;
+}
+
+gdn_status gdn_chunk_fwd(const void* Q, const void* K, const void* V, int32_t qkv_dtype,
+                         const float* beta, const float* g, const float* S0, void* O,
+                         int32_t o_dtype, float* S_out, int32_t B, int32_t H, int64_t T,
+                         int32_t d_k, int32_t d_v, int32_t C, float scale,
+                         const gdn_inverse_cfg* inv, uint64_t* stats, void* stream) {
+  (void)Q; (void)K; (void)V; (void)qkv_dtype; (void)beta; (void)g; (void)S0; (void)O;
+  (void)o_dtype; (void)S_out; (void)B; (void)H; (void)T; (void)d_k; (void)d_v; (void)C;
+  (void)scale; (void)inv; (void)stats; (void)stream;
+  return GDN_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

@@ -1,0 +1,149 @@
+// gdn_device.hpp -- gfx950 (CDNA4) device helpers shared by the GDN kernels.
+//
+// Fragment vocabulary used by every kernel (wave64, 16x16 tiles, lane l = 16*g + c
+// with g = l >> 4 in 0..3 and c = l & 15):
+//
+//   D-form tile (I,J) of a matrix M : lane (g,c) register r holds M[16I + 4g + r][16J + c]
+//                                     (what an MFMA 16x16 accumulator holds)
+//   T-form tile (I,J) of M          : lane (g,c) register r holds M[16I + c][16J + 4g + r]
+//                                     (the D-form of M^T, read transposed)
+//
+// A 16x16x32 MFMA contracts 32 k-values; lane (g,c) supplies 8 of them for row c of
+// the left operand and column c of the right operand.  We fix the slot->k map
+//   slot t of lane group g  <->  k = 32p + 16*(t/4) + 4g + (t%4)        (t = 0..7)
+// so that two stacked D-form tiles (2p, J), (2p+1, J) of M are, register for
+// register, the right-operand fragment of M's k-pair p ("column pack", CP), and two
+// side-by-side T-form tiles (I, 2p), (I, 2p+1) are the left-operand fragment of
+// M's rows ("row pack", RP).  Any consistent slot->k map leaves a contraction
+// unchanged, so products chain from accumulator to operand without touching LDS:
+//   (X Y) in D-form  = sum_p mfma(RP(X, I, p), CP(Y, p, J))
+//   (X Y) in T-form  = sum_p mfma(CP(Y, p, J), RP(X, I, p))
+// The fp32 path uses 16x16x4 MFMAs with slot g of sub-step u <-> k = 16K + 4g + u,
+// so register u of a D-form (T-form) tile is directly the operand of sub-step u.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+
+constexpr int WAVE = 64;
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---- MFMA wrappers ------------------------------------------------------------
+
+__device__ __forceinline__ f32x4 mma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_f32(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// fp8 (OCP e4m3 on gfx950) operands: 8 codes per lane packed in a 64-bit integer
+__device__ __forceinline__ f32x4 mma_fp8(long a, long b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
+}
+
+// ---- packing ------------------------------------------------------------------
+
+__device__ __forceinline__ bf16x8 pack8(const f32x4& lo, const f32x4& hi) {
+  bf16x8 r;
+  r[0] = (__bf16)lo[0];
+  r[1] = (__bf16)lo[1];
+  r[2] = (__bf16)lo[2];
+  r[3] = (__bf16)lo[3];
+  r[4] = (__bf16)hi[0];
+  r[5] = (__bf16)hi[1];
+  r[6] = (__bf16)hi[2];
+  r[7] = (__bf16)hi[3];
+  return r;
+}
+
+__device__ __forceinline__ bf16x4 pack4(const f32x4& v) {
+  bf16x4 r;
+  r[0] = (__bf16)v[0];
+  r[1] = (__bf16)v[1];
+  r[2] = (__bf16)v[2];
+  r[3] = (__bf16)v[3];
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 join8(const bf16x4& lo, const bf16x4& hi) {
+  bf16x8 r;
+  r[0] = lo[0];
+  r[1] = lo[1];
+  r[2] = lo[2];
+  r[3] = lo[3];
+  r[4] = hi[0];
+  r[5] = hi[1];
+  r[6] = hi[2];
+  r[7] = hi[3];
+  return r;
+}
+
+__device__ __forceinline__ f32x4 unpack4(const bf16x4& v) {
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
+// ---- fp8 e4m3 (OCP) quantisation ------------------------------------------------
+// Largest finite e4m3 value is 448.  Values are clamped to +-448 before the hardware
+// conversion (round to nearest even), so an out-of-range input saturates instead of
+// becoming NaN; the callers count how often that happens.
+constexpr float FP8_MAX = 448.0f;
+// A value saturates when its correctly rounded e4m3 code would lie beyond 448: the
+// rounding boundary is 464, midway between 448 and the next step of that binade (480).
+constexpr float FP8_SAT = 464.0f;
+
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt_fp8x2(float a, float b, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+}
+
+template <int BYTE>
+__device__ __forceinline__ float fp8_to_f32(uint32_t word) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)word, BYTE);
+}
+
+// ---- wave-wide reductions and scans (wave64) ------------------------------------
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fminf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += (uint32_t)__shfl_xor((int)v, off, 64);
+  return v;
+}
+
+// inclusive prefix sum over the first n lanes (n <= 64); lanes >= n get garbage
+__device__ __forceinline__ float wave_inclusive_scan(float v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    float o = __shfl_up(v, off, 64);
+    if (l >= off) v += o;
+  }
+  return v;
+}
+
+}  // namespace gdn

@@ -1,0 +1,663 @@
+// tri_block.hpp -- one wave owns one C x C block (C = 16*NT, NT = 1, 2, 4) and keeps
+// every matrix of the solve in registers as 16x16 fp32 tiles (see gdn_device.hpp for
+// the D-form / T-form fragment vocabulary).
+//
+// Steps implemented here (all per block, all in registers):
+//   gates    : G = in-chunk cumsum of the per-token log-gates (wave prefix scan)
+//   build_A  : A = -tril(diag(beta) (K K^T .* exp(G_i - G_j)), -1) from K row
+//              fragments with MFMA (K K^T is symmetric, so the D-form tiles (J,I)
+//              of K K^T are the T-form tiles (I,J) of A -- both forms come from one
+//              set of MFMAs over all NT x NT tiles)
+//   neumann  : T = sum_{n<=N} A^n as H <- I + A H (N-1 products), optional band mask
+//              i - j <= N applied to A and to every intermediate (identical result to
+//              masking the final sum, since band entries of products of lower-
+//              triangular matrices only involve band entries)
+//   doubling : T = prod_{q<m} (I + A^(2^q)) as P <- P + P X, X <- X X
+// Pages: [GEO] "When Good Enough Is Optimal: Multiplication-Only Matrix Inversion
+// Approximation for Quantized Gated DeltaNet" -- problem statement (T = (I-A)^-1,
+// A strictly lower), Methodologie SS1 (truncated Neumann, Lemma 3.1), SS2 (mask).
+#pragma once
+#include "gdn_device.hpp"
+
+namespace gdn {
+
+enum : int { CMP_F32 = 0, CMP_BF16 = 1, CMP_FP8 = 2 };
+
+template <int NT>
+struct Mat {
+  f32x4 t[NT][NT];  // only lower tiles I >= J are meaningful
+};
+
+template <int NT>
+__device__ __forceinline__ f32x4 tile_or_zero(const Mat<NT>& M, int I, int J) {
+  return (I < NT && J < NT && I >= J) ? M.t[I][J] : zero4();
+}
+
+// identity 16x16 tile, same in D-form and T-form: element (4g + r, c)
+__device__ __forceinline__ f32x4 eye_tile() {
+  const int l = lane_id(), g = l >> 4, c = l & 15;
+  f32x4 e;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) e[r] = (4 * g + r == c) ? 1.f : 0.f;
+  return e;
+}
+
+// per-lane gate / beta values at the two index families a lane touches
+template <int NT>
+struct Gates {
+  float Gl, bl;      // this lane's G and beta (lane l = chunk position l)
+  bool split;        // exp(-G) finite for the whole block (min G >= -80)
+  float rc[NT];      // -beta exp(G) at 16X + c      (row factor of A, T-form)
+  float nc[NT];      // exp(-G) at 16X + c           (column factor of A, D-form)
+  float rr[NT][4];   // -beta exp(G) at 16X + 4g + r (row factor of A, D-form)
+  float nr[NT][4];   // exp(-G) at 16X + 4g + r      (column factor of A, T-form)
+};
+
+// gather G, beta and the two exponentials of G to a lane's index families
+template <int NT>
+__device__ __forceinline__ void gather_gates(float Gl, float bl, Gates<NT>& gt) {
+  const int l = lane_id(), grp = l >> 4, c = l & 15;
+  // split factors (used when exp(-G) stays finite, else the element-wise fallback
+  // of gram_to_A gathers G and beta itself)
+  gt.Gl = Gl;
+  gt.bl = bl;
+  gt.split = wave_min(Gl) >= -80.f;
+  const float rl = -bl * __expf(Gl), nl = __expf(-Gl);
+#pragma unroll
+  for (int X = 0; X < NT; ++X) {
+    const int ic = 16 * X + c;
+    gt.rc[X] = __shfl(rl, ic, 64);
+    gt.nc[X] = __shfl(nl, ic, 64);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int ir = 16 * X + 4 * grp + r;
+      gt.rr[X][r] = __shfl(rl, ir, 64);
+      gt.nr[X][r] = __shfl(nl, ir, 64);
+    }
+  }
+}
+
+// G = inclusive in-chunk cumsum of gamma (unless already cumulative), then gathered
+// to the index families.  beta, g point at this block's C values.
+template <int NT>
+__device__ __forceinline__ void load_gates(const float* __restrict__ beta,
+                                           const float* __restrict__ g, bool g_cumulative,
+                                           Gates<NT>& gt) {
+  constexpr int C = 16 * NT;
+  const int l = lane_id(), grp = l >> 4, c = l & 15;
+  float gl = (l < C) ? g[l] : 0.f;
+  float Gl = g_cumulative ? gl : wave_inclusive_scan(gl);
+  float bl = (l < C) ? beta[l] : 0.f;
+  gather_gates<NT>(Gl, bl, gt);
+}
+
+// S = K K^T over all NT x NT tiles in D-form (S[I][J] lane (g,c) reg r =
+// (K K^T)[16I + 4g + r][16J + c]).  K points at the block's [C][dk] rows.
+// bf16 K: 16x16x32 bf16 MFMA over 32-wide d slices (lane reads 16 contiguous bytes).
+template <int NT, int DK>
+__device__ __forceinline__ void gram_bf16(const __bf16* __restrict__ K, Mat<NT>& S) {
+  constexpr int NS = DK / 32;
+  const int l = lane_id(), g = l >> 4, c = l & 15;
+  bf16x8 kf[NT][NS];
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      kf[I][s] = *reinterpret_cast<const bf16x8*>(K + (size_t)(16 * I + c) * DK + 32 * s + 8 * g);
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int J = 0; J < NT; ++J) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int s = 0; s < NS; ++s) acc = mma_bf16(kf[I][s], kf[J][s], acc);
+      S.t[I][J] = acc;
+    }
+}
+
+// fp32 K: 16x16x4 f32 MFMA; lane (g,c) reads K[16I + c][16s + 4g .. +3] and uses
+// component u in sub-step u (slot g of sub-step u <-> d = 16s + 4g + u).
+template <int NT, int DK>
+__device__ __forceinline__ void gram_f32(const float* __restrict__ K, Mat<NT>& S) {
+  constexpr int NS = DK / 16;
+  const int l = lane_id(), g = l >> 4, c = l & 15;
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int J = 0; J < NT; ++J) S.t[I][J] = zero4();
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    f32x4 kf[NT];
+#pragma unroll
+    for (int I = 0; I < NT; ++I)
+      kf[I] = *reinterpret_cast<const f32x4*>(K + (size_t)(16 * I + c) * DK + 16 * s + 4 * g);
+#pragma unroll
+    for (int I = 0; I < NT; ++I)
+#pragma unroll
+      for (int J = 0; J < NT; ++J)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) S.t[I][J] = mma_f32(kf[I][u], kf[J][u], S.t[I][J]);
+  }
+}
+
+// ---- raw per-block inputs, loaded separately from their use so that a wave can
+// prefetch the next block while it computes the current one --------------------
+
+// K rows as 16x16x32 operand fragments (lane (g,c): K[16I + c][32s + 8g .. +7]) plus
+// this lane's gate and beta (lane l holds position l of the chunk, l < C)
+template <int NT, int DK>
+struct KBlock {
+  bf16x8 kf[NT][DK / 32];
+  float gl, bl;
+};
+
+template <int NT, int DK>
+__device__ __forceinline__ void load_kblock(const __bf16* __restrict__ K,
+                                            const float* __restrict__ beta,
+                                            const float* __restrict__ g, KBlock<NT, DK>& kb) {
+  constexpr int C = 16 * NT;
+  const int l = lane_id(), grp = l >> 4, c = l & 15;
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int s = 0; s < DK / 32; ++s)
+      kb.kf[I][s] = *reinterpret_cast<const bf16x8*>(K + (size_t)(16 * I + c) * DK + 32 * s + 8 * grp);
+  kb.gl = (l < C) ? g[l] : 0.f;
+  kb.bl = (l < C) ? beta[l] : 0.f;
+}
+
+// gate cumsum and gather to the two index families from the raw lane values
+template <int NT>
+__device__ __forceinline__ void gates_from_lanes(float gl, float bl, bool g_cumulative,
+                                                 Gates<NT>& gt) {
+  float Gl = g_cumulative ? gl : wave_inclusive_scan(gl);
+  gather_gates<NT>(Gl, bl, gt);
+}
+
+// Gram tiles from preloaded fragments (D-form), only tiles with |I - J| <= MAXD
+template <int NT, int DK, int MAXD = NT - 1>
+__device__ __forceinline__ void gram_from_frags(const KBlock<NT, DK>& kb, Mat<NT>& S) {
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int J = 0; J < NT; ++J) {
+      if (I - J > MAXD || J - I > MAXD) {
+        S.t[I][J] = zero4();
+        continue;
+      }
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int s = 0; s < DK / 32; ++s) acc = mma_bf16(kb.kf[I][s], kb.kf[J][s], acc);
+      S.t[I][J] = acc;
+    }
+}
+
+// A given in memory: raw lower tiles in both forms
+template <int NT>
+struct ABlock {
+  f32x4 t[NT][NT];  // T-form reads (row 16I + c, cols 16J + 4g .. +3)
+  f32x4 d[NT][NT];  // D-form reads (rows 16I + 4g + r, col 16J + c)
+};
+
+template <int NT>
+__device__ __forceinline__ void load_ablock(const float* __restrict__ A, ABlock<NT>& ab) {
+  constexpr int C = 16 * NT;
+  const int l = lane_id(), g = l >> 4, c = l & 15;
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int J = 0; J <= I; ++J) {
+      ab.t[I][J] = *reinterpret_cast<const f32x4*>(A + (size_t)(16 * I + c) * C + 16 * J + 4 * g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ab.d[I][J][r] = A[(size_t)(16 * I + 4 * g + r) * C + 16 * J + c];
+    }
+}
+
+// strict-lower and band masking of the raw A tiles
+template <int NT, int MAXD, bool BANDED>
+__device__ __forceinline__ void ablock_to_A(const ABlock<NT>& ab, int band, Mat<NT>& AD,
+                                            Mat<NT>& AT);
+
+// Lane-dependent part of (row - col) for an element of a 16x16 tile:
+//   D-form: i - j = 16(I - J) + r + lane_off,  T-form: i - j = 16(I - J) - r - lane_off,
+// with lane_off = 4g - c.  Masks compare against it instead of rebuilding indices.
+__device__ __forceinline__ int lane_off() {
+  const int l = lane_id();
+  return 4 * (l >> 4) - (l & 15);
+}
+
+// keep element iff lo <= (i - j) <= hi; tile-level uniform checks skip whole tiles
+template <int NT>
+__device__ __forceinline__ f32x4 band_select_D(f32x4 v, int IJ, int lo, int hi) {
+  const int lo_ = lane_off();
+  f32x4 o;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    int d = 16 * IJ + r + lo_;
+    o[r] = (d >= lo && d <= hi) ? v[r] : 0.f;
+  }
+  return o;
+}
+template <int NT>
+__device__ __forceinline__ f32x4 band_select_T(f32x4 v, int IJ, int lo, int hi) {
+  const int lo_ = lane_off();
+  f32x4 o;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    int d = 16 * IJ - r - lo_;
+    o[r] = (d >= lo && d <= hi) ? v[r] : 0.f;
+  }
+  return o;
+}
+
+template <int NT, int MAXD = NT - 1, bool BANDED = false>
+__device__ __forceinline__ void ablock_to_A(const ABlock<NT>& ab, int band, Mat<NT>& AD,
+                                            Mat<NT>& AT) {
+  const int hi = band < 0 ? (1 << 30) : band;
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int J = 0; J <= I; ++J) {
+      if (I - J > MAXD) {
+        AD.t[I][J] = zero4();
+        AT.t[I][J] = zero4();
+      } else if (BANDED || I == J) {
+        AD.t[I][J] = band_select_D<NT>(ab.d[I][J], I - J, 1, hi);
+        AT.t[I][J] = band_select_T<NT>(ab.t[I][J], I - J, 1, hi);
+      } else {
+        AD.t[I][J] = ab.d[I][J];
+        AT.t[I][J] = ab.t[I][J];
+      }
+    }
+}
+
+// A from the Gram tiles: AD (D-form) and AT (T-form), strictly lower.  With BANDED
+// the band mask (keep i - j <= band, band < 0 = none) is applied too.  The gate factor
+// is split as exp(G_i - G_j) = exp(G_i) exp(-G_j) when every exp(-G) of the block is
+// finite (G >= -80); otherwise each element takes exp of the difference.
+template <int NT, int MAXD = NT - 1, bool BANDED = false>
+__device__ __forceinline__ void gram_to_A(const Mat<NT>& S, const Gates<NT>& gt, int band,
+                                          Mat<NT>& AD, Mat<NT>& AT) {
+  const int hi = band < 0 ? (1 << 30) : band;
+  const bool split = gt.split;
+  const int lane = lane_id(), grp = lane >> 4, cl = lane & 15;
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int J = 0; J <= I; ++J) {
+      if (I - J > MAXD || (BANDED && 16 * (I - J) - 15 > hi)) {  // tile outside (uniform)
+        AD.t[I][J] = zero4();
+        AT.t[I][J] = zero4();
+        continue;
+      }
+      f32x4 d, t;
+      if (split) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          d[r] = gt.rr[I][r] * S.t[I][J][r] * gt.nc[J];
+          t[r] = gt.rc[I] * S.t[J][I][r] * gt.nr[J][r];
+        }
+      } else {
+        const float GcI = __shfl(gt.Gl, 16 * I + cl, 64), bcI = __shfl(gt.bl, 16 * I + cl, 64);
+        const float GcJ = __shfl(gt.Gl, 16 * J + cl, 64);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float GrI = __shfl(gt.Gl, 16 * I + 4 * grp + r, 64);
+          const float brI = __shfl(gt.bl, 16 * I + 4 * grp + r, 64);
+          const float GrJ = __shfl(gt.Gl, 16 * J + 4 * grp + r, 64);
+          d[r] = -brI * __expf(GrI - GcJ) * S.t[I][J][r];
+          t[r] = -bcI * __expf(GcI - GrJ) * S.t[J][I][r];
+        }
+      }
+      if (BANDED || I == J) {
+        AD.t[I][J] = band_select_D<NT>(d, I - J, 1, hi);
+        AT.t[I][J] = band_select_T<NT>(t, I - J, 1, hi);
+      } else {
+        AD.t[I][J] = d;
+        AT.t[I][J] = t;
+      }
+    }
+}
+
+// band mask on a D-form / T-form matrix (keep i - j <= band)
+template <int NT>
+__device__ __forceinline__ void mask_D(Mat<NT>& M, int band) {
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int J = 0; J <= I; ++J) {
+      if (16 * (I - J) + 15 <= band) continue;  // whole tile inside the band
+      if (16 * (I - J) - 15 > band) {
+        M.t[I][J] = zero4();
+        continue;
+      }
+      M.t[I][J] = band_select_D<NT>(M.t[I][J], I - J, -(1 << 30), band);
+    }
+}
+template <int NT>
+__device__ __forceinline__ void mask_T(Mat<NT>& M, int band) {
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int J = 0; J <= I; ++J) {
+      if (16 * (I - J) + 15 <= band) continue;
+      if (16 * (I - J) - 15 > band) {
+        M.t[I][J] = zero4();
+        continue;
+      }
+      M.t[I][J] = band_select_T<NT>(M.t[I][J], I - J, -(1 << 30), band);
+    }
+}
+
+template <int NT>
+__device__ __forceinline__ void add_eye(Mat<NT>& M) {
+  const f32x4 e = eye_tile();
+#pragma unroll
+  for (int I = 0; I < NT; ++I) M.t[I][I] += e;
+}
+
+// ---- products of lower-triangular matrices -----------------------------------
+// Z = X Y (+ I when EYE) for lower-triangular X (given in T-form, XT) and Y (given in
+// D-form, YD).  TFORM = false: Z in D-form; TFORM = true: Z in T-form.  Only tiles
+// with I - J <= MAXD are formed (the others are set to zero): with MAXD < NT - 1 the
+// caller guarantees that X and Y vanish beyond that tile distance and that the
+// result is band-masked afterwards, so no kept entry depends on a skipped tile.
+// The tile sum runs over the k-pairs p with J/2 <= p <= I/2.
+
+template <int NT>
+__device__ __forceinline__ f32x4 tile_init(int I, int J, bool eye) {
+  return (eye && I == J) ? eye_tile() : zero4();
+}
+
+template <int NT, bool TFORM, int MAXD, bool EYE>
+__device__ __forceinline__ void lmul_bf16(const Mat<NT>& XT, const Mat<NT>& YD, Mat<NT>& Z) {
+  constexpr int NP = (NT + 1) / 2;
+  bf16x8 rp[NT][NP], cp[NP][NT];
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      if (2 * p <= I && I - (2 * p + 1) <= MAXD)
+        rp[I][p] = pack8(tile_or_zero(XT, I, 2 * p), tile_or_zero(XT, I, 2 * p + 1));
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int J = 0; J < NT; ++J)
+      if (J <= 2 * p + 1 && 2 * p - J <= MAXD)
+        cp[p][J] = pack8(tile_or_zero(YD, 2 * p, J), tile_or_zero(YD, 2 * p + 1, J));
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int J = 0; J <= I; ++J) {
+      if (I - J > MAXD) {
+        Z.t[I][J] = zero4();
+        continue;
+      }
+      f32x4 acc = tile_init<NT>(I, J, EYE);
+#pragma unroll
+      for (int p = J / 2; p <= I / 2; ++p)
+        acc = TFORM ? mma_bf16(cp[p][J], rp[I][p], acc) : mma_bf16(rp[I][p], cp[p][J], acc);
+      Z.t[I][J] = acc;
+    }
+}
+
+template <int NT, bool TFORM, int MAXD, bool EYE>
+__device__ __forceinline__ void lmul_f32(const Mat<NT>& XT, const Mat<NT>& YD, Mat<NT>& Z) {
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int J = 0; J <= I; ++J) {
+      if (I - J > MAXD) {
+        Z.t[I][J] = zero4();
+        continue;
+      }
+      f32x4 acc = tile_init<NT>(I, J, EYE);
+#pragma unroll
+      for (int K = J; K <= I; ++K)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          acc = TFORM ? mma_f32(YD.t[K][J][u], XT.t[I][K][u], acc)
+                      : mma_f32(XT.t[I][K][u], YD.t[K][J][u], acc);
+      Z.t[I][J] = acc;
+    }
+}
+
+template <int NT, int CMP, bool TFORM, int MAXD = NT - 1, bool EYE = false>
+__device__ __forceinline__ void lmul(const Mat<NT>& XT, const Mat<NT>& YD, Mat<NT>& Z) {
+  if constexpr (CMP == CMP_F32)
+    lmul_f32<NT, TFORM, MAXD, EYE>(XT, YD, Z);
+  else
+    lmul_bf16<NT, TFORM, MAXD, EYE>(XT, YD, Z);
+}
+
+// ---- fp8 (e4m3) variant of the product, with per-block absmax scales ----------
+
+struct Fp8Counts {
+  uint32_t nonfinite, sat_dyn, sat_static, underflow;
+};
+
+// quantise 8 values (two tiles) to e4m3 codes with scale 1/inv_s applied first
+__device__ __forceinline__ long quant8(const f32x4& lo, const f32x4& hi, float inv_s) {
+  uint32_t w0 = cvt_fp8x2<false>(fminf(fmaxf(lo[0] * inv_s, -FP8_MAX), FP8_MAX),
+                                 fminf(fmaxf(lo[1] * inv_s, -FP8_MAX), FP8_MAX), 0u);
+  w0 = cvt_fp8x2<true>(fminf(fmaxf(lo[2] * inv_s, -FP8_MAX), FP8_MAX),
+                       fminf(fmaxf(lo[3] * inv_s, -FP8_MAX), FP8_MAX), w0);
+  uint32_t w1 = cvt_fp8x2<false>(fminf(fmaxf(hi[0] * inv_s, -FP8_MAX), FP8_MAX),
+                                 fminf(fmaxf(hi[1] * inv_s, -FP8_MAX), FP8_MAX), 0u);
+  w1 = cvt_fp8x2<true>(fminf(fmaxf(hi[2] * inv_s, -FP8_MAX), FP8_MAX),
+                       fminf(fmaxf(hi[3] * inv_s, -FP8_MAX), FP8_MAX), w1);
+  return (long)(((uint64_t)w1 << 32) | (uint64_t)w0);
+}
+
+// count diagnostics of quantising the lower tiles of M with scale s (dynamic) and
+// s_static (the static scale), per lane
+template <int NT>
+__device__ __forceinline__ void fp8_count(const Mat<NT>& M, float s, float s_static,
+                                          Fp8Counts& cnt) {
+  const float inv_s = 1.f / s, inv_st = 1.f / s_static;
+  constexpr float UNDER = 0.0009765625f;  // 2^-10: half the smallest e4m3 subnormal
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int J = 0; J <= I; ++J)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float x = M.t[I][J][r];
+        if (!__builtin_isfinite(x)) {
+          cnt.nonfinite++;
+          continue;
+        }
+        float a = fabsf(x);
+        cnt.sat_dyn += (a * inv_s >= FP8_SAT) ? 1u : 0u;
+        cnt.sat_static += (a * inv_st >= FP8_SAT) ? 1u : 0u;
+        cnt.underflow += (x != 0.f && a * inv_s <= UNDER) ? 1u : 0u;
+      }
+}
+
+template <int NT>
+__device__ __forceinline__ float absmax(const Mat<NT>& M) {
+  float m = 0.f;
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int J = 0; J <= I; ++J)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float a = fabsf(M.t[I][J][r]);
+        m = (a > m) ? a : m;  // NaN does not propagate into the scale
+      }
+  return wave_max(m);
+}
+
+__device__ __forceinline__ float fp8_scale(float amax) {
+  return (amax > 0.f && __builtin_isfinite(amax)) ? amax / FP8_MAX : 1.f;
+}
+
+// Z = sx * sy * (Xq Yq) with Xq, Yq the e4m3 codes of X / sx and Y / sy
+template <int NT, bool TFORM, int MAXD = NT - 1>
+__device__ __forceinline__ void lmul_fp8(const Mat<NT>& XT, float sx, const Mat<NT>& YD,
+                                         float sy, Mat<NT>& Z) {
+  constexpr int NP = (NT + 1) / 2;
+  long rp[NT][NP], cp[NP][NT];
+  const float ix = 1.f / sx, iy = 1.f / sy;
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      if (2 * p <= I && I - (2 * p + 1) <= MAXD)
+        rp[I][p] = quant8(tile_or_zero(XT, I, 2 * p), tile_or_zero(XT, I, 2 * p + 1), ix);
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int J = 0; J < NT; ++J)
+      if (J <= 2 * p + 1 && 2 * p - J <= MAXD)
+        cp[p][J] = quant8(tile_or_zero(YD, 2 * p, J), tile_or_zero(YD, 2 * p + 1, J), iy);
+  const float sxy = sx * sy;
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int J = 0; J <= I; ++J) {
+      if (I - J > MAXD) {
+        Z.t[I][J] = zero4();
+        continue;
+      }
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int p = J / 2; p <= I / 2; ++p)
+        acc = TFORM ? mma_fp8(cp[p][J], rp[I][p], acc) : mma_fp8(rp[I][p], cp[p][J], acc);
+      Z.t[I][J] = acc * sxy;
+    }
+}
+
+// fake-quantise the lower tiles of M (x -> s * q(x / s)); returns nothing, M updated
+template <int NT>
+__device__ __forceinline__ void fp8_roundtrip(Mat<NT>& M, float s) {
+  const float inv_s = 1.f / s;
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int J = 0; J <= I; ++J) {
+      long q = quant8(M.t[I][J], zero4(), inv_s);
+      uint32_t w = (uint32_t)(uint64_t)q;
+      M.t[I][J][0] = fp8_to_f32<0>(w) * s;
+      M.t[I][J][1] = fp8_to_f32<1>(w) * s;
+      M.t[I][J][2] = fp8_to_f32<2>(w) * s;
+      M.t[I][J][3] = fp8_to_f32<3>(w) * s;
+    }
+}
+
+// ---- the two inverse variants ------------------------------------------------
+// Inputs: AD, AT (A in D- and T-form; for fp8 compute already band-masked when the
+// mask is on, since out-of-band magnitudes would otherwise set the scales).
+// Output: TT, T in T-form (row-major friendly).
+// MAXD = NT - 1 is the general case; MAXD = 1 is valid when the band mask is on with
+// N <= 16 (every tile two or more tile-diagonals below the main one is then zero in
+// A, in every intermediate and in T).
+
+template <int NT, int CMP, int MAXD = NT - 1>
+__device__ __forceinline__ void neumann_T(const Mat<NT>& AD, const Mat<NT>& AT, int N, bool mask,
+                                          Mat<NT>& TT, Fp8Counts& cnt, bool count) {
+  const int band = mask ? N : (1 << 30);
+  if (N <= 1) {
+    TT = AT;
+    if constexpr (CMP == CMP_FP8) {
+      // T - I is A itself: quantise it like every other operand
+      float sA = fp8_scale(absmax(AT));
+      if (count) fp8_count(AT, sA, sA, cnt);
+      fp8_roundtrip(TT, sA);
+    }
+    if (mask) mask_T(TT, band);
+    add_eye(TT);
+    return;
+  }
+  Mat<NT> H = AD;  // H_1 = I + A (D-form)
+  add_eye(H);
+  if constexpr (CMP == CMP_FP8) {
+    const float sA = fp8_scale(absmax(AT));
+    if (count) fp8_count(AT, sA, sA, cnt);
+    for (int k = 2; k < N; ++k) {
+      const float sH = fp8_scale(absmax(H));
+      if (count) fp8_count(H, sH, sA, cnt);
+      Mat<NT> Z;
+      lmul_fp8<NT, false, MAXD>(AT, sA, H, sH, Z);
+      add_eye(Z);
+      if (mask) mask_D(Z, band);
+      H = Z;
+    }
+    const float sH = fp8_scale(absmax(H));
+    if (count) fp8_count(H, sH, sA, cnt);
+    lmul_fp8<NT, true, MAXD>(AT, sA, H, sH, TT);  // T - I = A H_{N-1}
+    if (mask) mask_T(TT, band);
+    const float sT = fp8_scale(absmax(TT));
+    if (count) fp8_count(TT, sT, sA, cnt);
+    fp8_roundtrip(TT, sT);
+    add_eye(TT);
+  } else {
+    // Entries inside the band of a product of lower-triangular matrices only involve
+    // entries inside the band of the factors, so masking the final sum gives exactly
+    // (bit for bit) what masking A and every intermediate would.
+    for (int k = 2; k < N; ++k) {
+      Mat<NT> Z;
+      lmul<NT, CMP, false, MAXD, true>(AT, H, Z);
+      H = Z;
+    }
+    lmul<NT, CMP, true, MAXD, true>(AT, H, TT);
+    if (mask) mask_T(TT, band);
+  }
+}
+
+// exact doubling: P = I + A; X = A; for q = 1..m-1: X <- X X; P <- P + P X
+template <int NT, int CMP>
+__device__ __forceinline__ void doubling_T(const Mat<NT>& AD, const Mat<NT>& AT, Mat<NT>& PT) {
+  constexpr int C = 16 * NT;
+  constexpr int M = (C <= 16) ? 4 : (C <= 32) ? 5 : 6;  // ceil(log2 C)
+  PT = AT;
+  add_eye(PT);
+  Mat<NT> XD = AD, XT = AT;
+#pragma unroll
+  for (int q = 1; q < M; ++q) {
+    Mat<NT> ND, NTm;
+    lmul<NT, CMP, false>(XT, XD, ND);  // X^2, D-form
+    if (q + 1 < M) lmul<NT, CMP, true>(XT, XD, NTm);  // X^2, T-form (not needed last)
+    XD = ND;
+    XT = NTm;
+    // P <- P + P X  (P X = X P: every factor is a polynomial in A)
+    Mat<NT> PX;
+    lmul<NT, CMP, true>(PT, XD, PX);
+#pragma unroll
+    for (int I = 0; I < NT; ++I)
+#pragma unroll
+      for (int J = 0; J <= I; ++J) PT.t[I][J] += PX.t[I][J];
+  }
+}
+
+// ---- stores ------------------------------------------------------------------
+// T-form tile (I,J): lane (g,c) holds row 16I + c, columns 16J + 4g .. +3.
+
+template <int NT, int MAXD = NT - 1>
+__device__ __forceinline__ void store_T_f32(float* __restrict__ out, const Mat<NT>& M) {
+  constexpr int C = 16 * NT;
+  const int l = lane_id(), g = l >> 4, c = l & 15;
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int J = 0; J < NT; ++J) {
+      f32x4 v = (J <= I && I - J <= MAXD) ? M.t[I][J] : zero4();
+      *reinterpret_cast<f32x4*>(out + (size_t)(16 * I + c) * C + 16 * J + 4 * g) = v;
+    }
+}
+
+template <int NT, int MAXD = NT - 1>
+__device__ __forceinline__ void store_T_bf16(__bf16* __restrict__ out, const Mat<NT>& M) {
+  constexpr int C = 16 * NT;
+  const int l = lane_id(), g = l >> 4, c = l & 15;
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int J = 0; J < NT; ++J) {
+      f32x4 v = (J <= I && I - J <= MAXD) ? M.t[I][J] : zero4();
+      *reinterpret_cast<bf16x4*>(out + (size_t)(16 * I + c) * C + 16 * J + 4 * g) = pack4(v);
+    }
+}
+
+}  // namespace gdn
