@@ -327,6 +327,7 @@ void oracle_chunk_fwd(int Bn, int Hn, int64_t Tn, int dk, int dv, int C, const d
     double* Up = (double*)malloc(sizeof(double) * C * dv);
     double* G = (double*)malloc(sizeof(double) * C);
     double* Snew = (double*)malloc(sizeof(double) * dk * dv);
+    double* P = (double*)malloc(sizeof(double) * C * C);
     if (S0)
       memcpy(S, S0 + (size_t)bh * dk * dv, sizeof(double) * dk * dv);
     else
@@ -349,17 +350,24 @@ void oracle_chunk_fwd(int Bn, int Hn, int64_t Tn, int dk, int dv, int C, const d
           for (int d = 0; d < dk; ++d) s += W[(size_t)i * dk + d] * S[(size_t)d * dv + e];
           Up[(size_t)i * dv + e] = U[(size_t)i * dv + e] - s;
         }
-      /* O = scale (diag(e^G) Q S + P U'),  P_ij = q_i.k_j e^{G_i - G_j} [i >= j] */
+      /* P_ij = q_i.k_j e^{G_i - G_j} for j <= i, 0 otherwise */
+      for (int i = 0; i < C; ++i)
+        for (int j = 0; j < C; ++j) {
+          double v = 0.0;
+          if (j <= i) {
+            double qk = 0.0;
+            for (int d = 0; d < dk; ++d) qk += Qc[(size_t)i * dk + d] * Kc[(size_t)j * dk + d];
+            v = qk * exp(G[i] - G[j]);
+          }
+          P[(size_t)i * C + j] = v;
+        }
+      /* O = scale (diag(e^G) Q S + P U') */
       for (int i = 0; i < C; ++i)
         for (int e = 0; e < dv; ++e) {
           double qs = 0.0;
           for (int d = 0; d < dk; ++d) qs += Qc[(size_t)i * dk + d] * S[(size_t)d * dv + e];
           double pu = 0.0;
-          for (int j = 0; j <= i; ++j) {
-            double qk = 0.0;
-            for (int d = 0; d < dk; ++d) qk += Qc[(size_t)i * dk + d] * Kc[(size_t)j * dk + d];
-            pu += qk * exp(G[i] - G[j]) * Up[(size_t)j * dv + e];
-          }
+          for (int j = 0; j <= i; ++j) pu += P[(size_t)i * C + j] * Up[(size_t)j * dv + e];
           Oc[(size_t)i * dv + e] = scale * (exp(G[i]) * qs + pu);
         }
       /* S = e^{G_C} S + K^T diag(e^{G_C - G}) U' */
@@ -382,6 +390,7 @@ void oracle_chunk_fwd(int Bn, int Hn, int64_t Tn, int dk, int dv, int C, const d
     free(Up);
     free(G);
     free(Snew);
+    free(P);
   }
 }
 
