@@ -151,6 +151,89 @@ def bench_c1(torch, tri, synth, steps, warmup):
     return results
 
 
+# ------------------------------------------------------------------ c3 / c4: chunk forward
+
+C3 = dict(B=4, H=16, T=8192, d_k=128, d_v=128, C=64)
+C4 = dict(B=4, H=16, T=32768, d_k=128, d_v=128, C=64)
+
+
+def chunk_bytes_flops(cfg, variant):
+    B, H, T, dk, dv, C = (cfg[k] for k in ("B", "H", "T", "d_k", "d_v", "C"))
+    tokens = B * H * T
+    by = tokens * (2 * dk * 2 + dv * 2) + tokens * 2 * 4 + tokens * dv * 2 + B * H * dk * dv * 4
+    n_chunks = tokens // C
+    inv = (2 * (((C - 1).bit_length()) - 1) if variant[0] == "exact" else variant[1] - 1) * 2 * C ** 3
+    per_chunk = (2 * C * C * dk          # K K^T
+                 + inv                   # inverse products
+                 + 2 * C * C * dk        # W = T diag(beta e^G) K
+                 + 2 * C * C * dv        # U = T diag(beta) V
+                 + 2 * C * dk * dv       # W S
+                 + 2 * C * dk * dv       # Q S
+                 + 2 * C * C * dk        # Q K^T
+                 + 2 * C * C * dv        # P U'
+                 + 2 * dk * C * dv)      # K^T U'
+    return B * T, by, n_chunks * per_chunk
+
+
+def bench_chunk(torch, tri, synth, cfg, variants, steps, warmup, n_sets=2, stats=False):
+    B, H, T, dk, dv, C = (cfg[k] for k in ("B", "H", "T", "d_k", "d_v", "C"))
+    sets = []
+    for s in range(n_sets):
+        x = synth.prefill(3 if s == 0 else 100 + s, B, H, T, dk, dv)
+        sets.append({k: v.cuda() for k, v in x.items()})
+        del x
+    outs = [(torch.empty((B, H, T, dv), device="cuda", dtype=torch.bfloat16),
+             torch.empty((B, H, dk, dv), device="cuda")) for _ in range(n_sets)]
+    st = torch.zeros(4, dtype=torch.int64, device="cuda") if stats else None
+    res = {}
+    for v in variants:
+        mode, N, mask, compute = v
+
+        def launch(i):
+            x = sets[i]
+            tri.gdn_chunk_fwd(x["Q"], x["K"], x["V"], x["beta"], x["g"], C=C, scale=dk ** -0.5,
+                              mode=mode, N=N, mask=mask, compute=compute, O=outs[i][0],
+                              S_out=outs[i][1], stats=st)
+        ms, _ = time_launches(torch, launch, n_sets, steps, warmup)
+        tok, by, fl = chunk_bytes_flops(cfg, v)
+        name = ("exact" if mode == "exact" else "N%d_%s" % (N, "masked" if mask else "unmasked")) + "_" + compute
+        res[name] = {"ms_per_step": ms, "tokens_per_s": tok / (ms * 1e-3),
+                     "hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "mfma_frac": fl / (ms * 1e-3) / 1e12 / (FP8_PEAK_TFLOPS if compute == "fp8" else BF16_PEAK_TFLOPS),
+                     "bytes": by, "flops": fl}
+        if stats:
+            launch(0)
+            torch.cuda.synchronize()
+            res[name]["fp8_stats"] = dict(zip(tri.FP8_STATS_FIELDS, st.cpu().tolist()))
+    del sets, outs
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_wy(torch, tri, synth, steps, warmup):
+    B, H, T, dk, dv, C = 2, 16, 16384, 128, 128, 64
+    nb = B * H * T // C
+    sets = [{k: v.cuda() for k, v in synth.blocks(2 if s == 0 else 200 + s, nb, C, dk, k_dtype="bf16",
+                                                   d_v=dv).items()} for s in range(2)]
+    outs = [(torch.empty((nb, C, dk), device="cuda", dtype=torch.bfloat16),
+             torch.empty((nb, C, dv), device="cuda", dtype=torch.bfloat16)) for _ in range(2)]
+
+    def launch(i):
+        x = sets[i]
+        tri.gdn_wy(x["K"], x["beta"], x["g"], x["V"], C=C, mode="neumann", N=3, mask=True,
+                   W_out=outs[i][0], U_out=outs[i][1])
+    ms, _ = time_launches(torch, launch, 2, steps, warmup)
+    tokens = B * T
+    by = B * H * T * (dk * 2 + dv * 2 + 8 + dk * 2 + dv * 2)
+    fl = nb * (2 * C * C * dk + 2 * 2 * C ** 3 + 2 * C * C * dk + 2 * C * C * dv)
+    del sets, outs
+    torch.cuda.empty_cache()
+    return {"C64_N3_masked": {"ms_per_step": ms, "tokens_per_s": tokens / (ms * 1e-3),
+                              "hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                              "mfma_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                              "bytes": by, "flops": fl}}
+
+
 def profile_c1(torch, tri, synth, n):
     """Headline launch n times on rotating buffer sets, then a plain 256 MiB copy n
     times: the copy's FETCH_SIZE / WRITE_SIZE per dispatch calibrate the counters."""
@@ -245,6 +328,25 @@ def main():
         "variants": c1,
         "source_digest": source_digest(),
     }
+    if args.only in ("all", "c3"):
+        c3 = bench_chunk(torch, tri, synth, C3,
+                         [("neumann", 3, True, "bf16"), ("neumann", 3, False, "bf16"),
+                          ("exact", 0, False, "bf16")], max(5, args.steps // 5), 2)
+        h3 = c3["N3_masked_bf16"]
+        out["chunk_fwd"] = {
+            "workload": "chunk-wise GDN prefill forward, B=4 H=16 seq=8192 d_k=d_v=128 C=64, "
+                        "N=3 band-masked inverse, bf16 Q/K/V/O, fp32 state",
+            "tokens_per_s": h3["tokens_per_s"], "ms_per_step": h3["ms_per_step"],
+            "roofline": {"bound": "hbm", "achieved": h3["bytes"] / (h3["ms_per_step"] * 1e-3) / 1e9,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": h3["hbm_frac"],
+                         "traffic": load_traffic("chunk_fwd_kernel<128,0,1,1>")},
+            "variants": c3}
+    if args.only in ("all", "c2"):
+        out["wy"] = bench_wy(torch, tri, synth, max(5, args.steps // 5), 2)
+    if args.only in ("all", "c4"):
+        out["chunk_fwd_fp8"] = bench_chunk(torch, tri, synth, C4,
+                                           [("neumann", 3, True, "fp8"), ("neumann", 3, False, "fp8")],
+                                           3, 1, n_sets=1, stats=True)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline_c1()
     print(json.dumps(out))

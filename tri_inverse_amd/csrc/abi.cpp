@@ -148,9 +148,35 @@ gdn_status gdn_tri_inverse_exact(const gdn_blocks* in, int32_t compute, void* T_
 gdn_status gdn_wy(const gdn_blocks* in, const void* T, int32_t t_dtype, const gdn_inverse_cfg* inv,
                   const void* V, int32_t d_v, int32_t gate_k, void* W_out, void* U_out,
                   int32_t out_dtype, void* stream) {
-  (void)in; (void)T; (void)t_dtype; (void)inv; (void)V; (void)d_v; (void)gate_k;
-  (void)W_out; (void)U_out; (void)out_dtype; (void)stream;
-  return GDN_ERR_UNSUPPORTED;
+  int src = 0;
+  if (in && in->A) return GDN_ERR_UNSUPPORTED;  // the products need K itself
+  gdn_status st = check_blocks(in, false, false, &src);
+  if (st != GDN_OK) return st;
+  if (T) {
+    if (t_dtype != GDN_F32 && t_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
+  } else {
+    if (!inv) return GDN_ERR_NULL_POINTER;
+    if (inv->mode != GDN_INV_NEUMANN && inv->mode != GDN_INV_EXACT) return GDN_ERR_BAD_SHAPE;
+    if (inv->mode == GDN_INV_NEUMANN && (inv->N < 1 || inv->N >= in->C)) return GDN_ERR_BAD_SHAPE;
+    if (inv->mask != 0 && inv->mask != 1) return GDN_ERR_BAD_SHAPE;
+    if (inv->compute != GDN_BF16) {
+      if (inv->compute == GDN_F32 || inv->compute == GDN_FP8_E4M3) return GDN_ERR_UNSUPPORTED;
+      return GDN_ERR_BAD_DTYPE;
+    }
+  }
+  if (d_v <= 0) return GDN_ERR_BAD_SHAPE;
+  if (gate_k != 0 && gate_k != 1) return GDN_ERR_BAD_SHAPE;
+  if (out_dtype != GDN_F32 && out_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
+  if (!(in->C == 32 || in->C == 64)) return GDN_ERR_UNSUPPORTED;
+  if (!(in->d_k == 64 || in->d_k == 128) || !(d_v == 64 || d_v == 128)) return GDN_ERR_UNSUPPORTED;
+  if (in->n_blocks == 0) return GDN_OK;
+  if (!V || !W_out || !U_out) return GDN_ERR_NULL_POINTER;
+  if (!aligned16(V) || !aligned16(W_out) || !aligned16(U_out) || (T && !aligned16(T)))
+    return GDN_ERR_BAD_ALIGNMENT;
+  const int mode = T ? 0 : inv->mode, N = T ? 0 : inv->N, mask = T ? 0 : inv->mask;
+  return launch_result(gdn::launch_wy(to_args(in), T, t_dtype == GDN_BF16, mode, N, mask, V, d_v,
+                                      gate_k, W_out, U_out, out_dtype == GDN_BF16,
+                                      as_stream(stream)));
 }
 
 gdn_status gdn_chunk_fwd(const void* Q, const void* K, const void* V, int32_t qkv_dtype,
@@ -158,10 +184,59 @@ gdn_status gdn_chunk_fwd(const void* Q, const void* K, const void* V, int32_t qk
                          int32_t o_dtype, float* S_out, int32_t B, int32_t H, int64_t T,
                          int32_t d_k, int32_t d_v, int32_t C, float scale,
                          const gdn_inverse_cfg* inv, uint64_t* stats, void* stream) {
-  (void)Q; (void)K; (void)V; (void)qkv_dtype; (void)beta; (void)g; (void)S0; (void)O;
-  (void)o_dtype; (void)S_out; (void)B; (void)H; (void)T; (void)d_k; (void)d_v; (void)C;
-  (void)scale; (void)inv; (void)stats; (void)stream;
-  return GDN_ERR_UNSUPPORTED;
+  if (!inv) return GDN_ERR_NULL_POINTER;
+  if (B < 0 || H < 0 || T < 0 || d_k <= 0 || d_v <= 0 || C <= 0) return GDN_ERR_BAD_SHAPE;
+  if (qkv_dtype != GDN_BF16) return (qkv_dtype == GDN_F32) ? GDN_ERR_UNSUPPORTED : GDN_ERR_BAD_DTYPE;
+  if (o_dtype != GDN_F32 && o_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
+  if (!chunk_ok(C)) return GDN_ERR_UNSUPPORTED;
+  if (T % C != 0) return GDN_ERR_BAD_SHAPE;
+  if (inv->mode != GDN_INV_NEUMANN && inv->mode != GDN_INV_EXACT) return GDN_ERR_BAD_SHAPE;
+  if (inv->mode == GDN_INV_NEUMANN && (inv->N < 1 || inv->N >= C)) return GDN_ERR_BAD_SHAPE;
+  if (inv->mask != 0 && inv->mask != 1) return GDN_ERR_BAD_SHAPE;
+  if (inv->compute != GDN_BF16 && inv->compute != GDN_FP8_E4M3 && inv->compute != GDN_F32)
+    return GDN_ERR_BAD_DTYPE;
+  if (inv->compute == GDN_F32) return GDN_ERR_UNSUPPORTED;
+  if (inv->compute == GDN_FP8_E4M3 && inv->mode != GDN_INV_NEUMANN) return GDN_ERR_UNSUPPORTED;
+  if (C != 64) return GDN_ERR_UNSUPPORTED;
+  if (!(d_k == 64 || d_k == 128)) return GDN_ERR_UNSUPPORTED;
+  if (d_v % 32 != 0 || d_v > 256) return GDN_ERR_UNSUPPORTED;
+  if (stats && !aligned16(stats)) return GDN_ERR_BAD_ALIGNMENT;
+  hipStream_t s = as_stream(stream);
+  auto* st64 = reinterpret_cast<unsigned long long*>(stats);
+  const bool empty = (int64_t)B * H == 0 || T == 0;
+  if (!empty) {
+    if (!Q || !K || !V || !beta || !g || !O || !S_out) return GDN_ERR_NULL_POINTER;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(beta) || !aligned16(g) ||
+        !aligned16(O) || !aligned16(S_out) || (S0 && !aligned16(S0)))
+      return GDN_ERR_BAD_ALIGNMENT;
+  }
+  if (st64) {
+    gdn::launch_zero_stats(st64, s);
+    if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;
+  }
+  if (empty) return GDN_OK;
+  gdn::ChunkLaunch p;
+  p.Q = Q;
+  p.K = K;
+  p.V = V;
+  p.beta = beta;
+  p.g = g;
+  p.S0 = S0;
+  p.O = O;
+  p.S_out = S_out;
+  p.stats = st64;
+  p.T = T;
+  p.B = B;
+  p.H = H;
+  p.d_k = d_k;
+  p.d_v = d_v;
+  p.o_bf16 = o_dtype == GDN_BF16;
+  p.mode = inv->mode;
+  p.N = inv->N;
+  p.mask = inv->mask;
+  p.cmp = inv->compute;
+  p.scale = scale;
+  return launch_result(gdn::launch_chunk_fwd(p, s));
 }
 
 }  // extern "C"

@@ -28,4 +28,29 @@ int launch_neumann(const BlocksArgs& a, int src, int N, int mask, int cmp, void*
 int launch_exact(const BlocksArgs& a, int src, int cmp, void* T_out, int t_bf16, hipStream_t s);
 void launch_zero_stats(unsigned long long* stats, hipStream_t s);
 
+// WY products; T given (t_bf16 selects its dtype) or formed with (mode, N, mask);
+// C in {32, 64}, d_k and d_v in {64, 128}
+int launch_wy(const BlocksArgs& a, const void* T, int t_bf16, int mode, int N, int mask,
+              const void* V, int d_v, int gate_k, void* W_out, void* U_out, int out_bf16,
+              hipStream_t s);
+
+struct ChunkLaunch {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const float* beta;
+  const float* g;
+  const float* S0;
+  void* O;
+  float* S_out;
+  unsigned long long* stats;
+  int64_t T;
+  int B, H, d_k, d_v;
+  int o_bf16;
+  int mode, N, mask, cmp;
+  float scale;
+};
+// chunk-wise forward, C = 64; d_k in {64, 128}; d_v a multiple of 32
+int launch_chunk_fwd(const ChunkLaunch& p, hipStream_t s);
+
 }  // namespace gdn

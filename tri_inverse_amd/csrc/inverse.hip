@@ -12,7 +12,6 @@ namespace gdn {
 
 // input source of A for one block
 enum : int { SRC_A = 0, SRC_K_BF16 = 1, SRC_K_F32 = 2 };
-enum : int { MODE_NEUMANN = 0, MODE_EXACT = 1 };
 
 // Raw inputs of one block (what the prefetch holds): K fragments + lane gate values,
 // or A's lower tiles.
