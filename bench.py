@@ -254,6 +254,24 @@ def profile_c1(torch, tri, synth, n):
     torch.cuda.synchronize()
 
 
+def profile_c3(torch, tri, synth, n):
+    """Prefill forward (B=4 H=16 seq 8192, N=3 masked) n times, then the 256 MiB copy."""
+    cfg = C3
+    x = {k: v.cuda() for k, v in synth.prefill(3, cfg["B"], cfg["H"], cfg["T"], cfg["d_k"],
+                                                cfg["d_v"]).items()}
+    O = torch.empty((cfg["B"], cfg["H"], cfg["T"], cfg["d_v"]), device="cuda", dtype=torch.bfloat16)
+    S = torch.empty((cfg["B"], cfg["H"], cfg["d_k"], cfg["d_v"]), device="cuda")
+    for _ in range(n):
+        tri.gdn_chunk_fwd(x["Q"], x["K"], x["V"], x["beta"], x["g"], C=64, scale=cfg["d_k"] ** -0.5,
+                          N=3, mask=True, O=O, S_out=S)
+    torch.cuda.synchronize()
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(n):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 def cpu_baseline_c1():
     import oracle
     import synth
@@ -299,7 +317,10 @@ def main():
 
     torch.cuda.set_device(0)
     if args.profile_launches:
-        profile_c1(torch, tri, synth, args.profile_launches)
+        if args.only == "c3":
+            profile_c3(torch, tri, synth, args.profile_launches)
+        else:
+            profile_c1(torch, tri, synth, args.profile_launches)
         return
     c1 = bench_c1(torch, tri, synth, args.steps, args.warmup)
     head = c1["N3_masked_Tf32"]

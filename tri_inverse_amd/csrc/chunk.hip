@@ -20,11 +20,12 @@
 // Work split: one workgroup per (batch, head, 32 columns of d_v), four waves:
 //   wave 0, 1  consumers: each owns 16 state columns S[:, 16v..16v+15] (fp32, in
 //              registers) and runs the sequential scan;
-//   wave 2     producer: gates, A, T for chunk c+1 (T as bf16 row-pack fragments);
-//   wave 3     producer: P for chunk c+1 (hi/lo bf16), Q and K staged for the
-//              consumers, K^T for the state update.
+//   wave 2     producer: gates, A and T (bf16 row-pack fragments) of the next chunk;
+//   wave 3     producer: P (hi/lo bf16) of the current chunk; K and Q fragments and
+//              K^T of the next chunk.
 // Producers fill one half of a double-buffered LDS area while the consumers read
-// the other; one barrier per chunk hands over.  Y, U' and P enter the MFMAs as hi/lo
+// the other; one barrier per chunk hands over, and every global load is issued at
+// least one iteration before its data is used (see the schedule above the kernel).  Y, U' and P enter the MFMAs as hi/lo
 // bf16 pairs (x = xh + xl, both bf16; products take xh yh + xl yh + xh yl), which
 // brings the error of O and S to about 1e-4 relative (rounding each of them to a
 // single bf16 would cost 1e-3 or more each), leaving the bf16 rounding of O itself
@@ -68,8 +69,11 @@ struct ChunkLds {
   __bf16 kt[DK][CH + KT_PAD];      // K^T: kt[d][token]
   float beta[CH];
   float eg[CH];                    // exp(G_i)
+  float eng[CH];                   // exp(-G_i)
   float egcg[CH];                  // exp(G_C - G_i)
+  float G[CH];                     // G_i
   float egc;                       // exp(G_C)
+  int split;                       // exp(-G) finite over the chunk
 };
 
 // 8 consecutive-in-slot bf16 of row `row` for k-pair p in the permuted order
@@ -96,19 +100,27 @@ __device__ __forceinline__ void pack8_hilo(const f32x4& a, const f32x4& b, bf16x
   lo = pack8(a - unpack_lo(hi), b - unpack_hi(hi));
 }
 
-// ---- producer wave 2: gates, A, T ------------------------------------------------
+// raw inputs of one chunk for the A/T producer (held in registers one chunk ahead)
+template <int DK>
+struct KChunk {
+  KBlock<CNT, DK> kb;
+  __device__ __forceinline__ void load(const ChunkArgs& a, int64_t row0) {
+    const int l = lane_id(), c = l & 15;
+#pragma unroll
+    for (int I = 0; I < CNT; ++I)
+#pragma unroll
+      for (int p = 0; p < DK / 32; ++p) kb.kf[I][p] = load_rowpack<DK>(a.K + row0 * DK, 16 * I + c, p);
+    kb.gl = a.g[row0 + l];
+    kb.bl = a.beta[row0 + l];
+  }
+};
+
+// ---- producer wave 2: gates, A, T, and the K layouts the other waves read ----------
 template <int DK, int MODE, int CMP, int MAXD>
-__device__ __forceinline__ void produce_T(const ChunkArgs& a, int64_t row0, ChunkLds<DK>& L,
+__device__ __forceinline__ void produce_T(const ChunkArgs& a, const KChunk<DK>& in, ChunkLds<DK>& L,
                                           Fp8Counts& cnt, bool count) {
   const int l = lane_id(), g = l >> 4, c = l & 15;
-  // K rows in the permuted order (also the consumers' left-operand fragments)
-  KBlock<CNT, DK> kb;
-#pragma unroll
-  for (int I = 0; I < CNT; ++I)
-#pragma unroll
-    for (int p = 0; p < DK / 32; ++p) kb.kf[I][p] = load_rowpack<DK>(a.K + row0 * DK, 16 * I + c, p);
-  kb.gl = a.g[row0 + l];
-  kb.bl = a.beta[row0 + l];
+  const KBlock<CNT, DK>& kb = in.kb;
   Gates<CNT> gt;
   gates_from_lanes<CNT>(kb.gl, kb.bl, false, gt);
   Mat<CNT> S, AD, AT, TT;
@@ -127,38 +139,33 @@ __device__ __forceinline__ void produce_T(const ChunkArgs& a, int64_t row0, Chun
       if (2 * p <= I && I - (2 * p + 1) <= MAXD)
         L.trp[I][p][l] = pack8(tile_or_zero(TT, I, 2 * p), tile_or_zero(TT, I, 2 * p + 1));
     }
-#pragma unroll
-  for (int I = 0; I < CNT; ++I)
-#pragma unroll
-    for (int p = 0; p < DK / 32; ++p) L.krp[I][p][l] = kb.kf[I][p];
-  // gate factors for the consumers
+  // gate factors
   const float GC = __shfl(gt.Gl, CH - 1, 64);
   L.beta[l] = kb.bl;
   L.eg[l] = __expf(gt.Gl);
+  L.eng[l] = __expf(-gt.Gl);
   L.egcg[l] = __expf(GC - gt.Gl);
-  if (l == 0) L.egc = __expf(GC);
+  L.G[l] = gt.Gl;
+  if (l == 0) {
+    L.egc = __expf(GC);
+    L.split = gt.split ? 1 : 0;
+  }
 }
 
-// ---- producer wave 3: P (hi/lo), Q staging, K^T ----------------------------------
+// ---- producer wave 3: P = Q K^T .* exp(G_i - G_j) .* [i >= j] (hi/lo) -------------
+// Reads K and Q fragments and the gates of the same chunk from LDS.
 template <int DK>
-__device__ __forceinline__ void produce_P(const ChunkArgs& a, int64_t row0, ChunkLds<DK>& L) {
+__device__ __forceinline__ void produce_P(const ChunkLds<DK>& Lin, ChunkLds<DK>& Lout) {
   const int l = lane_id(), g = l >> 4, c = l & 15;
-  bf16x8 qf[CNT][DK / 32], kf[CNT][DK / 32];
-#pragma unroll
-  for (int I = 0; I < CNT; ++I)
-#pragma unroll
-    for (int p = 0; p < DK / 32; ++p) {
-      qf[I][p] = load_rowpack<DK>(a.Q + row0 * DK, 16 * I + c, p);
-      kf[I][p] = load_rowpack<DK>(a.K + row0 * DK, 16 * I + c, p);
-    }
-  const float Gl = wave_inclusive_scan(a.g[row0 + l]);
-  const bool split = wave_min(Gl) >= -80.f;
-  const float el = __expf(Gl), nl = __expf(-Gl);
+  const bool split = Lin.split != 0;
   const int lo_ = 4 * g - c;
 #pragma unroll
   for (int I = 0; I < CNT; ++I) {
-    const float rowf = __shfl(el, 16 * I + c, 64);   // exp(G_i), i = 16I + c
-    const float Gi = __shfl(Gl, 16 * I + c, 64);
+    const float rowf = Lin.eg[16 * I + c];  // exp(G_i), i = 16I + c
+    const float Gi = Lin.G[16 * I + c];
+    bf16x8 qf[DK / 32];
+#pragma unroll
+    for (int p = 0; p < DK / 32; ++p) qf[p] = Lin.qrp[I][p][l];
     f32x4 pt[CNT];
 #pragma unroll
     for (int J = 0; J < CNT; ++J) {
@@ -169,15 +176,12 @@ __device__ __forceinline__ void produce_P(const ChunkArgs& a, int64_t row0, Chun
       // T-form tile (I,J): lane (g,c) reg r = q_{16I+c} . k_{16J+4g+r}
       f32x4 acc = zero4();
 #pragma unroll
-      for (int p = 0; p < DK / 32; ++p) acc = mma_bf16(kf[J][p], qf[I][p], acc);
+      for (int p = 0; p < DK / 32; ++p) acc = mma_bf16(Lin.krp[J][p][l], qf[p], acc);
+      const f32x4 ncol = *reinterpret_cast<const f32x4*>(&Lin.eng[16 * J + 4 * g]);
+      const f32x4 Gcol = *reinterpret_cast<const f32x4*>(&Lin.G[16 * J + 4 * g]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int jj = 16 * J + 4 * g + r;
-        float f;
-        if (split)
-          f = rowf * __shfl(nl, jj, 64);
-        else
-          f = __expf(Gi - __shfl(Gl, jj, 64));
+        const float f = split ? rowf * ncol[r] : __expf(Gi - Gcol[r]);
         const int d = 16 * (I - J) - r - lo_;       // i - j
         acc[r] = (d >= 0) ? acc[r] * f : 0.f;
       }
@@ -188,58 +192,102 @@ __device__ __forceinline__ void produce_P(const ChunkArgs& a, int64_t row0, Chun
       if (2 * p <= I) {
         bf16x8 h, lw;
         pack8_hilo(pt[2 * p], (2 * p + 1 < CNT) ? pt[2 * p + 1] : zero4(), h, lw);
-        L.prh[I][p][l] = h;
-        L.prl[I][p][l] = lw;
+        Lout.prh[I][p][l] = h;
+        Lout.prl[I][p][l] = lw;
       }
     }
   }
-  // stage Q fragments and K^T for the consumers
-#pragma unroll
-  for (int I = 0; I < CNT; ++I)
-#pragma unroll
-    for (int p = 0; p < DK / 32; ++p) {
-      L.qrp[I][p][l] = qf[I][p];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int d = 32 * p + 16 * (t >> 2) + 4 * g + (t & 3);
-        L.kt[d][16 * I + c] = kf[I][p][t];
-      }
-    }
 }
 
 // ---- consumer waves: the state scan ----------------------------------------------
-template <int DK, int MAXD>
+// Each phase first gathers the LDS fragments it needs into registers, then issues
+// its MFMAs with independent accumulators adjacent, so LDS latency and MFMA latency
+// overlap instead of serialising.
+template <int DK, int MAXD, bool OBF16>
 struct Consumer {
+  static constexpr int NP = DK / 32;
   f32x4 S[DK / 16];  // D-form tiles: lane (g,c) reg r = S[16a + 4g + r][col0 + c]
+  f32x4 qsg[CNT];    // previous chunk: e^{G_i} (Q S)_i in T-form (row 16I + c)
+  bf16x8 cuh[2], cul[2];  // previous chunk: U' column packs, hi / lo
 
   __device__ __forceinline__ void load_v(const ChunkArgs& a, int64_t row0, int col0, f32x4 (&v)[CNT]) {
     const int l = lane_id(), g = l >> 4, c = l & 15;
+    const __bf16* base = a.V + (row0 + 4 * g) * a.dv + col0 + c;
 #pragma unroll
     for (int I = 0; I < CNT; ++I)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        v[I][r] = (float)a.V[(row0 + 16 * I + 4 * g + r) * a.dv + col0 + c];
+      for (int r = 0; r < 4; ++r) v[I][r] = (float)base[(16 * I + r) * a.dv];
   }
 
-  __device__ __forceinline__ void step(const ChunkArgs& a, int64_t row0, int col0,
-                                       const ChunkLds<DK>& L, const f32x4 (&vd)[CNT]) {
+  // O of the previous chunk: scale (e^G Q S + P U'), T-form rows 16I + c
+  __device__ __forceinline__ void emit_O(const ChunkArgs& a, int64_t row0, int col0,
+                                         const ChunkLds<DK>& L) {
     const int l = lane_id(), g = l >> 4, c = l & 15;
-    constexpr int NP = DK / 32;
+    bf16x8 ph[CNT][2], pl[CNT][2];
+#pragma unroll
+    for (int I = 0; I < CNT; ++I)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        if (2 * p <= I) {
+          ph[I][p] = L.prh[I][p][l];
+          pl[I][p] = L.prl[I][p][l];
+        }
+    f32x4 acc[CNT];
+#pragma unroll
+    for (int I = 0; I < CNT; ++I) acc[I] = qsg[I];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int k = 0; k < 3; ++k)
+#pragma unroll
+        for (int I = 0; I < CNT; ++I)
+          if (2 * p <= I) {
+            const bf16x8& uu = (k == 1) ? cul[p] : cuh[p];
+            const bf16x8& pp = (k == 2) ? pl[I][p] : ph[I][p];
+            acc[I] = mma_bf16(uu, pp, acc[I]);
+          }
+#pragma unroll
+    for (int I = 0; I < CNT; ++I) {
+      const f32x4 o = acc[I] * a.scale;
+      const int64_t off = (row0 + 16 * I + c) * a.dv + col0 + 4 * g;
+      if constexpr (OBF16)
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.O) + off) = pack4(o);
+      else
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.O) + off) = o;
+    }
+  }
+
+  // state part of one chunk: K S, Q S, Y, U' = T Y, state update; keeps e^G Q S and U'
+  __device__ __forceinline__ void step(const ChunkLds<DK>& L, const f32x4 (&vd)[CNT]) {
+    const int l = lane_id(), g = l >> 4, c = l & 15;
     bf16x8 cps[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) cps[p] = pack8(S[2 * p], S[2 * p + 1]);
-    // K S (D-form) and Q S (T-form), contraction over d_k
-    f32x4 ks[CNT], qs[CNT];
+    // K S (D-form) and Q S (T-form), contraction over d_k; two row tiles at a time
+    f32x4 ks[CNT];
 #pragma unroll
-    for (int I = 0; I < CNT; ++I) {
-      f32x4 acck = zero4(), accq = zero4();
+    for (int I0 = 0; I0 < CNT; I0 += 2) {
+      bf16x8 kf[2][NP], qf[2][NP];
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        acck = mma_bf16(L.krp[I][p][l], cps[p], acck);
-        accq = mma_bf16(cps[p], L.qrp[I][p][l], accq);
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          kf[i][p] = L.krp[I0 + i][p][l];
+          qf[i][p] = L.qrp[I0 + i][p][l];
+        }
+      f32x4 ak[2] = {zero4(), zero4()}, aq[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          ak[i] = mma_bf16(kf[i][p], cps[p], ak[i]);
+          aq[i] = mma_bf16(cps[p], qf[i][p], aq[i]);
+        }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        ks[I0 + i] = ak[i];
+        qsg[I0 + i] = aq[i] * L.eg[16 * (I0 + i) + c];
       }
-      ks[I] = acck;
-      qs[I] = accq;
     }
     // Y = diag(beta) (V - diag(e^G) K S), D-form rows 16I + 4g + r
     f32x4 y[CNT];
@@ -253,44 +301,24 @@ struct Consumer {
     pack8_hilo(y[0], y[1], cyh[0], cyl[0]);
     pack8_hilo(y[2], y[3], cyh[1], cyl[1]);
     // U' = T Y (D-form), Y as a hi/lo pair
+    bf16x8 tf[CNT][2];
+#pragma unroll
+    for (int I = 0; I < CNT; ++I)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        if (2 * p <= I && I - (2 * p + 1) <= MAXD) tf[I][p] = L.trp[I][p][l];
     f32x4 u[CNT];
 #pragma unroll
-    for (int I = 0; I < CNT; ++I) {
-      f32x4 acc = zero4();
+    for (int I = 0; I < CNT; ++I) u[I] = zero4();
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
-        if (2 * p <= I && I - (2 * p + 1) <= MAXD) {
-          const bf16x8 t = L.trp[I][p][l];
-          acc = mma_bf16(t, cyh[p], acc);
-          acc = mma_bf16(t, cyl[p], acc);
-        }
-      u[I] = acc;
-    }
-    bf16x8 cuh[2], cul[2];
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int I = 0; I < CNT; ++I)
+          if (2 * p <= I && I - (2 * p + 1) <= MAXD) u[I] = mma_bf16(tf[I][p], k ? cyl[p] : cyh[p], u[I]);
     pack8_hilo(u[0], u[1], cuh[0], cul[0]);
     pack8_hilo(u[2], u[3], cuh[1], cul[1]);
-    // O = scale (diag(e^G) Q S + P U'), T-form: lane (g,c) holds row 16I + c, cols 4g..4g+3
-#pragma unroll
-    for (int I = 0; I < CNT; ++I) {
-      const float egi = L.eg[16 * I + c];
-      f32x4 acc = qs[I] * egi;
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-        if (2 * p <= I) {
-          const bf16x8 ph = L.prh[I][p][l], pl = L.prl[I][p][l];
-          acc = mma_bf16(cuh[p], ph, acc);
-          acc = mma_bf16(cul[p], ph, acc);
-          acc = mma_bf16(cuh[p], pl, acc);
-        }
-      acc = acc * a.scale;
-      const int64_t orow = row0 + 16 * I + c;
-      if (a.o_bf16) {
-        *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.O) + orow * a.dv + col0 + 4 * g) =
-            pack4(acc);
-      } else {
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.O) + orow * a.dv + col0 + 4 * g) = acc;
-      }
-    }
     // S <- e^{G_C} S + K^T diag(e^{G_C - G}) U'
     f32x4 ut[CNT];
 #pragma unroll
@@ -300,22 +328,37 @@ struct Consumer {
     pack8_hilo(ut[2], ut[3], cth[1], ctl[1]);
     const float egc = L.egc;
 #pragma unroll
-    for (int A = 0; A < DK / 16; ++A) {
-      f32x4 acc = S[A] * egc;
+    for (int A0 = 0; A0 < DK / 16; A0 += 4) {
+      bf16x8 kt[4][2];
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const __bf16* kr = &L.kt[16 * A + c][32 * p + 4 * g];
-        const bf16x8 kfr = join8(*reinterpret_cast<const bf16x4*>(kr),
-                                 *reinterpret_cast<const bf16x4*>(kr + 16));
-        acc = mma_bf16(kfr, cth[p], acc);
-        acc = mma_bf16(kfr, ctl[p], acc);
-      }
-      S[A] = acc;
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const __bf16* kr = &L.kt[16 * (A0 + i) + c][32 * p + 4 * g];
+          kt[i][p] = join8(*reinterpret_cast<const bf16x4*>(kr), *reinterpret_cast<const bf16x4*>(kr + 16));
+        }
+      f32x4 acc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = S[A0 + i] * egc;
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] = mma_bf16(kt[i][p], k ? ctl[p] : cth[p], acc[i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[A0 + i] = acc[i];
     }
   }
 };
 
-template <int DK, int MODE, int CMP, int MAXD>
+// Schedule (iteration c = 0 .. nchunks, one barrier each, buffers by chunk parity):
+//   wave 2: T and gates of chunk c+1 (its K rows were loaded one iteration earlier;
+//           chunk c+2's rows are loaded now)
+//   wave 3: P of chunk c from chunk c's K/Q fragments in LDS; K and Q rows of chunk
+//           c+1 loaded now and staged (fragments, K^T) at the end of the iteration
+//   waves 0, 1: state part of chunk c, and O of chunk c-1 (needs P of chunk c-1)
+template <int DK, int MODE, int CMP, int MAXD, bool OBF16>
 __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkArgs a) {
   __shared__ ChunkLds<DK> lds[2];
   const int wave = threadIdx.x / WAVE;
@@ -331,22 +374,29 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkArgs a) {
   const int64_t nchunks = a.T / CH;
   const int64_t head_row0 = (int64_t)bh * a.T;
   const bool count = (CMP == CMP_FP8) && a.stats != nullptr;
-  Fp8Counts cnt{0, 0, 0, 0};
 
-  if (wave >= 2) {
-    // producers: chunk 0 first, then chunk c + 1 while the consumers do chunk c
-    for (int64_t ci = 0; ci <= nchunks; ++ci) {
-      if (ci < nchunks) {
-        ChunkLds<DK>& L = lds[ci & 1];
-        if (wave == 2)
-          produce_T<DK, MODE, CMP, MAXD>(a, head_row0 + ci * CH, L, cnt, count);
-        else
-          produce_P<DK>(a, head_row0 + ci * CH, L);
-      }
+  if (wave == 2) {
+    Fp8Counts cnt{0, 0, 0, 0};
+    // ping-pong register buffers: a buffer's rows are consumed one full iteration
+    // (one barrier) after their loads are issued
+    KChunk<DK> b0, b1;
+    b0.load(a, head_row0);
+    produce_T<DK, MODE, CMP, MAXD>(a, b0, lds[0], cnt, count);
+    if (nchunks > 1) b0.load(a, head_row0 + CH);
+    __syncthreads();
+    for (int64_t ci = 0; ci <= nchunks; ci += 2) {
+      // iteration ci: T of chunk ci+1 from b0, rows of chunk ci+2 into b1
+      if (ci + 2 < nchunks) b1.load(a, head_row0 + (ci + 2) * CH);
+      if (ci + 1 < nchunks) produce_T<DK, MODE, CMP, MAXD>(a, b0, lds[(ci + 1) & 1], cnt, count);
+      __syncthreads();
+      if (ci + 1 > nchunks) break;
+      // iteration ci+1: T of chunk ci+2 from b1, rows of chunk ci+3 into b0
+      if (ci + 3 < nchunks) b0.load(a, head_row0 + (ci + 3) * CH);
+      if (ci + 2 < nchunks) produce_T<DK, MODE, CMP, MAXD>(a, b1, lds[(ci + 2) & 1], cnt, count);
       __syncthreads();
     }
     if constexpr (CMP == CMP_FP8) {
-      if (wave == 2 && count) {
+      if (count) {
         uint32_t v0 = wave_sum_u32(cnt.nonfinite), v1 = wave_sum_u32(cnt.sat_dyn);
         uint32_t v2 = wave_sum_u32(cnt.sat_static), v3 = wave_sum_u32(cnt.underflow);
         if (l == 0) {
@@ -359,24 +409,69 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkArgs a) {
     }
     return;
   }
+  if (wave == 3) {
+    // stages chunk c+1's K fragments, K^T and Q fragments at the end of iteration c;
+    // their rows are loaded at the start of the iteration, so the P computation of
+    // chunk c hides the load latency
+    auto stage = [&](int64_t row0, ChunkLds<DK>& L, const bf16x8 (&kq)[CNT][DK / 32],
+                     const bf16x8 (&qq)[CNT][DK / 32]) {
+#pragma unroll
+      for (int I = 0; I < CNT; ++I)
+#pragma unroll
+        for (int p = 0; p < DK / 32; ++p) {
+          L.krp[I][p][l] = kq[I][p];
+          L.qrp[I][p][l] = qq[I][p];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const int d = 32 * p + 16 * (t >> 2) + 4 * g + (t & 3);
+            L.kt[d][16 * I + c] = kq[I][p][t];
+          }
+        }
+    };
+    bf16x8 kq[CNT][DK / 32], qq[CNT][DK / 32];
+    auto load = [&](int64_t row0) {
+#pragma unroll
+      for (int I = 0; I < CNT; ++I)
+#pragma unroll
+        for (int p = 0; p < DK / 32; ++p) {
+          kq[I][p] = load_rowpack<DK>(a.K + row0 * DK, 16 * I + c, p);
+          qq[I][p] = load_rowpack<DK>(a.Q + row0 * DK, 16 * I + c, p);
+        }
+    };
+    load(head_row0);
+    stage(head_row0, lds[0], kq, qq);
+    __syncthreads();
+    for (int64_t ci = 0; ci <= nchunks; ++ci) {
+      const bool more = ci + 1 < nchunks;
+      if (more) load(head_row0 + (ci + 1) * CH);
+      if (ci < nchunks) produce_P<DK>(lds[ci & 1], lds[ci & 1]);
+      if (more) stage(head_row0 + (ci + 1) * CH, lds[(ci + 1) & 1], kq, qq);
+      __syncthreads();
+    }
+    return;
+  }
 
   // consumers
   const int col0 = slice * DVS + 16 * wave;
-  Consumer<DK, MAXD> cs;
+  Consumer<DK, MAXD, OBF16> cs;
 #pragma unroll
   for (int A = 0; A < DK / 16; ++A)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       cs.S[A][r] = a.S0 ? a.S0[((size_t)bh * DK + 16 * A + 4 * g + r) * a.dv + col0 + c] : 0.f;
-  f32x4 vd[CNT];
-  cs.load_v(a, head_row0, col0, vd);
-  __syncthreads();  // chunk 0 produced
-  for (int64_t ci = 0; ci < nchunks; ++ci) {
-    f32x4 vn[CNT];
-    if (ci + 1 < nchunks) cs.load_v(a, head_row0 + (ci + 1) * CH, col0, vn);
-    cs.step(a, head_row0 + ci * CH, col0, lds[ci & 1], vd);
-#pragma unroll
-    for (int I = 0; I < CNT; ++I) vd[I] = vn[I];
+  // V rows: ping-pong registers, loaded one iteration before use
+  f32x4 v0[CNT], v1[CNT];
+  cs.load_v(a, head_row0, col0, v0);
+  __syncthreads();  // chunk 0's T, K and Q are in LDS
+  for (int64_t ci = 0; ci <= nchunks; ci += 2) {
+    if (ci + 1 < nchunks) cs.load_v(a, head_row0 + (ci + 1) * CH, col0, v1);
+    if (ci >= 1) cs.emit_O(a, head_row0 + (ci - 1) * CH, col0, lds[(ci - 1) & 1]);
+    if (ci < nchunks) cs.step(lds[ci & 1], v0);
+    __syncthreads();
+    if (ci + 1 > nchunks) break;
+    if (ci + 2 < nchunks) cs.load_v(a, head_row0 + (ci + 2) * CH, col0, v0);
+    cs.emit_O(a, head_row0 + ci * CH, col0, lds[ci & 1]);
+    if (ci + 1 < nchunks) cs.step(lds[(ci + 1) & 1], v1);
     __syncthreads();
   }
 #pragma unroll
@@ -408,8 +503,12 @@ int launch_chunk_fwd(const ChunkLaunch& p, hipStream_t s) {
   const dim3 block(4 * WAVE);
   const bool narrow = p.mode == 0 && p.mask && p.N <= 16;
   auto go = [&](auto dk, auto mode, auto cmp, auto maxd) {
-    hipLaunchKernelGGL((chunk_fwd_kernel<dk.value, mode.value, cmp.value, maxd.value>), grid, block, 0,
-                       s, a);
+    if (a.o_bf16)
+      hipLaunchKernelGGL((chunk_fwd_kernel<dk.value, mode.value, cmp.value, maxd.value, true>), grid,
+                         block, 0, s, a);
+    else
+      hipLaunchKernelGGL((chunk_fwd_kernel<dk.value, mode.value, cmp.value, maxd.value, false>), grid,
+                         block, 0, s, a);
     return 0;
   };
   using I0 = std::integral_constant<int, 0>;
