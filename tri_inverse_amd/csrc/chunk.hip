@@ -6,8 +6,8 @@
 // chunks; Methodologie SS1-2 give the truncated / masked inverse used here.
 // [PSDA] "A Persistent-State Dataflow Accelerator for Memory-Bound Linear Attention
 // Decode on FPGA", section 2.A: keep the recurrent state on chip and stream only the
-// per-token inputs.  Here the state slice lives in a wave's registers for the whole
-// sequence.
+// per-token inputs.  Here each state slice lives in one wave's registers for the
+// whole sequence.
 //
 // Per chunk (rows r = 0..63, G = in-chunk cumsum of the log-gates):
 //   T   = inverse of I - A (truncated Neumann or exact doubling)
@@ -17,28 +17,37 @@
 //   O   = scale (diag(exp(G)) Q S + P U')
 //   S  <- exp(G_C) S + K^T diag(exp(G_C - G)) U'
 //
-// Work split: one workgroup per (batch, head, 32 columns of d_v), four waves:
-//   wave 0, 1  consumers: each owns 16 state columns S[:, 16v..16v+15] (fp32, in
-//              registers) and runs the sequential scan;
-//   wave 2     producer: gates, A and T (bf16 row-pack fragments) of the next chunk;
-//   wave 3     producer: P (hi/lo bf16) of the current chunk; K and Q fragments and
-//              K^T of the next chunk.
-// Producers fill one half of a double-buffered LDS area while the consumers read
-// the other; one barrier per chunk hands over, and every global load is issued at
-// least one iteration before its data is used (see the schedule above the kernel).  Y, U' and P enter the MFMAs as hi/lo
-// bf16 pairs (x = xh + xl, both bf16; products take xh yh + xl yh + xh yl), which
-// brings the error of O and S to about 1e-4 relative (rounding each of them to a
-// single bf16 would cost 1e-3 or more each), leaving the bf16 rounding of O itself
-// as the dominant error.
+// One workgroup per (batch, head, 32 columns of d_v) with eight waves; waves w and
+// w + 4 share a SIMD, so every SIMD interleaves two waves:
+//   waves 0, 1  state waves (SIMDs of their own): each owns 16 columns of S (fp32, in
+//               registers) and runs the sequential part of a chunk: K S, Y, U' = T Y and
+//               the state update.  They hand S^T (bf16) and U' (hi/lo) to the output
+//               waves.
+//   waves 3, 7  output waves (one SIMD), one chunk behind: P and
+//               O = scale (e^G Q S + P U') for row tiles {0, 3} and {1, 2} of the chunk
+//               (equal shares of the triangular P), all 32 columns.
+//   wave 2      gates and T of the next chunk.
+//   wave 6      copies K rows, V columns, log-gates and beta of the chunk after next
+//               into a 4-deep LDS ring.
+//   waves 4, 5  only join the barriers.
+// One barrier per chunk hands every buffer over (schedule above the kernel).  The K
+// rows sit in LDS row-major; the K^T operand of the state update comes from the same
+// rows through the LDS transpose read.  Q is read once per workgroup, each lane taking
+// 16 contiguous bytes (8 consecutive d), so the contractions over d that involve Q use
+// that natural order of d in both operands.  Y, U' and P enter the MFMAs as hi/lo bf16
+// pairs (x = xh + xl; products take xh yh + xl yh + xh yl), which holds the error of O
+// and S near 1e-4 relative, so that the bf16 rounding of O itself dominates.
 #include "gdn_kernels.hpp"
 #include "tri_block.hpp"
 
 namespace gdn {
 
-constexpr int CH = 64;           // chunk size (tokens)
-constexpr int CNT = 4;           // 16-row tiles per chunk
-constexpr int DVS = 32;          // d_v columns per workgroup
-constexpr int KT_PAD = 8;        // padding of the K^T rows in LDS (bank spread)
+constexpr int CH = 64;     // chunk size (tokens)
+constexpr int CNT = 4;     // 16-row tiles per chunk
+constexpr int DVS = 32;    // d_v columns per workgroup
+constexpr int KPAD = 8;    // bf16 padding of the LDS K rows (bank spread)
+constexpr int VPAD = 8;    // bf16 padding of the LDS V rows
+constexpr int NWAVES = 8;
 
 struct ChunkArgs {
   const __bf16* Q;
@@ -53,38 +62,76 @@ struct ChunkArgs {
   int64_t T;
   int BH;
   int dv;
-  int o_bf16;
   int N;
   int mask;
   float scale;
 };
 
+// raw inputs of one chunk staged in LDS: K rows (row-major), this workgroup's V
+// columns (row-major), log-gates and beta
 template <int DK>
-struct ChunkLds {
-  bf16x8 krp[CNT][DK / 32][WAVE];  // K rows as left-operand fragments (permuted k order)
-  bf16x8 qrp[CNT][DK / 32][WAVE];  // Q rows, same
-  bf16x8 trp[CNT][2][WAVE];        // T rows (T-form row packs)
-  bf16x8 prh[CNT][2][WAVE];        // P rows, high part
-  bf16x8 prl[CNT][2][WAVE];        // P rows, low part
-  __bf16 kt[DK][CH + KT_PAD];      // K^T: kt[d][token]
+struct alignas(16) ChunkIn {
+  __bf16 k[CH][DK + KPAD];
+  __bf16 v[CH][DVS + VPAD];
+  float g[CH];
   float beta[CH];
-  float eg[CH];                    // exp(G_i)
-  float eng[CH];                   // exp(-G_i)
-  float egcg[CH];                  // exp(G_C - G_i)
-  float G[CH];                     // G_i
-  float egc;                       // exp(G_C)
-  int split;                       // exp(-G) finite over the chunk
 };
 
-// 8 consecutive-in-slot bf16 of row `row` for k-pair p in the permuted order
-// (k = 32p + 4g .. +3 and 32p + 16 + 4g .. +3)
+// gate factors of one chunk
+struct alignas(16) ChunkGates {
+  float beta[CH];
+  float eg[CH];    // exp(G_i)
+  float eng[CH];   // exp(-G_i)
+  float egcg[CH];  // exp(G_C - G_i)
+  float G[CH];
+  float egc;       // exp(G_C)
+  int split;       // exp(-G) finite over the chunk
+};
+
+// products of one chunk handed from their producers to their readers
 template <int DK>
-__device__ __forceinline__ bf16x8 load_rowpack(const __bf16* __restrict__ base, int row, int p) {
+struct alignas(16) ChunkBuf {
+  bf16x8 trp[CNT][2][WAVE];         // T rows (row packs)
+  __bf16 st[2][16][DK + KPAD];      // per state wave: S^T before the chunk, st[col][d]
+  bf16x8 uh[2][2][WAVE];            // per state wave: U' column packs, high
+  bf16x8 ul[2][2][WAVE];            // per state wave: U' column packs, low
+};
+
+// row `row` as an operand fragment for k-pair p: slot t <-> k = 32p + 16(t/4) + 4g + t%4
+template <int DK>
+__device__ __forceinline__ bf16x8 rowpack_lds(const ChunkIn<DK>& R, int row, int p) {
   const int g = lane_id() >> 4;
-  const __bf16* src = base + (size_t)row * DK + 32 * p + 4 * g;
-  bf16x4 lo = *reinterpret_cast<const bf16x4*>(src);
-  bf16x4 hi = *reinterpret_cast<const bf16x4*>(src + 16);
-  return join8(lo, hi);
+  const __bf16* src = &R.k[row][32 * p + 4 * g];
+  return join8(*reinterpret_cast<const bf16x4*>(src), *reinterpret_cast<const bf16x4*>(src + 16));
+}
+
+// K^T operand fragment, row tile a (d = 16a + c), token pair p:
+// lane (g, c) slot t <-> K[32p + 16(t/4) + 4g + t%4][16a + c], by the transpose read
+template <int DK>
+__device__ __forceinline__ bf16x8 ktpack_lds(const ChunkIn<DK>& R, int a, int p) {
+  const int l = lane_id(), g = l >> 4, j = l & 15;
+  const __bf16* p0 = &R.k[32 * p + 4 * g + (j >> 2)][16 * a + 4 * (j & 3)];
+  const __bf16* p1 = &R.k[32 * p + 16 + 4 * g + (j >> 2)][16 * a + 4 * (j & 3)];
+  return join8(lds_read_tr4(p0), lds_read_tr4(p1));
+}
+
+// natural d order (slot t <-> d = 32p + 8g + t): K row `row` from LDS, and the Q rows
+// of row tiles I0, I1 of a chunk from global memory (16 contiguous bytes per lane)
+template <int DK>
+__device__ __forceinline__ bf16x8 rowfrag_nat(const ChunkIn<DK>& R, int row, int p) {
+  const int g = lane_id() >> 4;
+  return *reinterpret_cast<const bf16x8*>(&R.k[row][32 * p + 8 * g]);
+}
+
+template <int DK, int I0, int I1>
+__device__ __forceinline__ void load_q_nat(const ChunkArgs& a, int64_t row0, bf16x8 (&q)[2][DK / 32]) {
+  const int l = lane_id(), g = l >> 4, c = l & 15;
+  const __bf16* base = a.Q + (row0 + c) * DK + 8 * g;
+#pragma unroll
+  for (int p = 0; p < DK / 32; ++p) {
+    q[0][p] = *reinterpret_cast<const bf16x8*>(base + (16 * I0) * DK + 32 * p);
+    q[1][p] = *reinterpret_cast<const bf16x8*>(base + (16 * I1) * DK + 32 * p);
+  }
 }
 
 __device__ __forceinline__ f32x4 unpack_lo(const bf16x8& v) {
@@ -100,29 +147,22 @@ __device__ __forceinline__ void pack8_hilo(const f32x4& a, const f32x4& b, bf16x
   lo = pack8(a - unpack_lo(hi), b - unpack_hi(hi));
 }
 
-// raw inputs of one chunk for the A/T producer (held in registers one chunk ahead)
-template <int DK>
-struct KChunk {
-  KBlock<CNT, DK> kb;
-  __device__ __forceinline__ void load(const ChunkArgs& a, int64_t row0) {
-    const int l = lane_id(), c = l & 15;
-#pragma unroll
-    for (int I = 0; I < CNT; ++I)
-#pragma unroll
-      for (int p = 0; p < DK / 32; ++p) kb.kf[I][p] = load_rowpack<DK>(a.K + row0 * DK, 16 * I + c, p);
-    kb.gl = a.g[row0 + l];
-    kb.bl = a.beta[row0 + l];
-  }
-};
-
-// ---- producer wave 2: gates, A, T, and the K layouts the other waves read ----------
+// ---- wave 2: gates, A, T ------------------------------------------------------------
 template <int DK, int MODE, int CMP, int MAXD>
-__device__ __forceinline__ void produce_T(const ChunkArgs& a, const KChunk<DK>& in, ChunkLds<DK>& L,
-                                          Fp8Counts& cnt, bool count) {
-  const int l = lane_id(), g = l >> 4, c = l & 15;
-  const KBlock<CNT, DK>& kb = in.kb;
+__device__ __forceinline__ void produce_T(const ChunkArgs& a, const ChunkIn<DK>& R,
+                                          bf16x8 (&trp)[CNT][2][WAVE], ChunkGates& GT, Fp8Counts& cnt,
+                                          bool count) {
+  const int l = lane_id(), c = l & 15;
+  const float gl = R.g[l], bl = R.beta[l];
+  KBlock<CNT, DK> kb;
+#pragma unroll
+  for (int I = 0; I < CNT; ++I)
+#pragma unroll
+    for (int p = 0; p < DK / 32; ++p) kb.kf[I][p] = rowpack_lds<DK>(R, 16 * I + c, p);
+  kb.gl = gl;
+  kb.bl = bl;
   Gates<CNT> gt;
-  gates_from_lanes<CNT>(kb.gl, kb.bl, false, gt);
+  gates_from_lanes<CNT>(gl, bl, false, gt);
   Mat<CNT> S, AD, AT, TT;
   constexpr bool BANDED = (MODE == MODE_NEUMANN && CMP == CMP_FP8);
   gram_from_frags<CNT, DK, MAXD>(kb, S);
@@ -135,167 +175,63 @@ __device__ __forceinline__ void produce_T(const ChunkArgs& a, const KChunk<DK>& 
 #pragma unroll
   for (int I = 0; I < CNT; ++I)
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    for (int p = 0; p < 2; ++p)
       if (2 * p <= I && I - (2 * p + 1) <= MAXD)
-        L.trp[I][p][l] = pack8(tile_or_zero(TT, I, 2 * p), tile_or_zero(TT, I, 2 * p + 1));
-    }
-  // gate factors
+        trp[I][p][l] = pack8(tile_or_zero(TT, I, 2 * p), tile_or_zero(TT, I, 2 * p + 1));
   const float GC = __shfl(gt.Gl, CH - 1, 64);
-  L.beta[l] = kb.bl;
-  L.eg[l] = __expf(gt.Gl);
-  L.eng[l] = __expf(-gt.Gl);
-  L.egcg[l] = __expf(GC - gt.Gl);
-  L.G[l] = gt.Gl;
+  GT.beta[l] = bl;
+  GT.eg[l] = __expf(gt.Gl);
+  GT.eng[l] = __expf(-gt.Gl);
+  GT.egcg[l] = __expf(GC - gt.Gl);
+  GT.G[l] = gt.Gl;
   if (l == 0) {
-    L.egc = __expf(GC);
-    L.split = gt.split ? 1 : 0;
+    GT.egc = __expf(GC);
+    GT.split = gt.split ? 1 : 0;
   }
 }
 
-// ---- producer wave 3: P = Q K^T .* exp(G_i - G_j) .* [i >= j] (hi/lo) -------------
-// Reads K and Q fragments and the gates of the same chunk from LDS.
-template <int DK>
-__device__ __forceinline__ void produce_P(const ChunkLds<DK>& Lin, ChunkLds<DK>& Lout) {
-  const int l = lane_id(), g = l >> 4, c = l & 15;
-  const bool split = Lin.split != 0;
-  const int lo_ = 4 * g - c;
-#pragma unroll
-  for (int I = 0; I < CNT; ++I) {
-    const float rowf = Lin.eg[16 * I + c];  // exp(G_i), i = 16I + c
-    const float Gi = Lin.G[16 * I + c];
-    bf16x8 qf[DK / 32];
-#pragma unroll
-    for (int p = 0; p < DK / 32; ++p) qf[p] = Lin.qrp[I][p][l];
-    f32x4 pt[CNT];
-#pragma unroll
-    for (int J = 0; J < CNT; ++J) {
-      if (J > I) {
-        pt[J] = zero4();
-        continue;
-      }
-      // T-form tile (I,J): lane (g,c) reg r = q_{16I+c} . k_{16J+4g+r}
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int p = 0; p < DK / 32; ++p) acc = mma_bf16(Lin.krp[J][p][l], qf[p], acc);
-      const f32x4 ncol = *reinterpret_cast<const f32x4*>(&Lin.eng[16 * J + 4 * g]);
-      const f32x4 Gcol = *reinterpret_cast<const f32x4*>(&Lin.G[16 * J + 4 * g]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float f = split ? rowf * ncol[r] : __expf(Gi - Gcol[r]);
-        const int d = 16 * (I - J) - r - lo_;       // i - j
-        acc[r] = (d >= 0) ? acc[r] * f : 0.f;
-      }
-      pt[J] = acc;
-    }
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      if (2 * p <= I) {
-        bf16x8 h, lw;
-        pack8_hilo(pt[2 * p], (2 * p + 1 < CNT) ? pt[2 * p + 1] : zero4(), h, lw);
-        Lout.prh[I][p][l] = h;
-        Lout.prl[I][p][l] = lw;
-      }
-    }
-  }
-}
-
-// ---- consumer waves: the state scan ----------------------------------------------
-// Each phase first gathers the LDS fragments it needs into registers, then issues
-// its MFMAs with independent accumulators adjacent, so LDS latency and MFMA latency
-// overlap instead of serialising.
-template <int DK, int MAXD, bool OBF16>
-struct Consumer {
+// ---- waves 0, 1: the state scan -------------------------------------------------------
+template <int DK, int MAXD>
+struct StateWave {
   static constexpr int NP = DK / 32;
   f32x4 S[DK / 16];  // D-form tiles: lane (g,c) reg r = S[16a + 4g + r][col0 + c]
-  f32x4 qsg[CNT];    // previous chunk: e^{G_i} (Q S)_i in T-form (row 16I + c)
-  bf16x8 cuh[2], cul[2];  // previous chunk: U' column packs, hi / lo
 
-  __device__ __forceinline__ void load_v(const ChunkArgs& a, int64_t row0, int col0, f32x4 (&v)[CNT]) {
+  // one chunk: S packs out, K S, Y, U' = T Y (out), state update
+  __device__ __forceinline__ void step(const ChunkIn<DK>& R, const ChunkGates& GT, ChunkBuf<DK>& B, int v) {
     const int l = lane_id(), g = l >> 4, c = l & 15;
-    const __bf16* base = a.V + (row0 + 4 * g) * a.dv + col0 + c;
+    // V tiles in D-form (rows 16I + 4g + r, column 16v + c) by the transpose read
+    bf16x4 vt[CNT];
 #pragma unroll
-    for (int I = 0; I < CNT; ++I)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[I][r] = (float)base[(16 * I + r) * a.dv];
-  }
-
-  // O of the previous chunk: scale (e^G Q S + P U'), T-form rows 16I + c
-  __device__ __forceinline__ void emit_O(const ChunkArgs& a, int64_t row0, int col0,
-                                         const ChunkLds<DK>& L) {
-    const int l = lane_id(), g = l >> 4, c = l & 15;
-    bf16x8 ph[CNT][2], pl[CNT][2];
-#pragma unroll
-    for (int I = 0; I < CNT; ++I)
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-        if (2 * p <= I) {
-          ph[I][p] = L.prh[I][p][l];
-          pl[I][p] = L.prl[I][p][l];
-        }
-    f32x4 acc[CNT];
-#pragma unroll
-    for (int I = 0; I < CNT; ++I) acc[I] = qsg[I];
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-#pragma unroll
-      for (int k = 0; k < 3; ++k)
-#pragma unroll
-        for (int I = 0; I < CNT; ++I)
-          if (2 * p <= I) {
-            const bf16x8& uu = (k == 1) ? cul[p] : cuh[p];
-            const bf16x8& pp = (k == 2) ? pl[I][p] : ph[I][p];
-            acc[I] = mma_bf16(uu, pp, acc[I]);
-          }
-#pragma unroll
-    for (int I = 0; I < CNT; ++I) {
-      const f32x4 o = acc[I] * a.scale;
-      const int64_t off = (row0 + 16 * I + c) * a.dv + col0 + 4 * g;
-      if constexpr (OBF16)
-        *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.O) + off) = pack4(o);
-      else
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.O) + off) = o;
-    }
-  }
-
-  // state part of one chunk: K S, Q S, Y, U' = T Y, state update; keeps e^G Q S and U'
-  __device__ __forceinline__ void step(const ChunkLds<DK>& L, const f32x4 (&vd)[CNT]) {
-    const int l = lane_id(), g = l >> 4, c = l & 15;
+    for (int I = 0; I < CNT; ++I) vt[I] = lds_read_tr4(&R.v[16 * I + 4 * g + (c >> 2)][16 * v + 4 * (c & 3)]);
+    // S as bf16: column packs for K S here, S^T rows (4 consecutive d per lane and
+    // tile) for the output waves
     bf16x8 cps[NP];
 #pragma unroll
-    for (int p = 0; p < NP; ++p) cps[p] = pack8(S[2 * p], S[2 * p + 1]);
-    // K S (D-form) and Q S (T-form), contraction over d_k; two row tiles at a time
+    for (int p = 0; p < NP; ++p) {
+      const bf16x4 s0 = pack4(S[2 * p]), s1 = pack4(S[2 * p + 1]);
+      cps[p] = join8(s0, s1);
+      *reinterpret_cast<bf16x4*>(&B.st[v][c][32 * p + 4 * g]) = s0;
+      *reinterpret_cast<bf16x4*>(&B.st[v][c][32 * p + 16 + 4 * g]) = s1;
+    }
+    // K S (D-form), contraction over d_k, all four row tiles interleaved
     f32x4 ks[CNT];
 #pragma unroll
-    for (int I0 = 0; I0 < CNT; I0 += 2) {
-      bf16x8 kf[2][NP], qf[2][NP];
+    for (int I = 0; I < CNT; ++I) ks[I] = zero4();
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+    for (int p = 0; p < NP; ++p) {
+      bf16x8 kf[CNT];
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-          kf[i][p] = L.krp[I0 + i][p][l];
-          qf[i][p] = L.qrp[I0 + i][p][l];
-        }
-      f32x4 ak[2] = {zero4(), zero4()}, aq[2] = {zero4(), zero4()};
+      for (int I = 0; I < CNT; ++I) kf[I] = rowpack_lds<DK>(R, 16 * I + c, p);
 #pragma unroll
-      for (int p = 0; p < NP; ++p)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          ak[i] = mma_bf16(kf[i][p], cps[p], ak[i]);
-          aq[i] = mma_bf16(cps[p], qf[i][p], aq[i]);
-        }
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        ks[I0 + i] = ak[i];
-        qsg[I0 + i] = aq[i] * L.eg[16 * (I0 + i) + c];
-      }
+      for (int I = 0; I < CNT; ++I) ks[I] = mma_bf16(kf[I], cps[p], ks[I]);
     }
     // Y = diag(beta) (V - diag(e^G) K S), D-form rows 16I + 4g + r
     f32x4 y[CNT];
 #pragma unroll
     for (int I = 0; I < CNT; ++I) {
-      const f32x4 b4 = *reinterpret_cast<const f32x4*>(&L.beta[16 * I + 4 * g]);
-      const f32x4 e4 = *reinterpret_cast<const f32x4*>(&L.eg[16 * I + 4 * g]);
-      y[I] = b4 * (vd[I] - e4 * ks[I]);
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(&GT.beta[16 * I + 4 * g]);
+      const f32x4 e4 = *reinterpret_cast<const f32x4*>(&GT.eg[16 * I + 4 * g]);
+      y[I] = b4 * (unpack4(vt[I]) - e4 * ks[I]);
     }
     bf16x8 cyh[2], cyl[2];
     pack8_hilo(y[0], y[1], cyh[0], cyl[0]);
@@ -306,7 +242,7 @@ struct Consumer {
     for (int I = 0; I < CNT; ++I)
 #pragma unroll
       for (int p = 0; p < 2; ++p)
-        if (2 * p <= I && I - (2 * p + 1) <= MAXD) tf[I][p] = L.trp[I][p][l];
+        if (2 * p <= I && I - (2 * p + 1) <= MAXD) tf[I][p] = B.trp[I][p][l];
     f32x4 u[CNT];
 #pragma unroll
     for (int I = 0; I < CNT; ++I) u[I] = zero4();
@@ -317,26 +253,28 @@ struct Consumer {
 #pragma unroll
         for (int I = 0; I < CNT; ++I)
           if (2 * p <= I && I - (2 * p + 1) <= MAXD) u[I] = mma_bf16(tf[I][p], k ? cyl[p] : cyh[p], u[I]);
-    pack8_hilo(u[0], u[1], cuh[0], cul[0]);
-    pack8_hilo(u[2], u[3], cuh[1], cul[1]);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      bf16x8 h, lw;
+      pack8_hilo(u[2 * p], u[2 * p + 1], h, lw);
+      B.uh[v][p][l] = h;
+      B.ul[v][p][l] = lw;
+    }
     // S <- e^{G_C} S + K^T diag(e^{G_C - G}) U'
     f32x4 ut[CNT];
 #pragma unroll
-    for (int I = 0; I < CNT; ++I) ut[I] = u[I] * *reinterpret_cast<const f32x4*>(&L.egcg[16 * I + 4 * g]);
+    for (int I = 0; I < CNT; ++I) ut[I] = u[I] * *reinterpret_cast<const f32x4*>(&GT.egcg[16 * I + 4 * g]);
     bf16x8 cth[2], ctl[2];
     pack8_hilo(ut[0], ut[1], cth[0], ctl[0]);
     pack8_hilo(ut[2], ut[3], cth[1], ctl[1]);
-    const float egc = L.egc;
+    const float egc = GT.egc;
 #pragma unroll
     for (int A0 = 0; A0 < DK / 16; A0 += 4) {
       bf16x8 kt[4][2];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const __bf16* kr = &L.kt[16 * (A0 + i) + c][32 * p + 4 * g];
-          kt[i][p] = join8(*reinterpret_cast<const bf16x4*>(kr), *reinterpret_cast<const bf16x4*>(kr + 16));
-        }
+        for (int p = 0; p < 2; ++p) kt[i][p] = ktpack_lds<DK>(R, A0 + i, p);
       f32x4 acc[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = S[A0 + i] * egc;
@@ -352,48 +290,238 @@ struct Consumer {
   }
 };
 
-// Schedule (iteration c = 0 .. nchunks, one barrier each, buffers by chunk parity):
-//   wave 2: T and gates of chunk c+1 (its K rows were loaded one iteration earlier;
-//           chunk c+2's rows are loaded now)
-//   wave 3: P of chunk c from chunk c's K/Q fragments in LDS; K and Q rows of chunk
-//           c+1 loaded now and staged (fragments, K^T) at the end of the iteration
-//   waves 0, 1: state part of chunk c, and O of chunk c-1 (needs P of chunk c-1)
+// ---- waves 3, 7: P and O = scale (e^G Q S + P U') for row tiles I0, I1 -----------------
+// q holds the chunk's Q rows of those tiles (natural d order).
+template <int DK, int I0, int I1, bool OBF16>
+__device__ __forceinline__ void emit_rows(const ChunkArgs& a, int64_t row0, int col0, const ChunkIn<DK>& R,
+                                          const ChunkGates& GT, const ChunkBuf<DK>& B,
+                                          const bf16x8 (&q)[2][DK / 32]) {
+  constexpr int NP = DK / 32;
+  constexpr int IS[2] = {I0, I1};
+  const int l = lane_id(), g = l >> 4, c = l & 15;
+  // Q S for both column halves (T-form: lane (g,c) reg r = row 16I + c, column 4g + r)
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) acc[i][h] = zero4();
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bf16x8 sf = *reinterpret_cast<const bf16x8*>(&B.st[h][c][32 * p + 8 * g]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) acc[i][h] = mma_bf16(sf, q[i][p], acc[i][h]);
+    }
+  // raw P tiles (I, J), J <= I, one K tile-row at a time
+  f32x4 pt[2][CNT];
+#pragma unroll
+  for (int J = 0; J < CNT; ++J) {
+    if (J > I0 && J > I1) continue;
+    bf16x8 kf[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) kf[p] = rowfrag_nat<DK>(R, 16 * J + c, p);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (J > IS[i]) continue;
+      f32x4 t = zero4();
+#pragma unroll
+      for (int p = 0; p < NP; ++p) t = mma_bf16(kf[p], q[i][p], t);
+      pt[i][J] = t;
+    }
+  }
+  // decay and causal mask of P; e^G on Q S.  exp(-G) finite over the chunk: the decay
+  // factor splits into a row and a column factor (uniform branch)
+  const bool split = __builtin_amdgcn_readfirstlane(GT.split) != 0;
+  const int lo_ = 4 * g - c;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int I = IS[i];
+    const float rowf = GT.eg[16 * I + c];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) acc[i][h] = acc[i][h] * rowf;
+#pragma unroll
+    for (int J = 0; J < CNT; ++J) {
+      if (J > I) {
+        pt[i][J] = zero4();
+        continue;
+      }
+      f32x4 fac;
+      if (split) {
+        fac = *reinterpret_cast<const f32x4*>(&GT.eng[16 * J + 4 * g]) * rowf;
+      } else {
+        const float Gi = GT.G[16 * I + c];
+        const f32x4 Gcol = *reinterpret_cast<const f32x4*>(&GT.G[16 * J + 4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) fac[r] = __expf(Gi - Gcol[r]);
+      }
+      if (J < I) {
+        pt[i][J] = pt[i][J] * fac;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pt[i][J][r] = (r + lo_ <= 0) ? pt[i][J][r] * fac[r] : 0.f;  // i >= j
+      }
+    }
+  }
+  // + P U' (T-form), U' and P as hi/lo pairs
+  bf16x8 uh[2][2], ul[2][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      uh[h][q2] = B.uh[h][q2][l];
+      ul[h][q2] = B.ul[h][q2][l];
+    }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      if (2 * q2 > IS[i]) continue;
+      bf16x8 ph, pl;
+      pack8_hilo(pt[i][2 * q2], pt[i][2 * q2 + 1], ph, pl);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        acc[i][h] = mma_bf16(uh[h][q2], ph, acc[i][h]);
+        acc[i][h] = mma_bf16(ul[h][q2], ph, acc[i][h]);
+        acc[i][h] = mma_bf16(uh[h][q2], pl, acc[i][h]);
+      }
+    }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x4 o = acc[i][h] * a.scale;
+      const int64_t off = (row0 + 16 * IS[i] + c) * a.dv + col0 + 16 * h + 4 * g;
+      if constexpr (OBF16)
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.O) + off) = pack4(o);
+      else
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.O) + off) = o;
+    }
+}
+
+// Slot `idx` of an LDS ring.  The byte offset goes through readfirstlane so that the
+// compiler treats it as one opaque uniform value: each access is then a per-lane base
+// plus a constant folded into the instruction's offset field, instead of a separately
+// strength-reduced address per access.
+template <class T>
+__device__ __forceinline__ T& ring(T* base, int idx) {
+  const uint32_t off = __builtin_amdgcn_readfirstlane((uint32_t)idx * (uint32_t)sizeof(T));
+  return *reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
+}
+
+// Hand-over of LDS buffers between the waves of the workgroup: wait for this wave's
+// LDS accesses, then the barrier.  Global memory is never exchanged between waves
+// here, so outstanding global loads (prefetches into registers) stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Schedule: iterations it = -1 .. nchunks with one barrier at the end of each, and one
+// barrier before the loop.  Rings: raw inputs of chunk j in in[j % 4], gate factors in
+// gr[j % 3], the other products of chunk j in buf[j % 2].
+//   wave 6      it: stores chunk it+2 into in (loaded at it-1), loads chunk it+3
+//   wave 2      it: T, gates of chunk it+1  reads in         writes buf.trp, gr
+//   waves 0, 1  it: state step of chunk it  reads in, gr, buf.trp
+//                                           writes buf.st, buf.uh/ul
+//   waves 3, 7  it: P, O of chunk it-1      reads in, gr, buf.{st, uh, ul}
+// Every slot is written in one iteration and read only in later ones, and its next
+// write comes after its last read: in[j] is written at j-2, read at j-1 .. j+1 and
+// rewritten at j+2; gr[j] is read at j and j+1 and rewritten at j+2; buf[j].trp is read
+// at j and rewritten at j+1, the other buf[j] fields are read at j+1 and rewritten at
+// j+2.  In iteration it, the output waves read buf[(it-1) % 2] = buf[(it+1) % 2] while
+// wave 2 writes that buffer's trp, a field they do not touch.  Global loads are issued
+// one iteration before their data is needed (register ping-pong, no loop-carried
+// copies, no conditional loads), so their latency overlaps a whole iteration.
+constexpr int W_STATE0 = 0, W_STATE1 = 1, W_T = 2, W_OUT0 = 3, W_STAGE = 6, W_OUT1 = 7;
+
 template <int DK, int MODE, int CMP, int MAXD, bool OBF16>
-__global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkArgs a) {
-  __shared__ ChunkLds<DK> lds[2];
-  const int wave = threadIdx.x / WAVE;
+__global__ __launch_bounds__(NWAVES * WAVE, 1) void chunk_fwd_kernel(ChunkArgs a) {
+  __shared__ ChunkIn<DK> in[4];
+  __shared__ ChunkGates gr[3];
+  __shared__ ChunkBuf<DK> buf[2];
+  // wave index as a uniform (scalar) value: role branches and loop counters stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
   const int l = lane_id(), g = l >> 4, c = l & 15;
   // workgroup -> (head, slice): the slices of one head are consecutive workgroup
-  // indices inside one XCD (workgroups are dealt round-robin over the 8 XCDs), so
-  // they share that XCD's L2 for the Q/K/V rows they all read
+  // indices inside one XCD (workgroups are dealt round-robin over the 8 XCDs), so they
+  // share that XCD's L2 for the rows they all read
   const int n_slices = a.dv / DVS;
   const int total = a.BH * n_slices;
   const int wg = blockIdx.x;
   const int idx = (total % 8 == 0) ? (wg % 8) * (total / 8) + wg / 8 : wg;
   const int bh = idx / n_slices, slice = idx % n_slices;
-  const int64_t nchunks = a.T / CH;
+  const int nchunks = (int)(a.T / CH);
   const int64_t head_row0 = (int64_t)bh * a.T;
-  const bool count = (CMP == CMP_FP8) && a.stats != nullptr;
+  const int last = nchunks - 1;  // >= 0: the launcher is never called with T = 0
 
-  if (wave == 2) {
+  if (wave == W_STAGE) {
+    // K: the chunk's rows are contiguous, 16 bytes per lane and instruction; V: this
+    // workgroup's 32 columns (64 bytes) of each row, 4 lanes per row
+    constexpr int SEG = DK / 8;
+    constexpr int NK = CH * SEG / WAVE;
+    constexpr int NV = CH * (DVS / 8) / WAVE;
+    struct Regs {
+      bf16x8 k[NK];
+      bf16x8 v[NV];
+      float g, b;
+    };
+    const __bf16* vlane = a.V + (head_row0 + (l >> 2)) * a.dv + slice * DVS + 8 * (l & 3);
+    auto load = [&](int ch, Regs& r) {
+      const __bf16* kc = a.K + (head_row0 + (int64_t)ch * CH) * DK;
+#pragma unroll
+      for (int i = 0; i < NK; ++i) r.k[i] = *reinterpret_cast<const bf16x8*>(kc + 8 * (i * WAVE + l));
+      const __bf16* vc = vlane + (int64_t)ch * CH * a.dv;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) r.v[i] = *reinterpret_cast<const bf16x8*>(vc + (int64_t)(16 * i) * a.dv);
+      r.g = a.g[head_row0 + (int64_t)ch * CH + l];
+      r.b = a.beta[head_row0 + (int64_t)ch * CH + l];
+    };
+    auto store = [&](const Regs& r, ChunkIn<DK>& S) {
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        const int e = i * WAVE + l;
+        *reinterpret_cast<bf16x8*>(&S.k[e / SEG][8 * (e % SEG)]) = r.k[i];
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) *reinterpret_cast<bf16x8*>(&S.v[16 * i + (l >> 2)][8 * (l & 3)]) = r.v[i];
+      S.g[l] = r.g;
+      S.beta[l] = r.b;
+    };
+    // chunk c sits in r0 for even c and in r1 for odd c.  Every load is issued
+    // unconditionally (chunk index clamped into range; loads past the end re-read the
+    // last chunk and are never stored) so that the wait before each store covers only
+    // the loads of that chunk, not the ones issued after it.
+    auto clampc = [&](int ch) { return ch < last ? ch : last; };
+    Regs r0, r1;
+    load(0, r0);
+    load(clampc(1), r1);
+    store(r0, in[0]);
+    lds_barrier();
+    for (int it = -1; it <= nchunks; it += 2) {
+      // iteration it (odd): chunk it+3 (even) -> r0, chunk it+2 (odd) r1 -> LDS
+      load(clampc(it + 3), r0);
+      if (it + 2 < nchunks) store(r1, ring(in, (it + 2) & 3));
+      lds_barrier();
+      if (it + 1 > nchunks) break;
+      // iteration it+1 (even): chunk it+4 (odd) -> r1, chunk it+3 (even) r0 -> LDS
+      load(clampc(it + 4), r1);
+      if (it + 3 < nchunks) store(r0, ring(in, (it + 3) & 3));
+      lds_barrier();
+    }
+    return;
+  }
+  if (wave == W_T) {
     Fp8Counts cnt{0, 0, 0, 0};
-    // ping-pong register buffers: a buffer's rows are consumed one full iteration
-    // (one barrier) after their loads are issued
-    KChunk<DK> b0, b1;
-    b0.load(a, head_row0);
-    produce_T<DK, MODE, CMP, MAXD>(a, b0, lds[0], cnt, count);
-    if (nchunks > 1) b0.load(a, head_row0 + CH);
-    __syncthreads();
-    for (int64_t ci = 0; ci <= nchunks; ci += 2) {
-      // iteration ci: T of chunk ci+1 from b0, rows of chunk ci+2 into b1
-      if (ci + 2 < nchunks) b1.load(a, head_row0 + (ci + 2) * CH);
-      if (ci + 1 < nchunks) produce_T<DK, MODE, CMP, MAXD>(a, b0, lds[(ci + 1) & 1], cnt, count);
-      __syncthreads();
-      if (ci + 1 > nchunks) break;
-      // iteration ci+1: T of chunk ci+2 from b1, rows of chunk ci+3 into b0
-      if (ci + 3 < nchunks) b0.load(a, head_row0 + (ci + 3) * CH);
-      if (ci + 2 < nchunks) produce_T<DK, MODE, CMP, MAXD>(a, b1, lds[(ci + 2) & 1], cnt, count);
-      __syncthreads();
+    const bool count = (CMP == CMP_FP8) && a.stats != nullptr;
+    lds_barrier();
+    for (int it = -1; it <= nchunks; ++it) {
+      const int ch = it + 1;
+      if (ch < nchunks)
+        produce_T<DK, MODE, CMP, MAXD>(a, ring(in, ch & 3), ring(buf, ch & 1).trp, ring(gr, ch % 3), cnt,
+                                       count);
+      lds_barrier();
     }
     if constexpr (CMP == CMP_FP8) {
       if (count) {
@@ -409,76 +537,59 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(ChunkArgs a) {
     }
     return;
   }
-  if (wave == 3) {
-    // stages chunk c+1's K fragments, K^T and Q fragments at the end of iteration c;
-    // their rows are loaded at the start of the iteration, so the P computation of
-    // chunk c hides the load latency
-    auto stage = [&](int64_t row0, ChunkLds<DK>& L, const bf16x8 (&kq)[CNT][DK / 32],
-                     const bf16x8 (&qq)[CNT][DK / 32]) {
-#pragma unroll
-      for (int I = 0; I < CNT; ++I)
-#pragma unroll
-        for (int p = 0; p < DK / 32; ++p) {
-          L.krp[I][p][l] = kq[I][p];
-          L.qrp[I][p][l] = qq[I][p];
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const int d = 32 * p + 16 * (t >> 2) + 4 * g + (t & 3);
-            L.kt[d][16 * I + c] = kq[I][p][t];
-          }
-        }
+  if (wave == W_OUT0 || wave == W_OUT1) {
+    // chunk ch = it - 1 in iteration it; that iteration also loads chunk ch + 1
+    auto out_loop = [&](auto i0, auto i1) {
+      constexpr int I0 = decltype(i0)::value, I1 = decltype(i1)::value;
+      auto clampc = [&](int ch) { return ch < 0 ? 0 : (ch < last ? ch : last); };
+      bf16x8 q0[2][DK / 32], q1[2][DK / 32];
+      auto work = [&](int ch, const bf16x8 (&q)[2][DK / 32]) {
+        emit_rows<DK, I0, I1, OBF16>(a, head_row0 + (int64_t)ch * CH, slice * DVS, ring(in, ch & 3),
+                                     ring(gr, ch % 3), ring(buf, ch & 1), q);
+      };
+      lds_barrier();
+      for (int it = -1; it <= nchunks; it += 2) {
+        int ch = it - 1;  // even
+        load_q_nat<DK, I0, I1>(a, head_row0 + (int64_t)clampc(ch + 1) * CH, q1);
+        if (ch >= 0 && ch < nchunks) work(ch, q0);
+        lds_barrier();
+        if (it + 1 > nchunks) break;
+        ch += 1;  // odd
+        load_q_nat<DK, I0, I1>(a, head_row0 + (int64_t)clampc(ch + 1) * CH, q0);
+        if (ch >= 0 && ch < nchunks) work(ch, q1);
+        lds_barrier();
+      }
     };
-    bf16x8 kq[CNT][DK / 32], qq[CNT][DK / 32];
-    auto load = [&](int64_t row0) {
-#pragma unroll
-      for (int I = 0; I < CNT; ++I)
-#pragma unroll
-        for (int p = 0; p < DK / 32; ++p) {
-          kq[I][p] = load_rowpack<DK>(a.K + row0 * DK, 16 * I + c, p);
-          qq[I][p] = load_rowpack<DK>(a.Q + row0 * DK, 16 * I + c, p);
-        }
-    };
-    load(head_row0);
-    stage(head_row0, lds[0], kq, qq);
-    __syncthreads();
-    for (int64_t ci = 0; ci <= nchunks; ++ci) {
-      const bool more = ci + 1 < nchunks;
-      if (more) load(head_row0 + (ci + 1) * CH);
-      if (ci < nchunks) produce_P<DK>(lds[ci & 1], lds[ci & 1]);
-      if (more) stage(head_row0 + (ci + 1) * CH, lds[(ci + 1) & 1], kq, qq);
-      __syncthreads();
-    }
+    if (wave == W_OUT0)
+      out_loop(std::integral_constant<int, 0>{}, std::integral_constant<int, 3>{});
+    else
+      out_loop(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
     return;
   }
-
-  // consumers
-  const int col0 = slice * DVS + 16 * wave;
-  Consumer<DK, MAXD, OBF16> cs;
+  if (wave != W_STATE0 && wave != W_STATE1) {
+    lds_barrier();
+    for (int it = -1; it <= nchunks; ++it) lds_barrier();
+    return;
+  }
+  // state waves
+  const int v = wave;
+  const int col0 = slice * DVS + 16 * v;
+  StateWave<DK, MAXD> sw;
 #pragma unroll
   for (int A = 0; A < DK / 16; ++A)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      cs.S[A][r] = a.S0 ? a.S0[((size_t)bh * DK + 16 * A + 4 * g + r) * a.dv + col0 + c] : 0.f;
-  // V rows: ping-pong registers, loaded one iteration before use
-  f32x4 v0[CNT], v1[CNT];
-  cs.load_v(a, head_row0, col0, v0);
-  __syncthreads();  // chunk 0's T, K and Q are in LDS
-  for (int64_t ci = 0; ci <= nchunks; ci += 2) {
-    if (ci + 1 < nchunks) cs.load_v(a, head_row0 + (ci + 1) * CH, col0, v1);
-    if (ci >= 1) cs.emit_O(a, head_row0 + (ci - 1) * CH, col0, lds[(ci - 1) & 1]);
-    if (ci < nchunks) cs.step(lds[ci & 1], v0);
-    __syncthreads();
-    if (ci + 1 > nchunks) break;
-    if (ci + 2 < nchunks) cs.load_v(a, head_row0 + (ci + 2) * CH, col0, v0);
-    cs.emit_O(a, head_row0 + ci * CH, col0, lds[ci & 1]);
-    if (ci + 1 < nchunks) cs.step(lds[(ci + 1) & 1], v1);
-    __syncthreads();
+      sw.S[A][r] = a.S0 ? a.S0[((size_t)bh * DK + 16 * A + 4 * g + r) * a.dv + col0 + c] : 0.f;
+  lds_barrier();
+  for (int it = -1; it <= nchunks; ++it) {
+    if (it >= 0 && it < nchunks) sw.step(ring(in, it & 3), ring(gr, it % 3), ring(buf, it & 1), v);
+    lds_barrier();
   }
 #pragma unroll
   for (int A = 0; A < DK / 16; ++A)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      a.S_out[((size_t)bh * DK + 16 * A + 4 * g + r) * a.dv + col0 + c] = cs.S[A][r];
+      a.S_out[((size_t)bh * DK + 16 * A + 4 * g + r) * a.dv + col0 + c] = sw.S[A][r];
 }
 
 int launch_chunk_fwd(const ChunkLaunch& p, hipStream_t s) {
@@ -495,15 +606,14 @@ int launch_chunk_fwd(const ChunkLaunch& p, hipStream_t s) {
   a.T = p.T;
   a.BH = p.B * p.H;
   a.dv = p.d_v;
-  a.o_bf16 = p.o_bf16;
   a.N = p.N;
   a.mask = p.mask;
   a.scale = p.scale;
   const dim3 grid((unsigned)(a.BH * (p.d_v / DVS)));
-  const dim3 block(4 * WAVE);
+  const dim3 block(NWAVES * WAVE);
   const bool narrow = p.mode == 0 && p.mask && p.N <= 16;
   auto go = [&](auto dk, auto mode, auto cmp, auto maxd) {
-    if (a.o_bf16)
+    if (p.o_bf16)
       hipLaunchKernelGGL((chunk_fwd_kernel<dk.value, mode.value, cmp.value, maxd.value, true>), grid,
                          block, 0, s, a);
     else

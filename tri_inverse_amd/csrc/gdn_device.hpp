@@ -109,6 +109,19 @@ __device__ __forceinline__ float fp8_to_f32(uint32_t word) {
   return __builtin_amdgcn_cvt_f32_fp8((int)word, BYTE);
 }
 
+// ---- LDS transpose read (gfx950 ds_read_b64_tr_b16) ------------------------------
+// Within each group of 16 lanes, lane i receives element (i % 4) of the 8-byte chunk
+// addressed by lane 4k + i/4 of its group, for k = 0..3.  With row-major bf16 rows
+// X[r][*] in LDS, lane (g, j) addressing X[r0 + 4g + j/4][c0 + 4(j%4)] therefore
+// receives X[r0 + 4g + k][c0 + j] for k = 0..3: four consecutive rows of column c0 + j.
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+
+__device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16* p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
 // ---- wave-wide reductions and scans (wave64) ------------------------------------
 
 __device__ __forceinline__ float wave_max(float v) {
