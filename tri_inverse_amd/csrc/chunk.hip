@@ -34,9 +34,12 @@
 // rows sit in LDS row-major; the K^T operand of the state update comes from the same
 // rows through the LDS transpose read.  Q is read once per workgroup, each lane taking
 // 16 contiguous bytes (8 consecutive d), so the contractions over d that involve Q use
-// that natural order of d in both operands.  Y, U' and P enter the MFMAs as hi/lo bf16
-// pairs (x = xh + xl; products take xh yh + xl yh + xh yl), which holds the error of O
-// and S near 1e-4 relative, so that the bf16 rounding of O itself dominates.
+// that natural order of d in both operands.  U' = T Y is formed as Y + (T - I) Y: the
+// identity part stays exact in fp32 and only the strictly lower part of T meets the
+// bf16-rounded Y.  U' (in O) and e^{G_C - G} U' (in the state update) and P enter the
+// MFMAs as hi/lo bf16 pairs (x = xh + xl; products take xh yh + xl yh + xh yl).  This
+// keeps the error of S near 1e-4 relative and that of O at the level of its own bf16
+// rounding.
 #include "gdn_kernels.hpp"
 #include "tri_block.hpp"
 
@@ -91,7 +94,7 @@ struct alignas(16) ChunkGates {
 // products of one chunk handed from their producers to their readers
 template <int DK>
 struct alignas(16) ChunkBuf {
-  bf16x8 trp[CNT][2][WAVE];         // T rows (row packs)
+  bf16x8 trp[CNT][2][WAVE];         // rows of T - I (row packs)
   __bf16 st[2][16][DK + KPAD];      // per state wave: S^T before the chunk, st[col][d]
   bf16x8 uh[2][2][WAVE];            // per state wave: U' column packs, high
   bf16x8 ul[2][2][WAVE];            // per state wave: U' column packs, low
@@ -172,6 +175,9 @@ __device__ __forceinline__ void produce_T(const ChunkArgs& a, const ChunkIn<DK>&
     doubling_T<CNT, CMP_BF16>(AD, AT, TT);
   else
     neumann_T<CNT, CMP, MAXD>(AD, AT, a.N, a.mask != 0, TT, cnt, count);
+  // T - I (exact in fp32): the state step adds the identity part of T Y in fp32
+#pragma unroll
+  for (int I = 0; I < CNT; ++I) TT.t[I][I] = TT.t[I][I] - eye_tile();
 #pragma unroll
   for (int I = 0; I < CNT; ++I)
 #pragma unroll
@@ -194,15 +200,31 @@ __device__ __forceinline__ void produce_T(const ChunkArgs& a, const ChunkIn<DK>&
 template <int DK, int MAXD>
 struct StateWave {
   static constexpr int NP = DK / 32;
-  f32x4 S[DK / 16];  // D-form tiles: lane (g,c) reg r = S[16a + 4g + r][col0 + c]
+  static constexpr int NA = DK / 16;
+  f32x4 S[NA];  // D-form tiles: lane (g,c) reg r = S[16a + 4g + r][col0 + c]
 
-  // one chunk: S packs out, K S, Y, U' = T Y (out), state update
+  // one chunk: S^T out, K S, Y, U' = T Y (out), state update.  LDS operands are
+  // requested in two batches, each ahead of the phase before the one that needs it, so
+  // that the reads overlap MFMA and VALU work instead of sitting between them.
   __device__ __forceinline__ void step(const ChunkIn<DK>& R, const ChunkGates& GT, ChunkBuf<DK>& B, int v) {
     const int l = lane_id(), g = l >> 4, c = l & 15;
-    // V tiles in D-form (rows 16I + 4g + r, column 16v + c) by the transpose read
+    // batch 1: K row packs, V tiles in D-form (rows 16I + 4g + r, column 16v + c) by the
+    // transpose read, beta and e^G
+    bf16x8 kf[CNT][NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int I = 0; I < CNT; ++I) kf[I][p] = rowpack_lds<DK>(R, 16 * I + c, p);
     bf16x4 vt[CNT];
 #pragma unroll
     for (int I = 0; I < CNT; ++I) vt[I] = lds_read_tr4(&R.v[16 * I + 4 * g + (c >> 2)][16 * v + 4 * (c & 3)]);
+    f32x4 b4[CNT], e4[CNT];
+#pragma unroll
+    for (int I = 0; I < CNT; ++I) {
+      b4[I] = *reinterpret_cast<const f32x4*>(&GT.beta[16 * I + 4 * g]);
+      e4[I] = *reinterpret_cast<const f32x4*>(&GT.eg[16 * I + 4 * g]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     // S as bf16: column packs for K S here, S^T rows (4 consecutive d per lane and
     // tile) for the output waves
     bf16x8 cps[NP];
@@ -213,79 +235,69 @@ struct StateWave {
       *reinterpret_cast<bf16x4*>(&B.st[v][c][32 * p + 4 * g]) = s0;
       *reinterpret_cast<bf16x4*>(&B.st[v][c][32 * p + 16 + 4 * g]) = s1;
     }
-    // K S (D-form), contraction over d_k, all four row tiles interleaved
+    // K S (D-form), contraction over d_k, the four row tiles interleaved
     f32x4 ks[CNT];
 #pragma unroll
     for (int I = 0; I < CNT; ++I) ks[I] = zero4();
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      bf16x8 kf[CNT];
+    for (int p = 0; p < NP; ++p)
 #pragma unroll
-      for (int I = 0; I < CNT; ++I) kf[I] = rowpack_lds<DK>(R, 16 * I + c, p);
-#pragma unroll
-      for (int I = 0; I < CNT; ++I) ks[I] = mma_bf16(kf[I], cps[p], ks[I]);
-    }
-    // Y = diag(beta) (V - diag(e^G) K S), D-form rows 16I + 4g + r
-    f32x4 y[CNT];
-#pragma unroll
-    for (int I = 0; I < CNT; ++I) {
-      const f32x4 b4 = *reinterpret_cast<const f32x4*>(&GT.beta[16 * I + 4 * g]);
-      const f32x4 e4 = *reinterpret_cast<const f32x4*>(&GT.eg[16 * I + 4 * g]);
-      y[I] = b4 * (unpack4(vt[I]) - e4 * ks[I]);
-    }
-    bf16x8 cyh[2], cyl[2];
-    pack8_hilo(y[0], y[1], cyh[0], cyl[0]);
-    pack8_hilo(y[2], y[3], cyh[1], cyl[1]);
-    // U' = T Y (D-form), Y as a hi/lo pair
+      for (int I = 0; I < CNT; ++I) ks[I] = mma_bf16(kf[I][p], cps[p], ks[I]);
+    __builtin_amdgcn_sched_barrier(0);
+    // batch 2: T row packs, e^{G_C - G}, e^{G_C}, K^T packs
     bf16x8 tf[CNT][2];
 #pragma unroll
     for (int I = 0; I < CNT; ++I)
 #pragma unroll
       for (int p = 0; p < 2; ++p)
         if (2 * p <= I && I - (2 * p + 1) <= MAXD) tf[I][p] = B.trp[I][p][l];
+    f32x4 w4[CNT];
+#pragma unroll
+    for (int I = 0; I < CNT; ++I) w4[I] = *reinterpret_cast<const f32x4*>(&GT.egcg[16 * I + 4 * g]);
+    const float egc = GT.egc;
+    bf16x8 kt[NA][2];
+#pragma unroll
+    for (int A = 0; A < NA; ++A)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) kt[A][p] = ktpack_lds<DK>(R, A, p);
+    __builtin_amdgcn_sched_barrier(0);
+    // Y = diag(beta) (V - diag(e^G) K S), D-form rows 16I + 4g + r
+    f32x4 y[CNT];
+#pragma unroll
+    for (int I = 0; I < CNT; ++I) y[I] = b4[I] * (unpack4(vt[I]) - e4[I] * ks[I]);
+    // U' = T Y = Y + (T - I) Y (D-form): the identity part exactly in fp32, the rest
+    // with Y rounded once to bf16
+    const bf16x8 cy[2] = {pack8(y[0], y[1]), pack8(y[2], y[3])};
     f32x4 u[CNT];
 #pragma unroll
-    for (int I = 0; I < CNT; ++I) u[I] = zero4();
+    for (int I = 0; I < CNT; ++I) u[I] = y[I];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int I = 0; I < CNT; ++I)
+        if (2 * p <= I && I - (2 * p + 1) <= MAXD) u[I] = mma_bf16(tf[I][p], cy[p], u[I]);
+    // S <- e^{G_C} S + K^T diag(e^{G_C - G}) U'
+    f32x4 ut[CNT];
+#pragma unroll
+    for (int I = 0; I < CNT; ++I) ut[I] = u[I] * w4[I];
+    bf16x8 cth[2], ctl[2];
+    pack8_hilo(ut[0], ut[1], cth[0], ctl[0]);
+    pack8_hilo(ut[2], ut[3], cth[1], ctl[1]);
+#pragma unroll
+    for (int A = 0; A < NA; ++A) S[A] = S[A] * egc;
 #pragma unroll
     for (int p = 0; p < 2; ++p)
 #pragma unroll
       for (int k = 0; k < 2; ++k)
 #pragma unroll
-        for (int I = 0; I < CNT; ++I)
-          if (2 * p <= I && I - (2 * p + 1) <= MAXD) u[I] = mma_bf16(tf[I][p], k ? cyl[p] : cyh[p], u[I]);
+        for (int A = 0; A < NA; ++A) S[A] = mma_bf16(kt[A][p], k ? ctl[p] : cth[p], S[A]);
+    // U' (hi/lo) for the output waves, off the state's dependency chain
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       bf16x8 h, lw;
       pack8_hilo(u[2 * p], u[2 * p + 1], h, lw);
       B.uh[v][p][l] = h;
       B.ul[v][p][l] = lw;
-    }
-    // S <- e^{G_C} S + K^T diag(e^{G_C - G}) U'
-    f32x4 ut[CNT];
-#pragma unroll
-    for (int I = 0; I < CNT; ++I) ut[I] = u[I] * *reinterpret_cast<const f32x4*>(&GT.egcg[16 * I + 4 * g]);
-    bf16x8 cth[2], ctl[2];
-    pack8_hilo(ut[0], ut[1], cth[0], ctl[0]);
-    pack8_hilo(ut[2], ut[3], cth[1], ctl[1]);
-    const float egc = GT.egc;
-#pragma unroll
-    for (int A0 = 0; A0 < DK / 16; A0 += 4) {
-      bf16x8 kt[4][2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int p = 0; p < 2; ++p) kt[i][p] = ktpack_lds<DK>(R, A0 + i, p);
-      f32x4 acc[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = S[A0 + i] * egc;
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] = mma_bf16(kt[i][p], k ? ctl[p] : cth[p], acc[i]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S[A0 + i] = acc[i];
     }
   }
 };
