@@ -211,27 +211,35 @@ def bench_chunk(torch, tri, synth, cfg, variants, steps, warmup, n_sets=2, stats
 
 
 def bench_wy(torch, tri, synth, steps, warmup):
-    B, H, T, dk, dv, C = 2, 16, 16384, 128, 128, 64
-    nb = B * H * T // C
-    sets = [{k: v.cuda() for k, v in synth.blocks(2 if s == 0 else 200 + s, nb, C, dk, k_dtype="bf16",
-                                                   d_v=dv).items()} for s in range(2)]
-    outs = [(torch.empty((nb, C, dk), device="cuda", dtype=torch.bfloat16),
-             torch.empty((nb, C, dv), device="cuda", dtype=torch.bfloat16)) for _ in range(2)]
+    """Chunk-size sweep: A build + masked N=3 inverse + W = T diag(beta) K, U = T diag(beta) V
+    at B=2, H=16, seq 16384, d_k = d_v = 128, for C = 64, 128, 256 (8192 / 4096 / 2048
+    blocks).  Bytes: K, V, beta, g read once, W and U (bf16) written once (1032 B per
+    token-head, independent of C).  FLOPs: the method's dense count per block, gram +
+    two Horner products + the two WY products (2 C^2 d each)."""
+    B, H, T, dk, dv = 2, 16, 16384, 128, 128
+    res = {}
+    for C in (64, 128, 256):
+        nb = B * H * T // C
+        sets = [{k: v.cuda() for k, v in synth.blocks(2 if s == 0 else 200 + s, nb, C, dk, k_dtype="bf16",
+                                                       d_v=dv).items()} for s in range(2)]
+        outs = [(torch.empty((nb, C, dk), device="cuda", dtype=torch.bfloat16),
+                 torch.empty((nb, C, dv), device="cuda", dtype=torch.bfloat16)) for _ in range(2)]
 
-    def launch(i):
-        x = sets[i]
-        tri.gdn_wy(x["K"], x["beta"], x["g"], x["V"], C=C, mode="neumann", N=3, mask=True,
-                   W_out=outs[i][0], U_out=outs[i][1])
-    ms, _ = time_launches(torch, launch, 2, steps, warmup)
-    tokens = B * T
-    by = B * H * T * (dk * 2 + dv * 2 + 8 + dk * 2 + dv * 2)
-    fl = nb * (2 * C * C * dk + 2 * 2 * C ** 3 + 2 * C * C * dk + 2 * C * C * dv)
-    del sets, outs
-    torch.cuda.empty_cache()
-    return {"C64_N3_masked": {"ms_per_step": ms, "tokens_per_s": tokens / (ms * 1e-3),
-                              "hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                              "mfma_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                              "bytes": by, "flops": fl}}
+        def launch(i):
+            x = sets[i]
+            tri.gdn_wy(x["K"], x["beta"], x["g"], x["V"], C=C, mode="neumann", N=3, mask=True,
+                       W_out=outs[i][0], U_out=outs[i][1])
+        ms, _ = time_launches(torch, launch, 2, steps, warmup)
+        tokens = B * T
+        by = B * H * T * (dk * 2 + dv * 2 + 8 + dk * 2 + dv * 2)
+        fl = nb * (2 * C * C * dk + 2 * 2 * C ** 3 + 2 * C * C * dk + 2 * C * C * dv)
+        res[f"C{C}_N3_masked"] = {"ms_per_step": ms, "tokens_per_s": tokens / (ms * 1e-3),
+                                  "hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                  "mfma_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                                  "bytes": by, "flops": fl, "n_blocks": nb}
+        del sets, outs
+        torch.cuda.empty_cache()
+    return res
 
 
 def profile_c1(torch, tri, synth, n):

@@ -112,7 +112,9 @@ gdn_status gdn_tri_inverse_neumann(const gdn_blocks* in, int32_t N, int32_t mask
   if (mask != 0 && mask != 1) return GDN_ERR_BAD_SHAPE;
   if (compute != GDN_F32 && compute != GDN_BF16 && compute != GDN_FP8_E4M3) return GDN_ERR_BAD_DTYPE;
   if (t_dtype != GDN_F32 && t_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
-  if (!chunk_small(in->C)) return GDN_ERR_UNSUPPORTED;
+  // C >= 128: the band kernel (masked, N <= 16, bf16 keys and products)
+  const bool band = !chunk_small(in->C);
+  if (band && (src != 1 || !mask || N > 16 || compute != GDN_BF16)) return GDN_ERR_UNSUPPORTED;
   if (stats && !aligned16(stats)) return GDN_ERR_BAD_ALIGNMENT;
   if (in->n_blocks > 0) {
     if (!T_out) return GDN_ERR_NULL_POINTER;
@@ -125,6 +127,9 @@ gdn_status gdn_tri_inverse_neumann(const gdn_blocks* in, int32_t N, int32_t mask
     if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;
   }
   if (in->n_blocks == 0) return GDN_OK;
+  if (band)
+    return launch_result(gdn::launch_band(to_args(in), nullptr, 0, N, 0, T_out, t_dtype == GDN_BF16,
+                                          nullptr, nullptr, 0, s));
   return launch_result(gdn::launch_neumann(to_args(in), src, N, mask, compute, T_out,
                                            t_dtype == GDN_BF16, st64, s));
 }
@@ -167,13 +172,19 @@ gdn_status gdn_wy(const gdn_blocks* in, const void* T, int32_t t_dtype, const gd
   if (d_v <= 0) return GDN_ERR_BAD_SHAPE;
   if (gate_k != 0 && gate_k != 1) return GDN_ERR_BAD_SHAPE;
   if (out_dtype != GDN_F32 && out_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
-  if (!(in->C == 32 || in->C == 64)) return GDN_ERR_UNSUPPORTED;
+  // C >= 128: the band kernel, T formed in-kernel as the masked sum with N <= 16
+  const bool band = in->C == 128 || in->C == 256;
+  if (band && (T || inv->mode != GDN_INV_NEUMANN || !inv->mask || inv->N > 16)) return GDN_ERR_UNSUPPORTED;
+  if (!(band || in->C == 32 || in->C == 64)) return GDN_ERR_UNSUPPORTED;
   if (!(in->d_k == 64 || in->d_k == 128) || !(d_v == 64 || d_v == 128)) return GDN_ERR_UNSUPPORTED;
   if (in->n_blocks == 0) return GDN_OK;
   if (!V || !W_out || !U_out) return GDN_ERR_NULL_POINTER;
   if (!aligned16(V) || !aligned16(W_out) || !aligned16(U_out) || (T && !aligned16(T)))
     return GDN_ERR_BAD_ALIGNMENT;
   const int mode = T ? 0 : inv->mode, N = T ? 0 : inv->N, mask = T ? 0 : inv->mask;
+  if (band)
+    return launch_result(gdn::launch_band(to_args(in), V, d_v, N, gate_k, nullptr, 0, W_out, U_out,
+                                          out_dtype == GDN_BF16, as_stream(stream)));
   return launch_result(gdn::launch_wy(to_args(in), T, t_dtype == GDN_BF16, mode, N, mask, V, d_v,
                                       gate_k, W_out, U_out, out_dtype == GDN_BF16,
                                       as_stream(stream)));

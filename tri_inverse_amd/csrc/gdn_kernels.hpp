@@ -34,6 +34,12 @@ int launch_wy(const BlocksArgs& a, const void* T, int t_bf16, int mode, int N, i
               const void* V, int d_v, int gate_k, void* W_out, void* U_out, int out_bf16,
               hipStream_t s);
 
+// masked truncated Neumann with band N <= 16 for C a multiple of 64 (d_k in {64, 128}):
+// T (T_out non-NULL, row-major [C][C]) or the WY products (d_v in {64, 128}); one
+// wave per 16-row tile, each on its own 32-row window
+int launch_band(const BlocksArgs& a, const void* V, int d_v, int N, int gate_k, void* T_out, int t_bf16,
+                void* W_out, void* U_out, int out_bf16, hipStream_t s);
+
 struct ChunkLaunch {
   const void* Q;
   const void* K;
