@@ -211,11 +211,13 @@ def bench_chunk(torch, tri, synth, cfg, variants, steps, warmup, n_sets=2, stats
 
 
 def bench_wy(torch, tri, synth, steps, warmup):
-    """Chunk-size sweep: A build + masked N=3 inverse + W = T diag(beta) K, U = T diag(beta) V
-    at B=2, H=16, seq 16384, d_k = d_v = 128, for C = 64, 128, 256 (8192 / 4096 / 2048
-    blocks).  Bytes: K, V, beta, g read once, W and U (bf16) written once (1032 B per
-    token-head, independent of C).  FLOPs: the method's dense count per block, gram +
-    two Horner products + the two WY products (2 C^2 d each)."""
+    """Chunk-size sweep: A build + inverse + W = T diag(beta) K, U = T diag(beta) V at B=2,
+    H=16, seq 16384, d_k = d_v = 128, for C = 64, 128, 256 (8192 / 4096 / 2048 blocks),
+    with the masked N=3 sum (the method), the unmasked one and the exact doubling product.
+    Bytes: K, V, beta, g read once, W and U (bf16) written once (1032 B per token-head,
+    independent of C).  FLOPs: the method's dense count per block: gram + the inverse's
+    C x C products (N-1 for the sum, 2(m-1) for doubling, m = ceil(log2 C)) + the two WY
+    products (2 C^2 d each)."""
     B, H, T, dk, dv = 2, 16, 16384, 128, 128
     res = {}
     for C in (64, 128, 256):
@@ -224,19 +226,21 @@ def bench_wy(torch, tri, synth, steps, warmup):
                                                        d_v=dv).items()} for s in range(2)]
         outs = [(torch.empty((nb, C, dk), device="cuda", dtype=torch.bfloat16),
                  torch.empty((nb, C, dv), device="cuda", dtype=torch.bfloat16)) for _ in range(2)]
-
-        def launch(i):
-            x = sets[i]
-            tri.gdn_wy(x["K"], x["beta"], x["g"], x["V"], C=C, mode="neumann", N=3, mask=True,
-                       W_out=outs[i][0], U_out=outs[i][1])
-        ms, _ = time_launches(torch, launch, 2, steps, warmup)
-        tokens = B * T
-        by = B * H * T * (dk * 2 + dv * 2 + 8 + dk * 2 + dv * 2)
-        fl = nb * (2 * C * C * dk + 2 * 2 * C ** 3 + 2 * C * C * dk + 2 * C * C * dv)
-        res[f"C{C}_N3_masked"] = {"ms_per_step": ms, "tokens_per_s": tokens / (ms * 1e-3),
-                                  "hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                  "mfma_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                                  "bytes": by, "flops": fl, "n_blocks": nb}
+        for mode, N, mask in (("neumann", 3, True), ("neumann", 3, False), ("exact", 0, False)):
+            def launch(i):
+                x = sets[i]
+                tri.gdn_wy(x["K"], x["beta"], x["g"], x["V"], C=C, mode=mode, N=max(N, 1), mask=mask,
+                           W_out=outs[i][0], U_out=outs[i][1])
+            ms, _ = time_launches(torch, launch, 2, steps, warmup)
+            tokens = B * T
+            by = B * H * T * (dk * 2 + dv * 2 + 8 + dk * 2 + dv * 2)
+            prods = 2 * ((C - 1).bit_length() - 1) if mode == "exact" else N - 1
+            fl = nb * (2 * C * C * dk + prods * 2 * C ** 3 + 2 * C * C * dk + 2 * C * C * dv)
+            name = f"C{C}_" + ("exact" if mode == "exact" else f"N{N}_{'masked' if mask else 'unmasked'}")
+            res[name] = {"ms_per_step": ms, "tokens_per_s": tokens / (ms * 1e-3),
+                         "hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "mfma_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                         "bytes": by, "flops": fl, "n_blocks": nb}
         del sets, outs
         torch.cuda.empty_cache()
     return res

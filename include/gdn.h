@@ -32,11 +32,10 @@
  *     caller's next synchronisation.  No C++ exception crosses the ABI.
  *   - The library allocates nothing, keeps no per-call state and is reentrant.
  *   - n_blocks == 0 (or B*H == 0, T == 0) is valid and enqueues nothing.
- *   - Supported chunk sizes C: 16, 32, 64 (all entry points); 128 and 256 for
- *     gdn_tri_inverse_neumann and gdn_wy with the masked sum (mask = 1, N <= 16),
- *     bf16 keys and bf16 products, T formed in-kernel.  d_k and d_v: multiples of
- *     32, at most 256, as each entry point states.  Anything else:
- *     GDN_ERR_UNSUPPORTED.
+ *   - Supported chunk sizes C: 16, 32, 64 (all entry points); 128 and 256 for the
+ *     inverse entry points and gdn_wy with bf16 keys and bf16 products (compute =
+ *     GDN_BF16), d_k and d_v in {64, 128}.  d_k and d_v otherwise: multiples of 32,
+ *     at most 256, as each entry point states.  Anything else: GDN_ERR_UNSUPPORTED.
  */
 #ifndef GDN_H
 #define GDN_H

@@ -94,22 +94,34 @@ def test_exact_and_build_A_validation():
 
 
 def test_large_chunk_routing():
-    """C = 128 and 256 are served for the masked sum with N <= 16, bf16 keys and bf16
-    products; other large-chunk requests report GDN_ERR_UNSUPPORTED (5) up front."""
+    """C = 128 and 256 take bf16 keys and bf16 products: the masked sum with N <= 16 on
+    the band kernel, every other Neumann / exact / given-T request on the full-triangle
+    kernel.  fp32 or fp8 products, A given, or head sizes outside {64, 128} report
+    GDN_ERR_UNSUPPORTED (5) up front; sizes are still range-checked (2)."""
     for C in (128, 256):
         assert neumann(blocks(C=C, n_blocks=0)) == 0
-        assert neumann(blocks(C=C, n_blocks=0), N=17) == 5           # band wider than a tile
-        assert neumann(blocks(C=C, n_blocks=0), mask=0) == 5
+        assert neumann(blocks(C=C, n_blocks=0), N=17) == 0            # full-triangle kernel
+        assert neumann(blocks(C=C, n_blocks=0), mask=0) == 0
         assert neumann(blocks(C=C, n_blocks=0), compute=tri.GDN_F32) == 5
+        assert neumann(blocks(C=C, n_blocks=0), compute=tri.GDN_FP8_E4M3) == 5
         assert neumann(blocks(C=C, n_blocks=0, A=FAKE, K=None, beta=None, g=None)) == 5  # A given
         assert neumann(blocks(C=C), N=C) == 2                         # N still range-checked
+        ex = lib.gdn_tri_inverse_exact(ctypes.byref(blocks(C=C, n_blocks=0)), tri.GDN_BF16, FAKE,
+                                       tri.GDN_F32, None)
+        assert ex == 0
+        ex = lib.gdn_tri_inverse_exact(ctypes.byref(blocks(C=C, n_blocks=0)), tri.GDN_F32, FAKE,
+                                       tri.GDN_F32, None)
+        assert ex == 5
     inv = tri.gdn_inverse_cfg()
     inv.mode, inv.N, inv.mask, inv.compute = tri.GDN_INV_NEUMANN, 3, 1, tri.GDN_BF16
     wy = lambda d, T=None, inv=inv, d_v=128: lib.gdn_wy(ctypes.byref(d), T, tri.GDN_F32, ctypes.byref(inv),
                                                           FAKE, d_v, 0, FAKE, FAKE, tri.GDN_BF16, None)
     for C in (128, 256):
         assert wy(blocks(C=C, n_blocks=0)) == 0
-        assert wy(blocks(C=C, n_blocks=0), T=FAKE) == 5               # given T: not at this size
+        assert wy(blocks(C=C, n_blocks=0), T=FAKE) == 0               # given T: full-triangle kernel
         assert wy(blocks(C=C, n_blocks=0), d_v=96) == 5
+        assert wy(blocks(C=C, n_blocks=0, d_k=256)) == 5
     inv.mask = 0
+    assert wy(blocks(C=128, n_blocks=0)) == 0
+    inv.compute = tri.GDN_FP8_E4M3
     assert wy(blocks(C=128, n_blocks=0)) == 5

@@ -110,3 +110,74 @@ def test_band_wy_full_size_sampled_blocks():
     Wr, Ur = oracle.wy(T64, f64(sub["K"]), f64(sub["V"]), f64(sub["beta"]), f64(sub["g"]), False)
     assert relF(f64(W[idx]), Wr) <= TOL
     assert relF(f64(U[idx]), Ur) <= TOL
+
+
+# ------------------------------------------------------------------ full lower triangle
+
+@pytest.mark.parametrize("C", [128, 256])
+@pytest.mark.parametrize("variant", [("neumann", 2, False), ("neumann", 3, False), ("neumann", 4, False),
+                                     ("neumann", 20, True), ("exact", 0, False)])
+def test_dense_inverse_large_chunks(C, variant):
+    mode, N, mask = variant
+    nb = 5
+    say(f"dense inverse C={C} {variant}")
+    inp = synth.blocks(31, nb, C, 128, k_dtype="bf16")
+    kw = dict(K=cuda(inp["K"]), beta=cuda(inp["beta"]), g=cuda(inp["g"]), C=C, compute="bf16",
+              t_dtype=torch.float32)
+    if mode == "exact":
+        T = tri.gdn_tri_inverse_exact(**kw)
+    else:
+        T = tri.gdn_tri_inverse_neumann(N=N, mask=mask, **kw)
+    torch.cuda.synchronize()
+    A64 = oracle.build_A(f64(inp["K"]), f64(inp["beta"]), f64(inp["g"]))
+    Tr = oracle.doubling(A64) if mode == "exact" else oracle.neumann(A64, N, mask)
+    T = f64(T)
+    assert relF(T, Tr) <= TOL, relF(T, Tr)
+    assert relF(eye_off(T), eye_off(Tr)) <= TOL, relF(eye_off(T), eye_off(Tr))
+    i, j = np.indices((C, C))
+    assert np.all(T[:, j > i] == 0) and np.all(T[:, i == j] == 1)
+    if mask:
+        assert np.all(T[:, i - j > N] == 0)
+
+
+@pytest.mark.parametrize("C", [128, 256])
+@pytest.mark.parametrize("source", ["neumann_unmasked", "exact", "given_f32", "given_bf16"])
+@pytest.mark.parametrize("gate_k", [False, True])
+def test_dense_wy_large_chunks(C, source, gate_k):
+    nb = 3
+    dk, dv = (128, 64) if C == 128 else (64, 128)
+    say(f"dense wy C={C} {source} gate_k={gate_k}")
+    inp = synth.blocks(32, nb, C, dk, k_dtype="bf16", d_v=dv)
+    A64 = oracle.build_A(f64(inp["K"]), f64(inp["beta"]), f64(inp["g"]))
+    args = (cuda(inp["K"]), cuda(inp["beta"]), cuda(inp["g"]), cuda(inp["V"]))
+    if source.startswith("given"):
+        Tt = torch.from_numpy(oracle.neumann(A64, 3, False)).to(torch.float32 if source == "given_f32"
+                                                                else torch.bfloat16)
+        T64 = f64(Tt)
+        W, U = tri.gdn_wy(*args, C=C, T=cuda(Tt), gate_k=gate_k, out_dtype=torch.float32)
+    elif source == "exact":
+        T64 = oracle.doubling(A64)
+        W, U = tri.gdn_wy(*args, C=C, mode="exact", gate_k=gate_k, out_dtype=torch.float32)
+    else:
+        T64 = oracle.neumann(A64, 3, False)
+        W, U = tri.gdn_wy(*args, C=C, mode="neumann", N=3, mask=False, gate_k=gate_k,
+                          out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    Wr, Ur = oracle.wy(T64, f64(inp["K"]), f64(inp["V"]), f64(inp["beta"]), f64(inp["g"]), gate_k)
+    assert relF(f64(W), Wr) <= TOL, relF(f64(W), Wr)
+    assert relF(f64(U), Ur) <= TOL, relF(f64(U), Ur)
+
+
+def test_dense_exact_cumulative_gates_many_blocks():
+    """Cumulative gates, T in bf16, 37 blocks of 256 (more blocks than one wave of
+    workgroups per XCD); sampled blocks against the oracle."""
+    C, nb = 256, 37
+    say("dense exact cumulative C=256")
+    inp = synth.blocks(33, nb, C, 128, k_dtype="bf16")
+    G = _cumulative(inp["g"], C).astype(np.float32)
+    T = tri.gdn_tri_inverse_exact(K=cuda(inp["K"]), beta=cuda(inp["beta"]), g=cuda(torch.from_numpy(G)), C=C,
+                                  compute="bf16", g_cumulative=True, t_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    idx = [0, 17, 36]
+    A64 = oracle.build_A(f64(inp["K"])[idx], f64(inp["beta"])[idx], G[idx], g_cumulative=True)
+    assert relF(f64(T[idx]), oracle.doubling(A64)) <= TOL

@@ -112,9 +112,11 @@ gdn_status gdn_tri_inverse_neumann(const gdn_blocks* in, int32_t N, int32_t mask
   if (mask != 0 && mask != 1) return GDN_ERR_BAD_SHAPE;
   if (compute != GDN_F32 && compute != GDN_BF16 && compute != GDN_FP8_E4M3) return GDN_ERR_BAD_DTYPE;
   if (t_dtype != GDN_F32 && t_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
-  // C >= 128: the band kernel (masked, N <= 16, bf16 keys and products)
-  const bool band = !chunk_small(in->C);
-  if (band && (src != 1 || !mask || N > 16 || compute != GDN_BF16)) return GDN_ERR_UNSUPPORTED;
+  // C >= 128 (bf16 keys and products): the band kernel for the masked sum with N <= 16,
+  // the full-triangle kernel otherwise
+  const bool large = !chunk_small(in->C);
+  if (large && (src != 1 || compute != GDN_BF16)) return GDN_ERR_UNSUPPORTED;
+  const bool band = large && mask && N <= 16;
   if (stats && !aligned16(stats)) return GDN_ERR_BAD_ALIGNMENT;
   if (in->n_blocks > 0) {
     if (!T_out) return GDN_ERR_NULL_POINTER;
@@ -130,6 +132,9 @@ gdn_status gdn_tri_inverse_neumann(const gdn_blocks* in, int32_t N, int32_t mask
   if (band)
     return launch_result(gdn::launch_band(to_args(in), nullptr, 0, N, 0, T_out, t_dtype == GDN_BF16,
                                           nullptr, nullptr, 0, s));
+  if (large)
+    return launch_result(gdn::launch_dense(to_args(in), nullptr, 0, 0, N, mask, nullptr, 0, 0, T_out,
+                                           t_dtype == GDN_BF16, nullptr, nullptr, 0, s));
   return launch_result(gdn::launch_neumann(to_args(in), src, N, mask, compute, T_out,
                                            t_dtype == GDN_BF16, st64, s));
 }
@@ -142,10 +147,14 @@ gdn_status gdn_tri_inverse_exact(const gdn_blocks* in, int32_t compute, void* T_
   if (compute == GDN_FP8_E4M3) return GDN_ERR_UNSUPPORTED;
   if (compute != GDN_F32 && compute != GDN_BF16) return GDN_ERR_BAD_DTYPE;
   if (t_dtype != GDN_F32 && t_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
-  if (!chunk_small(in->C)) return GDN_ERR_UNSUPPORTED;
+  const bool large = !chunk_small(in->C);
+  if (large && (src != 1 || compute != GDN_BF16)) return GDN_ERR_UNSUPPORTED;
   if (in->n_blocks == 0) return GDN_OK;
   if (!T_out) return GDN_ERR_NULL_POINTER;
   if (!aligned16(T_out)) return GDN_ERR_BAD_ALIGNMENT;
+  if (large)
+    return launch_result(gdn::launch_dense(to_args(in), nullptr, 0, 1, 0, 0, nullptr, 0, 0, T_out,
+                                           t_dtype == GDN_BF16, nullptr, nullptr, 0, as_stream(stream)));
   return launch_result(gdn::launch_exact(to_args(in), src, compute, T_out, t_dtype == GDN_BF16,
                                          as_stream(stream)));
 }
@@ -172,10 +181,11 @@ gdn_status gdn_wy(const gdn_blocks* in, const void* T, int32_t t_dtype, const gd
   if (d_v <= 0) return GDN_ERR_BAD_SHAPE;
   if (gate_k != 0 && gate_k != 1) return GDN_ERR_BAD_SHAPE;
   if (out_dtype != GDN_F32 && out_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
-  // C >= 128: the band kernel, T formed in-kernel as the masked sum with N <= 16
-  const bool band = in->C == 128 || in->C == 256;
-  if (band && (T || inv->mode != GDN_INV_NEUMANN || !inv->mask || inv->N > 16)) return GDN_ERR_UNSUPPORTED;
-  if (!(band || in->C == 32 || in->C == 64)) return GDN_ERR_UNSUPPORTED;
+  // C >= 128: the band kernel when T is formed as the masked sum with N <= 16, the
+  // full-triangle kernel otherwise (T formed, or given)
+  const bool large = in->C == 128 || in->C == 256;
+  const bool band = large && !T && inv->mode == GDN_INV_NEUMANN && inv->mask && inv->N <= 16;
+  if (!(large || in->C == 32 || in->C == 64)) return GDN_ERR_UNSUPPORTED;
   if (!(in->d_k == 64 || in->d_k == 128) || !(d_v == 64 || d_v == 128)) return GDN_ERR_UNSUPPORTED;
   if (in->n_blocks == 0) return GDN_OK;
   if (!V || !W_out || !U_out) return GDN_ERR_NULL_POINTER;
@@ -185,6 +195,10 @@ gdn_status gdn_wy(const gdn_blocks* in, const void* T, int32_t t_dtype, const gd
   if (band)
     return launch_result(gdn::launch_band(to_args(in), V, d_v, N, gate_k, nullptr, 0, W_out, U_out,
                                           out_dtype == GDN_BF16, as_stream(stream)));
+  if (large)
+    return launch_result(gdn::launch_dense(to_args(in), T, t_dtype == GDN_BF16, mode, N, mask, V, d_v,
+                                           gate_k, nullptr, 0, W_out, U_out, out_dtype == GDN_BF16,
+                                           as_stream(stream)));
   return launch_result(gdn::launch_wy(to_args(in), T, t_dtype == GDN_BF16, mode, N, mask, V, d_v,
                                       gate_k, W_out, U_out, out_dtype == GDN_BF16,
                                       as_stream(stream)));

@@ -40,6 +40,13 @@ int launch_wy(const BlocksArgs& a, const void* T, int t_bf16, int mode, int N, i
 int launch_band(const BlocksArgs& a, const void* V, int d_v, int N, int gate_k, void* T_out, int t_bf16,
                 void* W_out, void* U_out, int out_bf16, hipStream_t s);
 
+// full lower triangle at C in {128, 256} (d_k in {64, 128}): Neumann (any N, masked or
+// not) or exact doubling, as T (T_out) or as the WY products (d_v in {64, 128}); WY
+// of a given T (T_in, fp32 or bf16) too.  One workgroup of C/32 waves per block.
+int launch_dense(const BlocksArgs& a, const void* T_in, int t_in_bf16, int mode, int N, int mask,
+                 const void* V, int d_v, int gate_k, void* T_out, int t_bf16, void* W_out, void* U_out,
+                 int out_bf16, hipStream_t s);
+
 struct ChunkLaunch {
   const void* Q;
   const void* K;
