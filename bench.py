@@ -34,28 +34,29 @@ FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA
 N_SETS = 8
 
 
-def source_digest() -> str:
-    """Hash of the HIP sources: recorded next to counter-derived traffic figures so a
-    stale measurement is never reported for a changed kernel."""
+def source_digest(files=None) -> str:
+    """Hash of HIP sources (all of csrc/, or the named files of it): recorded next to
+    counter-derived traffic figures so a stale measurement is never reported for a
+    changed kernel."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tri_inverse_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + f.read())
+    names = files if files else [n for n in os.listdir(csrc) if n.endswith((".hip", ".hpp", ".cpp", ".h"))]
+    for name in sorted(names):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
 def load_traffic(kernel_key: str):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it was taken
-    on the current kernel sources (else None)."""
+    on the current sources of that kernel (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         data = json.load(f)
     ent = data.get(kernel_key)
-    if not ent or ent.get("source_digest") != source_digest():
+    if not ent or ent.get("source_digest") != source_digest(ent.get("source_files")):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -372,7 +373,7 @@ def main():
             "tokens_per_s": h3["tokens_per_s"], "ms_per_step": h3["ms_per_step"],
             "roofline": {"bound": "hbm", "achieved": h3["bytes"] / (h3["ms_per_step"] * 1e-3) / 1e9,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": h3["hbm_frac"],
-                         "traffic": load_traffic("chunk_fwd_kernel<128,0,1,1>")},
+                         "traffic": load_traffic("chunk_fwd_kernel<128,0,1,1,true>")},
             "variants": c3}
     if args.only in ("all", "c2"):
         out["wy"] = bench_wy(torch, tri, synth, max(5, args.steps // 5), 2)
