@@ -101,6 +101,8 @@ def c1_bytes_flops(variant, t_bytes=4):
     if variant[0] == "exact":
         m = (C - 1).bit_length()
         prods = 2 * (m - 1)
+    elif variant[0] == "residual":  # N-1 for T0, 1 for E, S Horner steps, 1 for T0 R
+        prods = variant[1] - 1 + 1 + variant[4] + 1
     else:
         prods = variant[1] - 1
     flops = gram + prods * 2 * C ** 3
@@ -125,6 +127,9 @@ def bench_c1(torch, tri, synth, steps, warmup):
             if variant[0] == "exact":
                 tri.gdn_tri_inverse_exact(K=x["K"], beta=x["beta"], g=x["g"], C=C, compute="bf16",
                                           out=outs[i])
+            elif variant[0] == "residual":
+                tri.gdn_tri_inverse_residual(K=x["K"], beta=x["beta"], g=x["g"], C=C, N=variant[1],
+                                             mask=variant[2], S=variant[4], compute="f32", out=outs[i])
             else:
                 tri.gdn_tri_inverse_neumann(K=x["K"], beta=x["beta"], g=x["g"], C=C, N=variant[1],
                                             mask=variant[2], compute="bf16", out=outs[i])
@@ -135,9 +140,11 @@ def bench_c1(torch, tri, synth, steps, warmup):
                 ("neumann", 4, True, torch.float32), ("neumann", 2, False, torch.float32),
                 ("neumann", 3, False, torch.float32), ("neumann", 4, False, torch.float32),
                 ("exact", 0, False, torch.float32), ("exact", 0, False, torch.bfloat16),
-                ("neumann", 3, True, torch.bfloat16)]
+                ("neumann", 3, True, torch.bfloat16), ("residual", 3, True, torch.float32, 8)]
     for v in variants:
         name = ("exact" if v[0] == "exact" else "N%d_%s" % (v[1], "masked" if v[2] else "unmasked"))
+        if v[0] == "residual":
+            name = "N%d_masked_residual_S%d_f32" % (v[1], v[4])
         name += "_T" + ("f32" if v[3] == torch.float32 else "bf16")
         st = steps if v == variants[0] else max(10, steps // 2)
         ms_step, ms_kernel = time_launches(torch, mk(v, v[3]), N_SETS, st, warmup)

@@ -134,6 +134,16 @@ gdn_status gdn_tri_inverse_neumann(const gdn_blocks* in, int32_t N, int32_t mask
 gdn_status gdn_tri_inverse_exact(const gdn_blocks* in, int32_t compute, void* T_out,
                                  int32_t t_dtype, void* stream);
 
+/* The truncated sum T(0) as in gdn_tri_inverse_neumann (N, mask) refined by the
+ * parallel residual correction of [GEO] Methodologie SS3: E = I - (I - A) T(0), then
+ * T = T(0) sum_{s=0}^{S} E^s, the sum of powers in Horner form (S products).  With the
+ * mask, E vanishes on subdiagonals 0..N, so T is exact on subdiagonals below
+ * (S+1)(N+1).  0 <= S <= 64 (GDN_ERR_BAD_SHAPE otherwise).  compute must be GDN_F32:
+ * E is a small difference of O(1) terms, which bf16 operands would not resolve
+ * (GDN_ERR_UNSUPPORTED otherwise).  C in {16, 32, 64}.  T_out as above. */
+gdn_status gdn_tri_inverse_residual(const gdn_blocks* in, int32_t N, int32_t mask, int32_t S,
+                                    int32_t compute, void* T_out, int32_t t_dtype, void* stream);
+
 /* WY products per block: W = T diag(s) K, U = T diag(beta) V with s = beta
  * (gate_k == 0) or s = beta .* exp(G) (gate_k != 0, the form the gated chunk
  * recurrence consumes).  T: if non-NULL, [n_blocks][C][C] of t_dtype (GDN_F32 or

@@ -125,3 +125,19 @@ def test_large_chunk_routing():
     assert wy(blocks(C=128, n_blocks=0)) == 0
     inv.compute = tri.GDN_FP8_E4M3
     assert wy(blocks(C=128, n_blocks=0)) == 5
+
+
+def test_residual_validation():
+    res = lambda d, N=3, mask=1, S=8, compute=tri.GDN_F32, T=FAKE: lib.gdn_tri_inverse_residual(
+        ctypes.byref(d) if d is not None else None, N, mask, S, compute, T, tri.GDN_F32, None)
+    assert res(None) == 1
+    assert res(blocks(), T=None) == 1
+    assert res(blocks(), S=-1) == 2
+    assert res(blocks(), S=65) == 2
+    assert res(blocks(), N=0) == 2
+    assert res(blocks(), mask=3) == 2
+    assert res(blocks(), compute=9) == 3
+    assert res(blocks(), compute=tri.GDN_BF16) == 5            # E needs fp32 products
+    assert res(blocks(C=128, n_blocks=0)) == 5
+    assert res(blocks(n_blocks=0)) == 0
+    assert res(blocks(A=FAKE, K=None, beta=None, g=None, n_blocks=0), S=0) == 0

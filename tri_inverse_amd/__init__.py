@@ -4,7 +4,7 @@ Thin ctypes layer: every function here has the name of the C entry point it call
 checks the tensors' device, dtype, shape and contiguity, and passes data pointers and
 the current HIP stream.  Every step of the computation runs in libgdn's HIP kernels;
 there is no CPU or PyTorch fallback.  If libgdn.so has not been built, importing this
-package raises ImportError (build it with ``python -m tri_inverse_amd.build``).
+package raises ImportError (build it with ``python tri_inverse_amd/build.py``).
 
 PyTorch is used only for device memory and streams.
 """
@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError("libgdn.so is not built (run `python -m tri_inverse_amd.build`); "
+    raise ImportError("libgdn.so is not built (run `python tri_inverse_amd/build.py`); "
                       "tri_inverse_amd has no fallback path")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -58,6 +58,8 @@ _lib.gdn_tri_inverse_neumann.restype = _i32
 _lib.gdn_tri_inverse_neumann.argtypes = [_P(gdn_blocks), _i32, _i32, _i32, _vp, _i32, _vp, _vp]
 _lib.gdn_tri_inverse_exact.restype = _i32
 _lib.gdn_tri_inverse_exact.argtypes = [_P(gdn_blocks), _i32, _vp, _i32, _vp]
+_lib.gdn_tri_inverse_residual.restype = _i32
+_lib.gdn_tri_inverse_residual.argtypes = [_P(gdn_blocks), _i32, _i32, _i32, _i32, _vp, _i32, _vp]
 _lib.gdn_wy.restype = _i32
 _lib.gdn_wy.argtypes = [_P(gdn_blocks), _vp, _i32, _P(gdn_inverse_cfg), _vp, _i32, _i32, _vp, _vp,
                         _i32, _vp]
@@ -66,7 +68,7 @@ _lib.gdn_chunk_fwd.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _v
                                _i64, _i32, _i32, _i32, _f32, _P(gdn_inverse_cfg), _vp, _vp]
 
 EXPORTED = ("gdn_abi_version", "gdn_status_string", "gdn_build_A", "gdn_tri_inverse_neumann",
-            "gdn_tri_inverse_exact", "gdn_wy", "gdn_chunk_fwd")
+            "gdn_tri_inverse_exact", "gdn_tri_inverse_residual", "gdn_wy", "gdn_chunk_fwd")
 
 
 class GdnError(RuntimeError):
@@ -189,6 +191,23 @@ def gdn_tri_inverse_exact(A=None, K=None, beta=None, g=None, C: int = 64, comput
     st = _lib.gdn_tri_inverse_exact(ctypes.byref(d), _compute_code(compute), _ptr(out),
                                     _TORCH_DTYPE[out.dtype], _stream(stream))
     _check(st, "gdn_tri_inverse_exact")
+    return out
+
+
+def gdn_tri_inverse_residual(A=None, K=None, beta=None, g=None, C: int = 64, N: int = 3,
+                             mask: bool = True, S: int = 8, compute="f32", t_dtype=torch.float32,
+                             g_cumulative: bool = False, out=None, stream=None):
+    """Truncated (optionally band-masked) Neumann sum refined by the parallel residual
+    correction T = T0 sum_{s<=S} E^s, E = I - (I - A) T0 -> T [n_blocks, C, C]."""
+    d, nb, _ = _blocks(A, K, beta, g, C, g_cumulative)
+    dev = (A if A is not None else K).device
+    if out is None:
+        out = torch.empty((nb, C, C), device=dev, dtype=t_dtype)
+    _dev(out, "out", (torch.float32, torch.bfloat16))
+    st = _lib.gdn_tri_inverse_residual(ctypes.byref(d), int(N), int(bool(mask)), int(S),
+                                       _compute_code(compute), _ptr(out), _TORCH_DTYPE[out.dtype],
+                                       _stream(stream))
+    _check(st, "gdn_tri_inverse_residual")
     return out
 
 

@@ -1,7 +1,7 @@
 """Build libgdn.so (the HIP library behind include/gdn.h) for gfx950 with hipcc.
 
 Every translation unit under csrc/ is compiled in parallel into _build/, then linked
-into tri_inverse_amd/libgdn.so.  Run as ``python -m tri_inverse_amd.build`` or through
+into tri_inverse_amd/libgdn.so.  Run as ``python tri_inverse_amd/build.py`` or through
 ``__graft_entry__.build()``.  Cross-compiles on a machine without a GPU.
 """
 from __future__ import annotations

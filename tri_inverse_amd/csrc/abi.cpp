@@ -159,6 +159,25 @@ gdn_status gdn_tri_inverse_exact(const gdn_blocks* in, int32_t compute, void* T_
                                          as_stream(stream)));
 }
 
+gdn_status gdn_tri_inverse_residual(const gdn_blocks* in, int32_t N, int32_t mask, int32_t S,
+                                    int32_t compute, void* T_out, int32_t t_dtype, void* stream) {
+  int src = 0;
+  gdn_status st = check_blocks(in, true, false, &src);
+  if (st != GDN_OK) return st;
+  if (N < 1 || N >= in->C) return GDN_ERR_BAD_SHAPE;
+  if (mask != 0 && mask != 1) return GDN_ERR_BAD_SHAPE;
+  if (S < 0 || S > 64) return GDN_ERR_BAD_SHAPE;
+  if (compute != GDN_F32 && compute != GDN_BF16 && compute != GDN_FP8_E4M3) return GDN_ERR_BAD_DTYPE;
+  if (t_dtype != GDN_F32 && t_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
+  if (compute != GDN_F32) return GDN_ERR_UNSUPPORTED;
+  if (!chunk_small(in->C)) return GDN_ERR_UNSUPPORTED;
+  if (in->n_blocks == 0) return GDN_OK;
+  if (!T_out) return GDN_ERR_NULL_POINTER;
+  if (!aligned16(T_out)) return GDN_ERR_BAD_ALIGNMENT;
+  return launch_result(gdn::launch_residual(to_args(in), src, N, mask, S, T_out, t_dtype == GDN_BF16,
+                                            as_stream(stream)));
+}
+
 gdn_status gdn_wy(const gdn_blocks* in, const void* T, int32_t t_dtype, const gdn_inverse_cfg* inv,
                   const void* V, int32_t d_v, int32_t gate_k, void* W_out, void* U_out,
                   int32_t out_dtype, void* stream) {

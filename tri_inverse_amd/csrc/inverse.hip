@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void build_A_kernel(BlocksArgs a, float* __res
 // (NT - 1 in general, 1 for the band-masked sum with N <= 16).
 template <int NT, int SRC, int DK, int CMP, int MODE, int MAXD>
 __global__ __launch_bounds__(256) void inverse_kernel(BlocksArgs a, int N, int mask, void* T_out,
-                                                      int t_bf16, unsigned long long* stats) {
+                                                      int t_bf16, unsigned long long* stats, int S) {
   constexpr int C = 16 * NT;
   const int64_t blk = (int64_t)blockIdx.x * (blockDim.x / WAVE) + (threadIdx.x / WAVE);
   if (blk >= a.n_blocks) return;
@@ -95,6 +95,8 @@ __global__ __launch_bounds__(256) void inverse_kernel(BlocksArgs a, int N, int m
   in.template to_A<MAXD, BANDED>(a, BANDED ? band : -1, AD, AT);
   if constexpr (MODE == MODE_EXACT)
     doubling_T<NT, CMP>(AD, AT, TT);
+  else if constexpr (MODE == MODE_RESIDUAL)
+    residual_T<NT>(AD, AT, N, mask != 0, S, TT);
   else
     neumann_T<NT, CMP, MAXD>(AD, AT, N, mask != 0, TT, cnt, count);
   if (t_bf16)
@@ -192,11 +194,11 @@ int launch_neumann(const BlocksArgs& a, int src, int N, int mask, int cmp, void*
       if (mask && N <= 16 && NTv > 2) {
         hipLaunchKernelGGL((inverse_kernel<NTv, sc.value, dk.value, cm.value, MODE_NEUMANN, 1>),
                            grid_for(a.n_blocks), dim3(WAVE * WAVES_PER_WG), 0, s, a, N, mask,
-                           T_out, t_bf16, stats);
+                           T_out, t_bf16, stats, 0);
       } else {
         hipLaunchKernelGGL((inverse_kernel<NTv, sc.value, dk.value, cm.value, MODE_NEUMANN, NTv - 1>),
                            grid_for(a.n_blocks), dim3(WAVE * WAVES_PER_WG), 0, s, a, N, mask,
-                           T_out, t_bf16, stats);
+                           T_out, t_bf16, stats, 0);
       }
       return 0;
     };
@@ -215,7 +217,7 @@ int launch_exact(const BlocksArgs& a, int src, int cmp, void* T_out, int t_bf16,
       hipLaunchKernelGGL((inverse_kernel<nt.value, sc.value, dk.value, cm.value, MODE_EXACT,
                                          nt.value - 1>),
                          grid_for(a.n_blocks), dim3(WAVE * WAVES_PER_WG), 0, s, a, 0, 0,
-                         T_out, t_bf16, (unsigned long long*)nullptr);
+                         T_out, t_bf16, (unsigned long long*)nullptr, 0);
       return 0;
     };
     switch (cmp) {
@@ -223,6 +225,17 @@ int launch_exact(const BlocksArgs& a, int src, int cmp, void* T_out, int t_bf16,
       case CMP_BF16: return go(std::integral_constant<int, CMP_BF16>{});
       default: return -1;
     }
+  });
+}
+
+// parallel residual correction on the Neumann sum: fp32 products throughout
+int launch_residual(const BlocksArgs& a, int src, int N, int mask, int S, void* T_out, int t_bf16,
+                    hipStream_t s) {
+  return dispatch_nt_src_dk(a.C, src, a.d_k, [&](auto nt, auto sc, auto dk) -> int {
+    hipLaunchKernelGGL((inverse_kernel<nt.value, sc.value, dk.value, CMP_F32, MODE_RESIDUAL, nt.value - 1>),
+                       grid_for(a.n_blocks), dim3(WAVE * WAVES_PER_WG), 0, s, a, N, mask, T_out, t_bf16,
+                       (unsigned long long*)nullptr, S);
+    return 0;
   });
 }
 

@@ -22,7 +22,7 @@
 namespace gdn {
 
 enum : int { CMP_F32 = 0, CMP_BF16 = 1, CMP_FP8 = 2 };
-enum : int { MODE_NEUMANN = 0, MODE_EXACT = 1 };
+enum : int { MODE_NEUMANN = 0, MODE_EXACT = 1, MODE_RESIDUAL = 2 };
 
 template <int NT>
 struct Mat {
@@ -605,6 +605,52 @@ __device__ __forceinline__ void neumann_T(const Mat<NT>& AD, const Mat<NT>& AT, 
     lmul<NT, CMP, true, MAXD, true>(AT, H, TT);
     if (mask) mask_T(TT, band);
   }
+}
+
+// ---- parallel residual correction ([GEO] Methodologie SS3) ----------------------
+// T(0) = the (optionally band-masked) truncated sum, E = I - (I - A) T(0) (its residual,
+// supported on subdiagonals > N when masked), and T = T(0) sum_{s<=S} E^s with the sum
+// of powers in Horner form R = I + E (I + E ( ... )).  E is a small difference of O(1)
+// terms, so every product here runs on the fp32 MFMA.  T(0) is formed in both tile
+// forms (right operand of A T(0), left operand of T(0) R).
+template <int NT>
+__device__ __forceinline__ void residual_T(const Mat<NT>& AD, const Mat<NT>& AT, int N, bool mask, int S,
+                                           Mat<NT>& TT) {
+  Mat<NT> HD = AD, HT = AT;  // H_1 = I + A
+  add_eye(HD);
+  add_eye(HT);
+  for (int k = 2; k <= N; ++k) {
+    Mat<NT> ZD, ZT;
+    lmul<NT, CMP_F32, false, NT - 1, true>(AT, HD, ZD);
+    lmul<NT, CMP_F32, true, NT - 1, true>(AT, HD, ZT);
+    HD = ZD;
+    HT = ZT;
+  }
+  if (mask) {
+    mask_D(HD, N);
+    mask_T(HT, N);
+  }
+  // E = A T(0) - (T(0) - I), T-form
+  Mat<NT> E;
+  lmul<NT, CMP_F32, true, NT - 1, false>(AT, HD, E);
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int J = 0; J <= I; ++J) E.t[I][J] -= HT.t[I][J];
+  add_eye(E);
+  // R = I + E R, S times, D-form
+  Mat<NT> R;
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int J = 0; J < NT; ++J) R.t[I][J] = zero4();
+  add_eye(R);
+  for (int s = 0; s < S; ++s) {
+    Mat<NT> Z;
+    lmul<NT, CMP_F32, false, NT - 1, true>(E, R, Z);
+    R = Z;
+  }
+  lmul<NT, CMP_F32, true, NT - 1, false>(HT, R, TT);
 }
 
 // exact doubling: P = I + A; X = A; for q = 1..m-1: X <- X X; P <- P + P X
