@@ -159,6 +159,36 @@ def bench_c1(torch, tri, synth, steps, warmup):
     return results
 
 
+def bench_fs_speedup(torch, tri, synth, steps, warmup):
+    """The pages' headline metric: speedup of the multiplication-only inverses over
+    forward substitution, here both on MI355X.  B=1, H=16, seq 8192 at C = 32 and 64
+    (4096 / 2048 blocks), A built in-kernel from bf16 keys, T fp32; forward substitution
+    in fp32 (the sequential baseline), the masked N=3 sum and exact doubling in bf16."""
+    res = {}
+    for C in (32, 64):
+        nb = C1["B"] * C1["H"] * C1["T"] // C
+        sets = [{k: v.cuda() for k, v in synth.blocks(1 if s == 0 else 1000 + s, nb, C, C1["d_k"],
+                                                       k_dtype="bf16").items()} for s in range(N_SETS)]
+        outs = [torch.empty((nb, C, C), device="cuda") for _ in range(N_SETS)]
+        calls = {
+            "fs": lambda x, o: tri.gdn_tri_inverse_fs(K=x["K"], beta=x["beta"], g=x["g"], C=C, out=o),
+            "N3_masked": lambda x, o: tri.gdn_tri_inverse_neumann(K=x["K"], beta=x["beta"], g=x["g"], C=C, N=3,
+                                                                  mask=True, compute="bf16", out=o),
+            "exact": lambda x, o: tri.gdn_tri_inverse_exact(K=x["K"], beta=x["beta"], g=x["g"], C=C,
+                                                            compute="bf16", out=o),
+        }
+        ms = {}
+        for name, f in calls.items():
+            ms[name], _ = time_launches(torch, lambda i, f=f: f(sets[i], outs[i]), N_SETS, steps, warmup)
+        res[f"C{C}"] = {"n_blocks": nb, "us_fs": ms["fs"] * 1e3, "us_N3_masked": ms["N3_masked"] * 1e3,
+                        "us_exact": ms["exact"] * 1e3,
+                        "speedup_N3_masked_over_fs": ms["fs"] / ms["N3_masked"],
+                        "speedup_exact_over_fs": ms["fs"] / ms["exact"]}
+        del sets, outs
+        torch.cuda.empty_cache()
+    return res
+
+
 # ------------------------------------------------------------------ c3 / c4: chunk forward
 
 C3 = dict(B=4, H=16, T=8192, d_k=128, d_v=128, C=64)
@@ -382,6 +412,8 @@ def main():
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": h3["hbm_frac"],
                          "traffic": load_traffic("chunk_fwd_kernel<128,0,1,1,true>")},
             "variants": c3}
+    if args.only in ("all", "fs"):
+        out["fs_speedup"] = bench_fs_speedup(torch, tri, synth, max(10, args.steps // 2), 3)
     if args.only in ("all", "c2"):
         out["wy"] = bench_wy(torch, tri, synth, max(5, args.steps // 5), 2)
     if args.only in ("all", "c4"):

@@ -144,6 +144,12 @@ gdn_status gdn_tri_inverse_exact(const gdn_blocks* in, int32_t compute, void* T_
 gdn_status gdn_tri_inverse_residual(const gdn_blocks* in, int32_t N, int32_t mask, int32_t S,
                                     int32_t compute, void* T_out, int32_t t_dtype, void* stream);
 
+/* T = (I - A)^-1 by forward substitution, T = I + A T row by row ([GEO] problem
+ * statement: the sequential baseline the multiplication-only inverses replace), in
+ * fp32 with C (C-1)/2 dependent-row multiply-adds per block.  C in {16, 32, 64}.
+ * T_out [n_blocks][C][C], t_dtype GDN_F32 or GDN_BF16. */
+gdn_status gdn_tri_inverse_fs(const gdn_blocks* in, void* T_out, int32_t t_dtype, void* stream);
+
 /* WY products per block: W = T diag(s) K, U = T diag(beta) V with s = beta
  * (gate_k == 0) or s = beta .* exp(G) (gate_k != 0, the form the gated chunk
  * recurrence consumes).  T: if non-NULL, [n_blocks][C][C] of t_dtype (GDN_F32 or

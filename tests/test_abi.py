@@ -141,3 +141,14 @@ def test_residual_validation():
     assert res(blocks(C=128, n_blocks=0)) == 5
     assert res(blocks(n_blocks=0)) == 0
     assert res(blocks(A=FAKE, K=None, beta=None, g=None, n_blocks=0), S=0) == 0
+
+
+def test_fs_validation():
+    fs = lambda d, T=FAKE, t=tri.GDN_F32: lib.gdn_tri_inverse_fs(ctypes.byref(d) if d is not None else None,
+                                                                  T, t, None)
+    assert fs(None) == 1
+    assert fs(blocks(), T=None) == 1
+    assert fs(blocks(), t=tri.GDN_FP8_E4M3) == 3
+    assert fs(blocks(C=128, n_blocks=0)) == 5
+    assert fs(blocks(n_blocks=0)) == 0
+    assert fs(blocks(), T=FAKE + 4) == 4

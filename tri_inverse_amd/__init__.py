@@ -60,6 +60,8 @@ _lib.gdn_tri_inverse_exact.restype = _i32
 _lib.gdn_tri_inverse_exact.argtypes = [_P(gdn_blocks), _i32, _vp, _i32, _vp]
 _lib.gdn_tri_inverse_residual.restype = _i32
 _lib.gdn_tri_inverse_residual.argtypes = [_P(gdn_blocks), _i32, _i32, _i32, _i32, _vp, _i32, _vp]
+_lib.gdn_tri_inverse_fs.restype = _i32
+_lib.gdn_tri_inverse_fs.argtypes = [_P(gdn_blocks), _vp, _i32, _vp]
 _lib.gdn_wy.restype = _i32
 _lib.gdn_wy.argtypes = [_P(gdn_blocks), _vp, _i32, _P(gdn_inverse_cfg), _vp, _i32, _i32, _vp, _vp,
                         _i32, _vp]
@@ -68,7 +70,8 @@ _lib.gdn_chunk_fwd.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _v
                                _i64, _i32, _i32, _i32, _f32, _P(gdn_inverse_cfg), _vp, _vp]
 
 EXPORTED = ("gdn_abi_version", "gdn_status_string", "gdn_build_A", "gdn_tri_inverse_neumann",
-            "gdn_tri_inverse_exact", "gdn_tri_inverse_residual", "gdn_wy", "gdn_chunk_fwd")
+            "gdn_tri_inverse_exact", "gdn_tri_inverse_residual", "gdn_tri_inverse_fs", "gdn_wy",
+            "gdn_chunk_fwd")
 
 
 class GdnError(RuntimeError):
@@ -208,6 +211,19 @@ def gdn_tri_inverse_residual(A=None, K=None, beta=None, g=None, C: int = 64, N: 
                                        _compute_code(compute), _ptr(out), _TORCH_DTYPE[out.dtype],
                                        _stream(stream))
     _check(st, "gdn_tri_inverse_residual")
+    return out
+
+
+def gdn_tri_inverse_fs(A=None, K=None, beta=None, g=None, C: int = 64, t_dtype=torch.float32,
+                       g_cumulative: bool = False, out=None, stream=None):
+    """Forward substitution (fp32), the sequential baseline -> T [n_blocks, C, C]."""
+    d, nb, _ = _blocks(A, K, beta, g, C, g_cumulative)
+    dev = (A if A is not None else K).device
+    if out is None:
+        out = torch.empty((nb, C, C), device=dev, dtype=t_dtype)
+    _dev(out, "out", (torch.float32, torch.bfloat16))
+    st = _lib.gdn_tri_inverse_fs(ctypes.byref(d), _ptr(out), _TORCH_DTYPE[out.dtype], _stream(stream))
+    _check(st, "gdn_tri_inverse_fs")
     return out
 
 

@@ -178,6 +178,18 @@ gdn_status gdn_tri_inverse_residual(const gdn_blocks* in, int32_t N, int32_t mas
                                             as_stream(stream)));
 }
 
+gdn_status gdn_tri_inverse_fs(const gdn_blocks* in, void* T_out, int32_t t_dtype, void* stream) {
+  int src = 0;
+  gdn_status st = check_blocks(in, true, false, &src);
+  if (st != GDN_OK) return st;
+  if (t_dtype != GDN_F32 && t_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
+  if (!chunk_small(in->C)) return GDN_ERR_UNSUPPORTED;
+  if (in->n_blocks == 0) return GDN_OK;
+  if (!T_out) return GDN_ERR_NULL_POINTER;
+  if (!aligned16(T_out)) return GDN_ERR_BAD_ALIGNMENT;
+  return launch_result(gdn::launch_fs(to_args(in), src, T_out, t_dtype == GDN_BF16, as_stream(stream)));
+}
+
 gdn_status gdn_wy(const gdn_blocks* in, const void* T, int32_t t_dtype, const gdn_inverse_cfg* inv,
                   const void* V, int32_t d_v, int32_t gate_k, void* W_out, void* U_out,
                   int32_t out_dtype, void* stream) {

@@ -30,6 +30,8 @@ void launch_zero_stats(unsigned long long* stats, hipStream_t s);
 // truncated sum refined by the parallel residual correction (S Horner steps in E), fp32
 int launch_residual(const BlocksArgs& a, int src, int N, int mask, int S, void* T_out, int t_bf16,
                     hipStream_t s);
+// forward substitution (fp32), the sequential baseline, C <= 64
+int launch_fs(const BlocksArgs& a, int src, void* T_out, int t_bf16, hipStream_t s);
 
 // WY products; T given (t_bf16 selects its dtype) or formed with (mode, N, mask);
 // C in {32, 64}, d_k and d_v in {64, 128}

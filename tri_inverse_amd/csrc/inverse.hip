@@ -108,6 +108,48 @@ __global__ __launch_bounds__(256) void inverse_kernel(BlocksArgs a, int N, int m
   }
 }
 
+// Forward substitution, the sequential baseline of [GEO]'s problem statement:
+// T = I + A T row by row, T[i][.] = e_i + sum_{m<i} A[i][m] T[m][.], in fp32.  One wave
+// per block; lane j holds column j of T in registers (Tc[i] = T[i][j]); each A[i][m] is
+// broadcast with one readlane straight from the T-form tiles of A (lane (g,c) reg r of
+// tile (I,J) holds A[16I + c][16J + 4g + r]).  C (C - 1) / 2 dependent-row FMAs.
+template <int NT, int SRC, int DK>
+__global__ __launch_bounds__(256) void fs_kernel(BlocksArgs a, void* T_out, int t_bf16) {
+  constexpr int C = 16 * NT;
+  const int64_t blk = (int64_t)blockIdx.x * (blockDim.x / WAVE) + (threadIdx.x / WAVE);
+  if (blk >= a.n_blocks) return;
+  BlockIn<NT, SRC, DK> in;
+  in.load(a, blk);
+  Mat<NT> AD, AT;
+  in.template to_A<NT - 1, false>(a, -1, AD, AT);
+  const int j = lane_id();
+  float Tc[C];
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    float acc = (j == i) ? 1.f : 0.f;
+#pragma unroll
+    for (int m = 0; m < i; ++m) {
+      // copy the element out first: a bit cast applied to a vector-element expression
+      // directly reads the vector's first element
+      const float e = AT.t[i / 16][m / 16][m % 4];
+      const float aim = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), 16 * ((m % 16) / 4) + (i % 16)));
+      acc = fmaf(aim, Tc[m], acc);
+    }
+    Tc[i] = acc;
+  }
+  if (j < C) {
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      const size_t o = (size_t)blk * C * C + (size_t)i * C + j;
+      if (t_bf16)
+        reinterpret_cast<__bf16*>(T_out)[o] = (__bf16)Tc[i];
+      else
+        reinterpret_cast<float*>(T_out)[o] = Tc[i];
+    }
+  }
+}
+
 __global__ void zero_u64_kernel(unsigned long long* p, int n) {
   int i = threadIdx.x;
   if (i < n) p[i] = 0ull;
@@ -235,6 +277,15 @@ int launch_residual(const BlocksArgs& a, int src, int N, int mask, int S, void* 
     hipLaunchKernelGGL((inverse_kernel<nt.value, sc.value, dk.value, CMP_F32, MODE_RESIDUAL, nt.value - 1>),
                        grid_for(a.n_blocks), dim3(WAVE * WAVES_PER_WG), 0, s, a, N, mask, T_out, t_bf16,
                        (unsigned long long*)nullptr, S);
+    return 0;
+  });
+}
+
+// forward substitution (fp32), the sequential baseline
+int launch_fs(const BlocksArgs& a, int src, void* T_out, int t_bf16, hipStream_t s) {
+  return dispatch_nt_src_dk(a.C, src, a.d_k, [&](auto nt, auto sc, auto dk) -> int {
+    hipLaunchKernelGGL((fs_kernel<nt.value, sc.value, dk.value>), grid_for(a.n_blocks),
+                       dim3(WAVE * WAVES_PER_WG), 0, s, a, T_out, t_bf16);
     return 0;
   });
 }

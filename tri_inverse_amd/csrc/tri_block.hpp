@@ -22,7 +22,7 @@
 namespace gdn {
 
 enum : int { CMP_F32 = 0, CMP_BF16 = 1, CMP_FP8 = 2 };
-enum : int { MODE_NEUMANN = 0, MODE_EXACT = 1, MODE_RESIDUAL = 2 };
+enum : int { MODE_NEUMANN = 0, MODE_EXACT = 1, MODE_RESIDUAL = 2, MODE_FS = 3 };
 
 template <int NT>
 struct Mat {
