@@ -284,6 +284,45 @@ def bench_wy(torch, tri, synth, steps, warmup):
     return res
 
 
+DEC = dict(H=32, d_k=128, d_v=128)
+
+
+def decode_bytes(B, H, n, dk, dv):
+    """Compulsory bytes of one decode call: the fp32 state read and written once, q, k,
+    v (bf16), beta and g read and o (bf16) written once per token."""
+    return B * H * (2 * dk * dv * 4 + n * (2 * dk * 2 + dv * 2 + 8 + dv * 2))
+
+
+def bench_decode(torch, tri, synth, steps, warmup):
+    """Gated delta rule token by token (the decode kernel), 32 heads, d_k = d_v = 128,
+    bf16 q/k/v/o, fp32 state updated in place:
+      batch64_step: one token for each of 64 sequences (B=64, n=1), four 128 MiB state
+        sets rotating so that the state is not served from the 256 MB Infinity Cache;
+      seq64: 64 tokens of one sequence per call, the state kept on chip (B=1, n=64);
+      batch1_step: one token of one sequence (B=1, n=1), the latency of one step."""
+    H, dk, dv = DEC["H"], DEC["d_k"], DEC["d_v"]
+    res = {}
+    for name, B, n, n_sets in (("batch64_step", 64, 1, 4), ("seq64", 1, 64, 4), ("batch1_step", 1, 1, 4)):
+        sets = []
+        for i in range(n_sets):
+            x = {k: v.cuda() for k, v in synth.prefill(60 + i, B, H, n, dk, dv).items()}
+            x["S"] = torch.zeros((B, H, dk, dv), device="cuda")
+            x["O"] = torch.empty((B, H, n, dv), device="cuda", dtype=torch.bfloat16)
+            sets.append(x)
+
+        def launch(i):
+            x = sets[i]
+            tri.gdn_decode(x["Q"], x["K"], x["V"], x["beta"], x["g"], S=x["S"], S_out=x["S"], O=x["O"])
+        ms, _ = time_launches(torch, launch, n_sets, steps, warmup)
+        by = decode_bytes(B, H, n, dk, dv)
+        res[name] = {"B": B, "H": H, "tokens_per_call": n, "ms_per_step": ms,
+                     "us_per_token": ms * 1e3 / n, "tokens_per_s": B * n / (ms * 1e-3),
+                     "bytes": by, "hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del sets
+        torch.cuda.empty_cache()
+    return res
+
+
 def profile_c1(torch, tri, synth, n):
     """Headline launch n times on rotating buffer sets, then a plain 256 MiB copy n
     times: the copy's FETCH_SIZE / WRITE_SIZE per dispatch calibrate the counters."""
@@ -414,6 +453,17 @@ def main():
             "variants": c3}
     if args.only in ("all", "fs"):
         out["fs_speedup"] = bench_fs_speedup(torch, tri, synth, max(10, args.steps // 2), 3)
+    if args.only in ("all", "decode"):
+        dec = bench_decode(torch, tri, synth, max(20, args.steps), 5)
+        hd = dec["batch64_step"]
+        out["decode"] = {
+            "workload": "GDN decode, 32 heads, d_k=d_v=128, bf16 q/k/v/o, fp32 state in place; "
+                        "headline: one step for 64 sequences",
+            "tokens_per_s": hd["tokens_per_s"], "ms_per_step": hd["ms_per_step"],
+            "roofline": {"bound": "hbm", "achieved": hd["bytes"] / (hd["ms_per_step"] * 1e-3) / 1e9,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": hd["hbm_frac"],
+                         "traffic": None},
+            "variants": dec}
     if args.only in ("all", "c2"):
         out["wy"] = bench_wy(torch, tri, synth, max(5, args.steps // 5), 2)
     if args.only in ("all", "c4"):

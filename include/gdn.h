@@ -175,6 +175,23 @@ gdn_status gdn_chunk_fwd(const void* Q, const void* K, const void* V, int32_t qk
                          int32_t d_k, int32_t d_v, int32_t C, float scale,
                          const gdn_inverse_cfg* inv, uint64_t* stats, void* stream);
 
+/* The gated delta rule one token at a time (decode).  Per (b, h), tokens t = 0..n-1 in
+ * order, a = exp(g_t), state S [d_k][d_v] fp32 entering as S_in (zeros if NULL):
+ *   r = S^T k_t, p = S^T q_t;  u = beta_t (v_t - a r);  S <- a S + k_t u^T;
+ *   o_t = scale (a p + (k_t . q_t) u)
+ * (the state read / delta correction / state write split of one step, [PSDA] section
+ * 2.B).  The state stays on chip for all n tokens of the call and is read and written
+ * once ([PSDA] section 2.A's persistent state); n = 1 is one decode step.
+ * Q, K [B][H][n][d_k] and V [B][H][n][d_v] in qkv_dtype (GDN_BF16 or GDN_F32); beta, g
+ * [B][H][n] fp32; S_in, S_out [B][H][d_k][d_v] fp32, and here S_out MAY equal S_in (the
+ * update in place; any other overlap is invalid); O [B][H][n][d_v] in o_dtype (GDN_BF16
+ * or GDN_F32).  d_k in {64, 128}; d_v a multiple of 32, at most 256
+ * (GDN_ERR_UNSUPPORTED otherwise).  n == 0 writes S_out = S_in (or zeros). */
+gdn_status gdn_decode(const void* Q, const void* K, const void* V, int32_t qkv_dtype,
+                      const float* beta, const float* g, const float* S_in, float* S_out,
+                      void* O, int32_t o_dtype, int32_t B, int32_t H, int32_t n,
+                      int32_t d_k, int32_t d_v, float scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

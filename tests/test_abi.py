@@ -152,3 +152,21 @@ def test_fs_validation():
     assert fs(blocks(C=128, n_blocks=0)) == 5
     assert fs(blocks(n_blocks=0)) == 0
     assert fs(blocks(), T=FAKE + 4) == 4
+
+
+def test_decode_validation():
+    def dec(Q=FAKE, S_in=None, S_out=FAKE, qd=tri.GDN_BF16, od=tri.GDN_BF16, B=1, H=1, n=1,
+            dk=128, dv=128):
+        return lib.gdn_decode(Q, FAKE, FAKE, qd, FAKE, FAKE, S_in, S_out, FAKE, od, B, H, n, dk,
+                              dv, 1.0, None)
+    assert dec(B=-1) == 2
+    assert dec(n=-1) == 2
+    assert dec(qd=tri.GDN_FP8_E4M3) == 3
+    assert dec(od=tri.GDN_FP8_E4M3) == 3
+    assert dec(dk=96) == 5
+    assert dec(dv=48) == 5
+    assert dec(dv=288) == 5
+    assert dec(B=0) == 0
+    assert dec(S_out=None) == 1
+    assert dec(Q=None) == 1
+    assert dec(S_in=FAKE + 8) == 4

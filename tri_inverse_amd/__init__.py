@@ -68,10 +68,13 @@ _lib.gdn_wy.argtypes = [_P(gdn_blocks), _vp, _i32, _P(gdn_inverse_cfg), _vp, _i3
 _lib.gdn_chunk_fwd.restype = _i32
 _lib.gdn_chunk_fwd.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
                                _i64, _i32, _i32, _i32, _f32, _P(gdn_inverse_cfg), _vp, _vp]
+_lib.gdn_decode.restype = _i32
+_lib.gdn_decode.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                            _i32, _i32, _f32, _vp]
 
 EXPORTED = ("gdn_abi_version", "gdn_status_string", "gdn_build_A", "gdn_tri_inverse_neumann",
             "gdn_tri_inverse_exact", "gdn_tri_inverse_residual", "gdn_tri_inverse_fs", "gdn_wy",
-            "gdn_chunk_fwd")
+            "gdn_chunk_fwd", "gdn_decode")
 
 
 class GdnError(RuntimeError):
@@ -296,4 +299,41 @@ def gdn_chunk_fwd(Q, K, V, beta, g, C: int = 64, scale: float | None = None, S0=
                             _ptr(O), _TORCH_DTYPE[O.dtype], _ptr(S_out), B, H, T, dk, dv, C,
                             float(scale), ctypes.byref(cfg), _ptr(stats), _stream(stream))
     _check(st, "gdn_chunk_fwd")
+    return O, S_out
+
+
+def gdn_decode(Q, K, V, beta, g, S=None, scale: float | None = None, S_out=None, O=None,
+               o_dtype=torch.bfloat16, stream=None):
+    """Gated delta rule token by token with the state kept on chip for all n tokens.
+    Q, K [B,H,n,d_k], V [B,H,n,d_v] (bf16 or fp32, one dtype); beta, g [B,H,n] fp32;
+    S [B,H,d_k,d_v] fp32 or None (zeros).  Pass S_out=S to update the state in place.
+    Returns (O [B,H,n,d_v], S_out [B,H,d_k,d_v] fp32)."""
+    for t, n_ in ((Q, "Q"), (K, "K"), (V, "V")):
+        _dev(t, n_, (torch.bfloat16, torch.float32))
+    if not (Q.dtype == K.dtype == V.dtype):
+        raise ValueError("Q, K and V must share one dtype")
+    _dev(beta, "beta", (torch.float32,))
+    _dev(g, "g", (torch.float32,))
+    if K.dim() != 4 or Q.shape != K.shape:
+        raise ValueError("Q and K must both be [B, H, n, d_k]")
+    B, H, n, dk = K.shape
+    dv = V.shape[-1]
+    if V.shape[:3] != (B, H, n) or beta.shape != (B, H, n) or g.shape != (B, H, n):
+        raise ValueError("V, beta, g must match Q/K in [B, H, n]")
+    if S is not None:
+        _dev(S, "S", (torch.float32,))
+        if S.shape != (B, H, dk, dv):
+            raise ValueError("S must be [B, H, d_k, d_v]")
+    if O is None:
+        O = torch.empty((B, H, n, dv), device=K.device, dtype=o_dtype)
+    if S_out is None:
+        S_out = torch.empty((B, H, dk, dv), device=K.device, dtype=torch.float32)
+    _dev(O, "O", (torch.float32, torch.bfloat16))
+    _dev(S_out, "S_out", (torch.float32,))
+    if scale is None:
+        scale = dk ** -0.5
+    st = _lib.gdn_decode(_ptr(Q), _ptr(K), _ptr(V), _TORCH_DTYPE[K.dtype], _ptr(beta), _ptr(g),
+                         _ptr(S), _ptr(S_out), _ptr(O), _TORCH_DTYPE[O.dtype], B, H, n, dk, dv,
+                         float(scale), _stream(stream))
+    _check(st, "gdn_decode")
     return O, S_out

@@ -295,4 +295,39 @@ gdn_status gdn_chunk_fwd(const void* Q, const void* K, const void* V, int32_t qk
   return launch_result(gdn::launch_chunk_fwd(p, s));
 }
 
+gdn_status gdn_decode(const void* Q, const void* K, const void* V, int32_t qkv_dtype,
+                      const float* beta, const float* g, const float* S_in, float* S_out,
+                      void* O, int32_t o_dtype, int32_t B, int32_t H, int32_t n,
+                      int32_t d_k, int32_t d_v, float scale, void* stream) {
+  if (B < 0 || H < 0 || n < 0 || d_k <= 0 || d_v <= 0) return GDN_ERR_BAD_SHAPE;
+  if (qkv_dtype != GDN_BF16 && qkv_dtype != GDN_F32) return GDN_ERR_BAD_DTYPE;
+  if (o_dtype != GDN_F32 && o_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
+  if (!(d_k == 64 || d_k == 128)) return GDN_ERR_UNSUPPORTED;
+  if (d_v % 32 != 0 || d_v > 256) return GDN_ERR_UNSUPPORTED;
+  if ((int64_t)B * H == 0) return GDN_OK;
+  if (!S_out) return GDN_ERR_NULL_POINTER;
+  if (n > 0 && (!Q || !K || !V || !beta || !g || !O)) return GDN_ERR_NULL_POINTER;
+  for (const void* p : {Q, K, V, (const void*)beta, (const void*)g, (const void*)S_in,
+                        (const void*)S_out, (const void*)O})
+    if (p && !aligned16(p)) return GDN_ERR_BAD_ALIGNMENT;
+  gdn::DecodeLaunch p;
+  p.Q = Q;
+  p.K = K;
+  p.V = V;
+  p.beta = beta;
+  p.g = g;
+  p.S_in = S_in;
+  p.S_out = S_out;
+  p.O = O;
+  p.B = B;
+  p.H = H;
+  p.n = n;
+  p.d_k = d_k;
+  p.d_v = d_v;
+  p.in_bf16 = qkv_dtype == GDN_BF16;
+  p.o_bf16 = o_dtype == GDN_BF16;
+  p.scale = scale;
+  return launch_result(gdn::launch_decode(p, as_stream(stream)));
+}
+
 }  // extern "C"

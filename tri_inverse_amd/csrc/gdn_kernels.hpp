@@ -71,4 +71,20 @@ struct ChunkLaunch {
 // chunk-wise forward, C = 64; d_k in {64, 128}; d_v a multiple of 32
 int launch_chunk_fwd(const ChunkLaunch& p, hipStream_t s);
 
+struct DecodeLaunch {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const float* beta;
+  const float* g;
+  const float* S_in;  // NULL = zeros; may equal S_out
+  float* S_out;
+  void* O;
+  int B, H, n, d_k, d_v;
+  int in_bf16, o_bf16;
+  float scale;
+};
+// gated delta rule token by token with the state resident on chip for all n tokens;
+// d_k in {64, 128}, d_v a multiple of 32 up to 256
+int launch_decode(const DecodeLaunch& p, hipStream_t s);
 }  // namespace gdn
