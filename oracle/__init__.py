@@ -59,12 +59,14 @@ def _load():
     lib.oracle_fs_inverse.argtypes = [i64, i32, P, P]
     lib.oracle_neumann.argtypes = [i64, i32, P, i32, i32, P]
     lib.oracle_doubling.argtypes = [i64, i32, P, P]
+    lib.oracle_neumann_int8.argtypes = [i64, i32, P, i32, i32, P]
     lib.oracle_residual.argtypes = [i64, i32, P, i32, i32, i32, P]
     lib.oracle_wy.argtypes = [i64, i32, i32, i32, P, P, P, P, P, i32, i32, P, P]
     lib.oracle_chunk_fwd.argtypes = [i32, i32, i64, i32, i32, i32, P, P, P, P, P, P, f64,
                                      i32, i32, i32, P, P]
     lib.oracle_recurrence.argtypes = [i32, i32, i64, i32, i32, P, P, P, P, P, P, f64, P, P]
-    for fn in ("oracle_build_A", "oracle_fs_inverse", "oracle_neumann", "oracle_doubling",
+    for fn in ("oracle_build_A", "oracle_fs_inverse", "oracle_neumann", "oracle_neumann_int8",
+               "oracle_doubling",
                "oracle_residual", "oracle_wy", "oracle_chunk_fwd", "oracle_recurrence",
                "oracle_set_threads"):
         getattr(lib, fn).restype = None
@@ -116,6 +118,16 @@ def neumann(A, N: int, mask: bool) -> np.ndarray:
     nb, C, _ = A.shape
     T = np.empty_like(A)
     _load().oracle_neumann(nb, C, _ptr(A), int(N), int(bool(mask)), _ptr(T))
+    return T
+
+
+def neumann_int8(A, N: int, mask: bool) -> np.ndarray:
+    """The Horner chain on int8 codes with per-block power-of-two scales ([GEO]
+    "Adaptation a la Quantification"; reading in gdn_oracle.c).  A holds fp32 values."""
+    A = _f64(A)
+    nb, C, _ = A.shape
+    T = np.empty_like(A)
+    _load().oracle_neumann_int8(nb, C, _ptr(A), int(N), int(bool(mask)), _ptr(T))
     return T
 
 

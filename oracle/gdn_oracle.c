@@ -166,6 +166,80 @@ void oracle_neumann(int64_t nb, int C, const double* A, int N, int mask, double*
   }
 }
 
+/* ---- NEXT-3: the power chain on INT8 operands -------------------------------
+ * [GEO] "Adaptation a la Quantification": the power chain of Methodologie SS1 runs on
+ * low-bit integer operands, and the mask of SS2 keeps the intermediates' range small
+ * enough for that.  The pages fix no scaling or rounding rule; the reading taken here:
+ *   - Horner on X = H - I, so that the identity never enters a product:
+ *       X_1 = A',  X_{k+1} = A' + A' X_k  (k = 1..N-1),  T = I + X_N
+ *     (the same sum I + A + ... + A^N as the Horner form of oracle_neumann);
+ *   - each operand of a product (A, and X_k) is quantised per block to int8 codes
+ *     q = x / 2^e rounded half to even, with one power-of-two scale 2^e per block and
+ *     operand: the smallest e with max|x| <= 127 2^e, so no code saturates;
+ *     A' = q(A) 2^eA is the dequantised A, used on both sides of the sum;
+ *   - the product of codes is exact (integer accumulation), and the sum
+ *     A' + (q(A) q(X_k)) 2^(eA + eX) is rounded once to fp32, the working precision of
+ *     the dequantised intermediates;
+ *   - with mask != 0, A and every X_k are band-masked (i - j <= N) before they are
+ *     quantised, so out-of-band magnitudes never set a scale.
+ * Every output value is an fp32 value, returned in fp64. */
+
+/* smallest integer e with amax <= 127 * 2^e (0 for an all-zero block), found by
+ * stepping e directly from that definition */
+static int int8_scale_exponent(double amax) {
+  if (!(amax > 0.0)) return 0;
+  int e = 0;
+  while (amax > 127.0 * ldexp(1.0, e)) ++e;
+  while (amax <= 127.0 * ldexp(1.0, e - 1)) --e;
+  return e;
+}
+
+/* codes q[i] = round_half_even(x[i] / 2^e) of one C x C operand; returns e */
+static int int8_quantise(int C, const double* X, long* q) {
+  double amax = 0.0;
+  for (size_t i = 0; i < (size_t)C * C; ++i)
+    if (fabs(X[i]) > amax) amax = fabs(X[i]);
+  const int e = int8_scale_exponent(amax);
+  for (size_t i = 0; i < (size_t)C * C; ++i) q[i] = (long)nearbyint(ldexp(X[i], -e));
+  return e;
+}
+
+void oracle_neumann_int8(int64_t nb, int C, const double* A, int N, int mask, double* T) {
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < nb; ++b) {
+    const size_t CC = (size_t)C * C;
+    double* Am = (double*)malloc(sizeof(double) * CC);
+    double* Ad = (double*)malloc(sizeof(double) * CC); /* A' */
+    double* X = (double*)malloc(sizeof(double) * CC);
+    long* qa = (long*)malloc(sizeof(long) * CC);
+    long* qx = (long*)malloc(sizeof(long) * CC);
+    memcpy(Am, A + (size_t)b * CC, sizeof(double) * CC);
+    if (mask) apply_band_mask(C, N, Am);
+    const int eA = int8_quantise(C, Am, qa);
+    for (size_t i = 0; i < CC; ++i) Ad[i] = ldexp((double)qa[i], eA);
+    memcpy(X, Ad, sizeof(double) * CC); /* X_1 = A' */
+    for (int k = 1; k < N; ++k) {
+      const int eX = int8_quantise(C, X, qx);
+      for (int i = 0; i < C; ++i)
+        for (int j = 0; j < C; ++j) {
+          long p = 0;
+          for (int m = 0; m < C; ++m) p += qa[(size_t)i * C + m] * qx[(size_t)m * C + j];
+          const double exact = Ad[(size_t)i * C + j] + ldexp((double)p, eA + eX);
+          X[(size_t)i * C + j] = (double)(float)exact;
+        }
+      if (mask) apply_band_mask(C, N, X);
+    }
+    double* Tb = T + (size_t)b * CC;
+    for (int i = 0; i < C; ++i)
+      for (int j = 0; j < C; ++j) Tb[(size_t)i * C + j] = X[(size_t)i * C + j] + (i == j ? 1.0 : 0.0);
+    free(Am);
+    free(Ad);
+    free(X);
+    free(qa);
+    free(qx);
+  }
+}
+
 /* ---- O5: exact multiplication-only doubling product --------------------------
  * T = prod_{i=0}^{m-1} (I + A^(2^i)),  m = ceil(log2 C).
  * Valid because A is nilpotent: by Lemma 3.1 of [GEO] (Methodologie SS1), A^n is

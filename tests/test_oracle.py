@@ -347,3 +347,91 @@ def test_threads_do_not_change_results():
     oracle.set_threads(4)
     T4 = oracle.neumann(A, 3, True)
     np.testing.assert_array_equal(T1, T4)
+
+
+# ---------------------------------------------------------------- INT8 power chain
+
+def _closed_form_truncated(C, rho, N, mask):
+    """I + sum_{n=1}^{N} (-rho)^n binom(i-j-1, n-1) for A = -rho L (L strictly lower ones)."""
+    i, j = np.indices((C, C))
+    m = i - j
+    T = np.eye(C)
+    for n in range(1, N + 1):
+        coef = np.vectorize(lambda mm: math.comb(mm - 1, n - 1) if mm >= 1 else 0)(m)
+        T = T + ((-rho) ** n) * coef
+    if mask:
+        T = np.where(m > N, 0.0, T)
+    return T
+
+
+@pytest.mark.parametrize("rho", [0.125, 0.25])
+@pytest.mark.parametrize("N", [1, 2, 3])
+@pytest.mark.parametrize("mask", [False, True])
+def test_int8_chain_exact_on_closed_form(rho, N, mask):
+    """A = -rho L with rho a power of two: every operand of the chain (A and the N <= 3
+    intermediates) is an exact multiple of its power-of-two scale with codes <= 127, and
+    every integer sum fits fp32, so the int8 chain must reproduce the closed-form
+    truncated sum exactly (a dropped term, a wrong sign, scale or index breaks this)."""
+    C = 64
+    A = (-rho * np.tril(np.ones((C, C)), -1))[None]
+    T = oracle.neumann_int8(A, N, mask)[0]
+    np.testing.assert_array_equal(T, _closed_form_truncated(C, rho, N, mask))
+
+
+@pytest.mark.parametrize("mask", [False, True])
+def test_int8_chain_exact_on_dyadic_inputs_N2(mask):
+    """A with entries code * 2^-9 (|code| <= 127, one code of 127): the codes of A and
+    of X_1 = A are exact, the product of codes is exact and the single fp32 rounding is
+    exact (sums below 2^24), so N = 2 equals the fp64 Horner sum I + A + A^2."""
+    rng = np.random.default_rng(11)
+    C, nb = 64, 6
+    codes = np.tril(rng.integers(-127, 128, size=(nb, C, C)), -1)
+    codes[:, 5, 1] = 127
+    A = codes * 2.0 ** -9
+    np.testing.assert_array_equal(oracle.neumann_int8(A, 2, mask), oracle.neumann(A, 2, mask))
+
+
+def test_int8_quantiser_properties():
+    """N = 1 returns I + A' with A' the dequantised A: A' is a multiple of one power of
+    two 2^e per block with codes in [-127, 127], |A' - A| <= 2^(e-1) (round to nearest),
+    and the scale is the finest one that does not saturate (127 * 2^(e-1) < max|A|)."""
+    A = _rand_A(12, 16, 64).astype(np.float32).astype(np.float64)
+    Ad = oracle.neumann_int8(A, 1, False) - np.eye(64)
+    for b in range(A.shape[0]):
+        amax = np.max(np.abs(A[b]))
+        e = math.frexp(amax / 127.0)[1]  # 2^(e-1) <= amax/127 < 2^e, or amax/127 = 2^(e-1)
+        if amax <= 127.0 * 2.0 ** (e - 1):
+            e -= 1
+        q = Ad[b] * 2.0 ** -e
+        np.testing.assert_array_equal(q, np.round(q))
+        assert np.max(np.abs(q)) <= 127
+        assert np.max(np.abs(Ad[b] - A[b])) <= 2.0 ** (e - 1)
+        assert 127.0 * 2.0 ** (e - 1) < amax <= 127.0 * 2.0 ** e
+
+
+def test_int8_mask_keeps_the_band_accurate():
+    """[GEO] Adaptation a la Quantification: without the mask, the large out-of-band
+    entries of the powers set coarse int8 scales and the entries that matter (the band)
+    lose their precision; with the mask they keep it.  Stress input A = -0.5 L with
+    N = 4, where the unmasked third power reaches 221 (an int8 step of 2)."""
+    C, N = 64, 4
+    A = (-0.5 * np.tril(np.ones((C, C)), -1))[None]
+    i, j = np.indices((C, C))
+    band = (i - j >= 0) & (i - j <= N)
+    ref = oracle.neumann(A, N, True)[0]
+    err_masked = np.max(np.abs(oracle.neumann_int8(A, N, True)[0] - ref)[band])
+    err_unmasked = np.max(np.abs(oracle.neumann_int8(A, N, False)[0] - ref)[band])
+    assert err_masked == 0.0
+    assert err_unmasked > 0.05
+
+
+def test_int8_chain_close_to_fp64_on_c1_inputs():
+    """On c1-like blocks the masked int8 chain stays within a few quantisation steps of
+    the fp64 masked sum (relative error of T - I below 2e-2)."""
+    A = _rand_A(13, 24, 64).astype(np.float32).astype(np.float64)
+    T8 = oracle.neumann_int8(A, 3, True)
+    Tf = oracle.neumann(A, 3, True)
+    I = np.eye(64)
+    assert _relF(T8 - I, Tf - I) < 2e-2
+    assert np.all(np.diagonal(T8, axis1=1, axis2=2) == 1.0)
+    assert np.all(np.triu(T8, 1) == 0.0)
