@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA
+INT8_PEAK_TOPS = 5000.0        # dense int8 MFMA
 N_SETS = 8
 
 
@@ -127,6 +128,9 @@ def bench_c1(torch, tri, synth, steps, warmup):
             if variant[0] == "exact":
                 tri.gdn_tri_inverse_exact(K=x["K"], beta=x["beta"], g=x["g"], C=C, compute="bf16",
                                           out=outs[i])
+            elif variant[0] == "int8":
+                tri.gdn_tri_inverse_neumann(K=x["K"], beta=x["beta"], g=x["g"], C=C, N=variant[1],
+                                            mask=variant[2], compute="int8", out=outs[i])
             elif variant[0] == "residual":
                 tri.gdn_tri_inverse_residual(K=x["K"], beta=x["beta"], g=x["g"], C=C, N=variant[1],
                                              mask=variant[2], S=variant[4], compute="f32", out=outs[i])
@@ -140,20 +144,28 @@ def bench_c1(torch, tri, synth, steps, warmup):
                 ("neumann", 4, True, torch.float32), ("neumann", 2, False, torch.float32),
                 ("neumann", 3, False, torch.float32), ("neumann", 4, False, torch.float32),
                 ("exact", 0, False, torch.float32), ("exact", 0, False, torch.bfloat16),
-                ("neumann", 3, True, torch.bfloat16), ("residual", 3, True, torch.float32, 8)]
+                ("neumann", 3, True, torch.bfloat16), ("residual", 3, True, torch.float32, 8),
+                ("int8", 3, True, torch.float32), ("int8", 3, False, torch.float32)]
     for v in variants:
         name = ("exact" if v[0] == "exact" else "N%d_%s" % (v[1], "masked" if v[2] else "unmasked"))
         if v[0] == "residual":
             name = "N%d_masked_residual_S%d_f32" % (v[1], v[4])
+        elif v[0] == "int8":
+            name = "N%d_%s_int8" % (v[1], "masked" if v[2] else "unmasked")
         name += "_T" + ("f32" if v[3] == torch.float32 else "bf16")
         st = steps if v == variants[0] else max(10, steps // 2)
         ms_step, ms_kernel = time_launches(torch, mk(v, v[3]), N_SETS, st, warmup)
         nb, by, fl = c1_bytes_flops(v, 4 if v[3] == torch.float32 else 2)
+        if v[0] == "int8":  # bf16 Gram, int8 products: MFMA time at each one's peak
+            gram = nb * 2 * C * C * C1["d_k"]
+            t_mfma = gram / (BF16_PEAK_TFLOPS * 1e12) + (fl - gram) / (INT8_PEAK_TOPS * 1e12)
+        else:
+            t_mfma = fl / (BF16_PEAK_TFLOPS * 1e12)
         results[name] = {
             "ms_per_step": ms_step, "ms_kernel": ms_kernel,
             "blocks_per_s": nb / (ms_step * 1e-3),
             "hbm_frac": by / (ms_kernel * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "mfma_frac": fl / (ms_kernel * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "mfma_frac": t_mfma / (ms_kernel * 1e-3),
             "bytes": by, "flops": fl,
         }
     return results

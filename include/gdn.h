@@ -60,7 +60,7 @@ typedef enum gdn_status {
 } gdn_status;
 
 /* element types (int32 codes in every signature) */
-typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1, GDN_FP8_E4M3 = 2 } gdn_dtype;
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1, GDN_FP8_E4M3 = 2, GDN_INT8 = 3 } gdn_dtype;
 
 /* inverse variants */
 typedef enum gdn_inv_mode {
@@ -75,6 +75,10 @@ typedef enum gdn_inv_mode {
  *   GDN_BF16 bf16 operands, fp32 accumulation (16x16x32 bf16 MFMA)
  *   GDN_FP8_E4M3 OCP e4m3 operands with one absmax/448 scale per block and tensor,
  *            fp32 accumulation (16x16x32 fp8 MFMA); Neumann mode only.
+ *   GDN_INT8 int8 codes with one power-of-two scale per block and operand (the
+ *            smallest 2^e with max|x| <= 127 2^e), int32 accumulation (16x16x64 i8
+ *            MFMA), Horner on X = H - I ([GEO] "Adaptation a la Quantification");
+ *            gdn_tri_inverse_neumann only, C <= 64.
  * N is ignored for GDN_INV_EXACT. */
 typedef struct gdn_inverse_cfg {
   int32_t mode;    /* gdn_inv_mode                  */
@@ -121,7 +125,10 @@ gdn_status gdn_build_A(const gdn_blocks* in, float* A_out, void* stream);
 
 /* T = M^(N) .* sum_{n=0}^{N} A^n (mask != 0) or the plain truncated sum (mask == 0),
  * evaluated as N-1 Horner products H <- I + A H ([GEO] Methodologie SS1-2).
- * compute: GDN_F32, GDN_BF16 or GDN_FP8_E4M3.  T_out [n_blocks][C][C], t_dtype GDN_F32
+ * compute: GDN_F32, GDN_BF16, GDN_FP8_E4M3 or GDN_INT8 (C <= 64).  With GDN_INT8 and a
+ * given fp32 A the result is exactly determined: every scaling is by a power of two,
+ * integer products are exact and each intermediate sum is rounded once to fp32.
+ * T_out [n_blocks][C][C], t_dtype GDN_F32
  * or GDN_BF16.  stats: device uint64_t[4] (see above) or NULL; when given it is
  * zeroed on `stream` and then accumulated (fp8 compute only; other computes write
  * zeros). */

@@ -170,3 +170,16 @@ def test_decode_validation():
     assert dec(S_out=None) == 1
     assert dec(Q=None) == 1
     assert dec(S_in=FAKE + 8) == 4
+
+
+def test_int8_compute_routing():
+    """int8 compute is accepted by the Neumann entry point at C <= 64 only."""
+    neu = lambda d, c: lib.gdn_tri_inverse_neumann(ctypes.byref(d), 3, 1, c, FAKE, tri.GDN_F32,
+                                                   None, None)
+    assert neu(blocks(n_blocks=0), tri.GDN_INT8) == 0
+    assert neu(blocks(n_blocks=0), 9) == 3
+    assert neu(blocks(C=128, n_blocks=0), tri.GDN_INT8) == 5
+    assert lib.gdn_tri_inverse_exact(ctypes.byref(blocks(n_blocks=0)), tri.GDN_INT8, FAKE,
+                                      tri.GDN_F32, None) == 5
+    assert lib.gdn_tri_inverse_residual(ctypes.byref(blocks(n_blocks=0)), 3, 1, 8, tri.GDN_INT8,
+                                        FAKE, tri.GDN_F32, None) == 5

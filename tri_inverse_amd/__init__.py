@@ -25,13 +25,13 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 # dtype and mode codes (gdn.h)
-GDN_F32, GDN_BF16, GDN_FP8_E4M3 = 0, 1, 2
+GDN_F32, GDN_BF16, GDN_FP8_E4M3, GDN_INT8 = 0, 1, 2, 3
 GDN_INV_NEUMANN, GDN_INV_EXACT = 0, 1
 GDN_OK = 0
 FP8_STATS_FIELDS = ("nonfinite", "sat_dynamic", "sat_static", "underflow")
 
 _COMPUTE = {"f32": GDN_F32, "fp32": GDN_F32, "bf16": GDN_BF16, "fp8": GDN_FP8_E4M3,
-            "e4m3": GDN_FP8_E4M3}
+            "e4m3": GDN_FP8_E4M3, "int8": GDN_INT8}
 _TORCH_DTYPE = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
 
 

@@ -83,10 +83,10 @@ __global__ __launch_bounds__(256) void inverse_kernel(BlocksArgs a, int N, int m
   constexpr int C = 16 * NT;
   const int64_t blk = (int64_t)blockIdx.x * (blockDim.x / WAVE) + (threadIdx.x / WAVE);
   if (blk >= a.n_blocks) return;
-  // fp8 masks A and every intermediate (the band sets the quantisation scales);
-  // bf16 / fp32 mask only the final sum (identical result, see neumann_T)
+  // fp8 and int8 mask A and every intermediate (the band sets the quantisation
+  // scales); bf16 / fp32 mask only the final sum (identical result, see neumann_T)
   const int band = (MODE == MODE_NEUMANN && mask) ? N : -1;
-  constexpr bool BANDED = (MODE == MODE_NEUMANN && CMP == CMP_FP8);
+  constexpr bool BANDED = (MODE == MODE_NEUMANN && (CMP == CMP_FP8 || CMP == CMP_INT8));
   Fp8Counts cnt{0, 0, 0, 0};
   const bool count = (CMP == CMP_FP8) && stats != nullptr;
   BlockIn<NT, SRC, DK> in;
@@ -97,6 +97,8 @@ __global__ __launch_bounds__(256) void inverse_kernel(BlocksArgs a, int N, int m
     doubling_T<NT, CMP>(AD, AT, TT);
   else if constexpr (MODE == MODE_RESIDUAL)
     residual_T<NT>(AD, AT, N, mask != 0, S, TT);
+  else if constexpr (CMP == CMP_INT8)
+    neumann_T_i8<NT, MAXD>(AD, AT, N, mask != 0, TT);
   else
     neumann_T<NT, CMP, MAXD>(AD, AT, N, mask != 0, TT, cnt, count);
   if (t_bf16)
@@ -248,6 +250,7 @@ int launch_neumann(const BlocksArgs& a, int src, int N, int mask, int cmp, void*
       case CMP_F32: return go(std::integral_constant<int, CMP_F32>{});
       case CMP_BF16: return go(std::integral_constant<int, CMP_BF16>{});
       case CMP_FP8: return go(std::integral_constant<int, CMP_FP8>{});
+      case CMP_INT8: return go(std::integral_constant<int, CMP_INT8>{});
       default: return -1;
     }
   });

@@ -21,7 +21,7 @@
 
 namespace gdn {
 
-enum : int { CMP_F32 = 0, CMP_BF16 = 1, CMP_FP8 = 2 };
+enum : int { CMP_F32 = 0, CMP_BF16 = 1, CMP_FP8 = 2, CMP_INT8 = 3 };
 enum : int { MODE_NEUMANN = 0, MODE_EXACT = 1, MODE_RESIDUAL = 2, MODE_FS = 3 };
 
 template <int NT>
@@ -545,6 +545,125 @@ __device__ __forceinline__ void fp8_roundtrip(Mat<NT>& M, float s) {
       M.t[I][J][2] = fp8_to_f32<2>(w) * s;
       M.t[I][J][3] = fp8_to_f32<3>(w) * s;
     }
+}
+
+// ---- int8 variant: per-block power-of-two scales, int32 accumulation ----------
+// [GEO] "Adaptation a la Quantification" runs the power chain on INT8 operands.  Codes
+// are round_half_even(x / 2^e) with one scale 2^e per block and operand, e the smallest
+// integer with max|x| <= 127 2^e.  Every scaling is by a power of two and so exact;
+// the products of codes are exact in int32 (|sum| <= 64 * 127^2 < 2^24).
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// amax = m 2^E with m in [0.5, 1): 127 2^(E-7) = (127/128) 2^E covers amax iff
+// m <= 127/128, else 127 2^(E-6) does; 127 2^(E-8) < 2^(E-1) <= amax never does.
+__device__ __forceinline__ int i8_exponent(float amax) {
+  if (!(amax > 0.f) || !__builtin_isfinite(amax)) return 0;
+  int E;
+  const float m = frexpf(amax, &E);
+  return (m <= 127.f / 128.f) ? E - 7 : E - 6;
+}
+
+// int8 codes of one tile's 4 registers, packed in register order (byte r = register r)
+__device__ __forceinline__ int q8x4(const f32x4& v, int neg_e) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int q = (int)__builtin_rintf(ldexpf(v[r], neg_e));
+    w |= ((uint32_t)q & 0xffu) << (8 * r);
+  }
+  return (int)w;
+}
+
+// x -> round(x / 2^e) 2^e on the lower tiles (the dequantised operand)
+template <int NT>
+__device__ __forceinline__ void i8_roundtrip(Mat<NT>& M, int e) {
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int J = 0; J <= I; ++J)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        M.t[I][J][r] = ldexpf(__builtin_rintf(ldexpf(M.t[I][J][r], -e)), e);
+}
+
+// One 16x16x64 int8 MFMA covers the whole contraction of a 64-wide block.  Slot map:
+// byte 4K + r of lane (g, c) <-> k = 16K + 4g + r, so the T-form tiles (I, 0..3) of A
+// give A's left fragment for row tile I and the D-form tiles (0..3, J) of X give X's
+// right fragment for column tile J (tiles beyond the block or above the diagonal are
+// zero codes).
+template <int NT>
+__device__ __forceinline__ i32x4 i8_rowfrag(const Mat<NT>& XT, int I, int neg_e) {
+  i32x4 f;
+#pragma unroll
+  for (int K = 0; K < 4; ++K) f[K] = q8x4(tile_or_zero(XT, I, K), neg_e);
+  return f;
+}
+template <int NT>
+__device__ __forceinline__ i32x4 i8_colfrag(const Mat<NT>& YD, int J, int neg_e) {
+  i32x4 f;
+#pragma unroll
+  for (int K = 0; K < 4; ++K) f[K] = q8x4(tile_or_zero(YD, K, J), neg_e);
+  return f;
+}
+
+__device__ __forceinline__ i32x4 mma_i8(const i32x4& a, const i32x4& b) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, i32x4{0, 0, 0, 0}, 0, 0, 0);
+}
+
+// Horner on X = H - I:  X_1 = A',  X_{k+1} = A' + A' X_k,  T = I + X_N, with A' the
+// dequantised A and every X_k quantised before its product; each sum is rounded once
+// to fp32.  AD, AT arrive band-masked when the mask is on (the band sets the scales),
+// and each X_k is masked before it is quantised.  C <= 64.
+template <int NT, int MAXD = NT - 1>
+__device__ __forceinline__ void neumann_T_i8(Mat<NT>& AD, Mat<NT>& AT, int N, bool mask, Mat<NT>& TT) {
+  static_assert(NT <= 4, "one 64-wide MFMA contraction per tile");
+  const int band = mask ? N : (1 << 30);
+  const int eA = i8_exponent(absmax(AT));
+  i8_roundtrip(AD, eA);
+  i8_roundtrip(AT, eA);
+  if (N <= 1) {
+    TT = AT;
+    add_eye(TT);
+    return;
+  }
+  i32x4 ra[NT];
+#pragma unroll
+  for (int I = 0; I < NT; ++I) ra[I] = i8_rowfrag(AT, I, -eA);
+  Mat<NT> X = AD;
+  for (int k = 1; k < N; ++k) {
+    const int eX = i8_exponent(absmax(X));
+    i32x4 cx[NT];
+#pragma unroll
+    for (int J = 0; J < NT; ++J) cx[J] = i8_colfrag(X, J, -eX);
+    const int es = eA + eX;
+    const bool last = (k == N - 1);
+#pragma unroll
+    for (int I = 0; I < NT; ++I)
+#pragma unroll
+      for (int J = 0; J <= I; ++J) {
+        if (I - J > MAXD) {
+          (last ? TT : X).t[I][J] = zero4();
+          continue;
+        }
+        if (last) {  // T-form: operands swapped
+          const i32x4 p = mma_i8(cx[J], ra[I]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) TT.t[I][J][r] = AT.t[I][J][r] + ldexpf((float)p[r], es);
+        } else {
+          const i32x4 p = mma_i8(ra[I], cx[J]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) X.t[I][J][r] = AD.t[I][J][r] + ldexpf((float)p[r], es);
+        }
+      }
+    if (mask) {
+      if (last)
+        mask_T(TT, band);
+      else
+        mask_D(X, band);
+    }
+  }
+  add_eye(TT);
 }
 
 // ---- the two inverse variants ------------------------------------------------
