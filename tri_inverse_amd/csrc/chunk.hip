@@ -19,17 +19,17 @@
 //
 // One workgroup per (batch, head, 32 columns of d_v) with eight waves; waves w and
 // w + 4 share a SIMD, so every SIMD interleaves two waves:
-//   waves 0, 1  state waves (SIMDs of their own): each owns 16 columns of S (fp32, in
-//               registers) and runs the sequential part of a chunk: K S, Y, U' = T Y and
-//               the state update.  They hand S^T (bf16) and U' (hi/lo) to the output
-//               waves.
-//   waves 3, 7  output waves (one SIMD), one chunk behind: P and
+//   waves 0, 1  state waves: each owns 16 columns of S (fp32, in registers) and runs
+//               the sequential part of a chunk: K S, Y, U' = T Y and the state update.
+//               They hand S^T (bf16) and U' (hi/lo) to the output waves.
+//   waves 4, 5  output waves, one chunk behind, each on a state wave's SIMD: P and
 //               O = scale (e^G Q S + P U') for row tiles {0, 3} and {1, 2} of the chunk
-//               (equal shares of the triangular P), all 32 columns.
+//               (equal shares of the triangular P), all 32 columns.  (Both output waves
+//               on one SIMD of their own measured 5 % slower.)
 //   wave 2      gates and T of the next chunk.
 //   wave 6      copies K rows, V columns, log-gates and beta of the chunk after next
 //               into a 4-deep LDS ring.
-//   waves 4, 5  only join the barriers.
+//   waves 3, 7  only join the barriers.
 // One barrier per chunk hands every buffer over (schedule above the kernel).  The K
 // rows sit in LDS row-major; the K^T operand of the state update comes from the same
 // rows through the LDS transpose read.  Q is read once per workgroup, each lane taking
@@ -100,21 +100,25 @@ struct alignas(16) ChunkBuf {
   bf16x8 ul[2][2][WAVE];            // per state wave: U' column packs, low
 };
 
-// row `row` as an operand fragment for k-pair p: slot t <-> k = 32p + 16(t/4) + 4g + t%4
-template <int DK>
-__device__ __forceinline__ bf16x8 rowpack_lds(const ChunkIn<DK>& R, int row, int p) {
-  const int g = lane_id() >> 4;
-  const __bf16* src = &R.k[row][32 * p + 4 * g];
-  return join8(*reinterpret_cast<const bf16x4*>(src), *reinterpret_cast<const bf16x4*>(src + 16));
-}
+// The state's d order.  Row 4g + r of the state's D-form tile a holds
+//   d = sdim(a, g, r) = 32 (a / 2) + 8 g + 4 (a % 2) + r,
+// so the two tiles 2p, 2p + 1 of one lane are, slot for slot, the natural-order
+// operand fragment (slot t <-> d = 32p + 8g + t) of the k-pair p: K S then reads K rows
+// with one 16-byte load per fragment, and S^T goes out with one 16-byte store.
+__device__ __forceinline__ int sdim(int a, int g, int r) { return 32 * (a >> 1) + 8 * g + 4 * (a & 1) + r; }
 
-// K^T operand fragment, row tile a (d = 16a + c), token pair p:
-// lane (g, c) slot t <-> K[32p + 16(t/4) + 4g + t%4][16a + c], by the transpose read
+// K^T operand fragment of state tile a (row c <-> d = sdim(a, c / 4, c % 4)), token
+// pair p: lane (g, c) slot t <-> K[32p + 16(t/4) + 4g + t%4][sdim(a, c/4, c%4)].  The
+// transpose read hands lane i element i % 4 of the 8-byte pieces addressed by lanes
+// 4k + i / 4 (k = 0..3); lane j addresses four consecutive d starting at
+// sdim(a, j % 4, 0), so lane i receives column sdim(a, i / 4, i % 4) of four
+// consecutive rows.
 template <int DK>
 __device__ __forceinline__ bf16x8 ktpack_lds(const ChunkIn<DK>& R, int a, int p) {
   const int l = lane_id(), g = l >> 4, j = l & 15;
-  const __bf16* p0 = &R.k[32 * p + 4 * g + (j >> 2)][16 * a + 4 * (j & 3)];
-  const __bf16* p1 = &R.k[32 * p + 16 + 4 * g + (j >> 2)][16 * a + 4 * (j & 3)];
+  const int d0 = sdim(a, j & 3, 0);
+  const __bf16* p0 = &R.k[32 * p + 4 * g + (j >> 2)][d0];
+  const __bf16* p1 = &R.k[32 * p + 16 + 4 * g + (j >> 2)][d0];
   return join8(lds_read_tr4(p0), lds_read_tr4(p1));
 }
 
@@ -161,7 +165,7 @@ __device__ __forceinline__ void produce_T(const ChunkArgs& a, const ChunkIn<DK>&
 #pragma unroll
   for (int I = 0; I < CNT; ++I)
 #pragma unroll
-    for (int p = 0; p < DK / 32; ++p) kb.kf[I][p] = rowpack_lds<DK>(R, 16 * I + c, p);
+    for (int p = 0; p < DK / 32; ++p) kb.kf[I][p] = rowfrag_nat<DK>(R, 16 * I + c, p);  // K K^T: any common d order
   kb.gl = gl;
   kb.bl = bl;
   Gates<CNT> gt;
@@ -201,20 +205,20 @@ template <int DK, int MAXD>
 struct StateWave {
   static constexpr int NP = DK / 32;
   static constexpr int NA = DK / 16;
-  f32x4 S[NA];  // D-form tiles: lane (g,c) reg r = S[16a + 4g + r][col0 + c]
+  f32x4 S[NA];  // D-form tiles: lane (g,c) reg r = S[sdim(a, g, r)][col0 + c]
 
   // one chunk: S^T out, K S, Y, U' = T Y (out), state update.  LDS operands are
   // requested in two batches, each ahead of the phase before the one that needs it, so
   // that the reads overlap MFMA and VALU work instead of sitting between them.
   __device__ __forceinline__ void step(const ChunkIn<DK>& R, const ChunkGates& GT, ChunkBuf<DK>& B, int v) {
     const int l = lane_id(), g = l >> 4, c = l & 15;
-    // batch 1: K row packs, V tiles in D-form (rows 16I + 4g + r, column 16v + c) by the
-    // transpose read, beta and e^G
+    // batch 1: K rows (natural d order, matching the state's d order), V tiles in
+    // D-form (rows 16I + 4g + r, column 16v + c) by the transpose read, beta and e^G
     bf16x8 kf[CNT][NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
-      for (int I = 0; I < CNT; ++I) kf[I][p] = rowpack_lds<DK>(R, 16 * I + c, p);
+      for (int I = 0; I < CNT; ++I) kf[I][p] = rowfrag_nat<DK>(R, 16 * I + c, p);
     bf16x4 vt[CNT];
 #pragma unroll
     for (int I = 0; I < CNT; ++I) vt[I] = lds_read_tr4(&R.v[16 * I + 4 * g + (c >> 2)][16 * v + 4 * (c & 3)]);
@@ -225,15 +229,13 @@ struct StateWave {
       e4[I] = *reinterpret_cast<const f32x4*>(&GT.eg[16 * I + 4 * g]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // S as bf16: column packs for K S here, S^T rows (4 consecutive d per lane and
-    // tile) for the output waves
+    // S as bf16: column packs for K S here (slot t <-> d = 32p + 8g + t), which are
+    // also S^T rows (8 consecutive d per lane) for the output waves
     bf16x8 cps[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      const bf16x4 s0 = pack4(S[2 * p]), s1 = pack4(S[2 * p + 1]);
-      cps[p] = join8(s0, s1);
-      *reinterpret_cast<bf16x4*>(&B.st[v][c][32 * p + 4 * g]) = s0;
-      *reinterpret_cast<bf16x4*>(&B.st[v][c][32 * p + 16 + 4 * g]) = s1;
+      cps[p] = pack8(S[2 * p], S[2 * p + 1]);
+      *reinterpret_cast<bf16x8*>(&B.st[v][c][32 * p + 8 * g]) = cps[p];
     }
     // K S (D-form), contraction over d_k, the four row tiles interleaved
     f32x4 ks[CNT];
@@ -302,7 +304,7 @@ struct StateWave {
   }
 };
 
-// ---- waves 3, 7: P and O = scale (e^G Q S + P U') for row tiles I0, I1 -----------------
+// ---- waves 4, 5: P and O = scale (e^G Q S + P U') for row tiles I0, I1 -----------------
 // q holds the chunk's Q rows of those tiles (natural d order).
 template <int DK, int I0, int I1, bool OBF16>
 __device__ __forceinline__ void emit_rows(const ChunkArgs& a, int64_t row0, int col0, const ChunkIn<DK>& R,
@@ -437,7 +439,7 @@ __device__ __forceinline__ void lds_barrier() {
 //   wave 2      it: T, gates of chunk it+1  reads in         writes buf.trp, gr
 //   waves 0, 1  it: state step of chunk it  reads in, gr, buf.trp
 //                                           writes buf.st, buf.uh/ul
-//   waves 3, 7  it: P, O of chunk it-1      reads in, gr, buf.{st, uh, ul}
+//   waves 4, 5  it: P, O of chunk it-1      reads in, gr, buf.{st, uh, ul}
 // Every slot is written in one iteration and read only in later ones, and its next
 // write comes after its last read: in[j] is written at j-2, read at j-1 .. j+1 and
 // rewritten at j+2; gr[j] is read at j and j+1 and rewritten at j+2; buf[j].trp is read
@@ -446,7 +448,7 @@ __device__ __forceinline__ void lds_barrier() {
 // wave 2 writes that buffer's trp, a field they do not touch.  Global loads are issued
 // one iteration before their data is needed (register ping-pong, no loop-carried
 // copies, no conditional loads), so their latency overlaps a whole iteration.
-constexpr int W_STATE0 = 0, W_STATE1 = 1, W_T = 2, W_OUT0 = 3, W_STAGE = 6, W_OUT1 = 7;
+constexpr int W_STATE0 = 0, W_STATE1 = 1, W_T = 2, W_OUT0 = 4, W_STAGE = 6, W_OUT1 = 5;
 
 template <int DK, int MODE, int CMP, int MAXD, bool OBF16>
 __global__ __launch_bounds__(NWAVES * WAVE, 1) void chunk_fwd_kernel(ChunkArgs a) {
@@ -591,7 +593,7 @@ __global__ __launch_bounds__(NWAVES * WAVE, 1) void chunk_fwd_kernel(ChunkArgs a
   for (int A = 0; A < DK / 16; ++A)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      sw.S[A][r] = a.S0 ? a.S0[((size_t)bh * DK + 16 * A + 4 * g + r) * a.dv + col0 + c] : 0.f;
+      sw.S[A][r] = a.S0 ? a.S0[((size_t)bh * DK + sdim(A, g, r)) * a.dv + col0 + c] : 0.f;
   lds_barrier();
   for (int it = -1; it <= nchunks; ++it) {
     if (it >= 0 && it < nchunks) sw.step(ring(in, it & 3), ring(gr, it % 3), ring(buf, it & 1), v);
@@ -601,7 +603,7 @@ __global__ __launch_bounds__(NWAVES * WAVE, 1) void chunk_fwd_kernel(ChunkArgs a
   for (int A = 0; A < DK / 16; ++A)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      a.S_out[((size_t)bh * DK + 16 * A + 4 * g + r) * a.dv + col0 + c] = sw.S[A][r];
+      a.S_out[((size_t)bh * DK + sdim(A, g, r)) * a.dv + col0 + c] = sw.S[A][r];
 }
 
 int launch_chunk_fwd(const ChunkLaunch& p, hipStream_t s) {
