@@ -31,7 +31,7 @@ def _ref(x, S0, scale):
 
 
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 256), (64, 96)])
-@pytest.mark.parametrize("n", [1, 5, 64])
+@pytest.mark.parametrize("n", [1, 3, 5, 64])
 def test_decode_parity(dk, dv, n):
     B, H = 2, 3
     say(f"decode dk={dk} dv={dv} n={n}")
