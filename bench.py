@@ -373,6 +373,27 @@ def profile_c3(torch, tri, synth, n):
     torch.cuda.synchronize()
 
 
+def profile_decode(torch, tri, synth, n):
+    """Decode step for 64 sequences (B=64 H=32 d=128, four rotating 128 MiB state sets)
+    n times, then the 256 MiB copy."""
+    B, H, dk, dv = 64, DEC["H"], DEC["d_k"], DEC["d_v"]
+    sets = []
+    for i in range(4):
+        x = {k: v.cuda() for k, v in synth.prefill(60 + i, B, H, 1, dk, dv).items()}
+        x["S"] = torch.zeros((B, H, dk, dv), device="cuda")
+        x["O"] = torch.empty((B, H, 1, dv), device="cuda", dtype=torch.bfloat16)
+        sets.append(x)
+    for i in range(n):
+        x = sets[i % 4]
+        tri.gdn_decode(x["Q"], x["K"], x["V"], x["beta"], x["g"], S=x["S"], S_out=x["S"], O=x["O"])
+    torch.cuda.synchronize()
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(n):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 def cpu_baseline_c1():
     import oracle
     import synth
@@ -420,6 +441,8 @@ def main():
     if args.profile_launches:
         if args.only == "c3":
             profile_c3(torch, tri, synth, args.profile_launches)
+        elif args.only == "decode":
+            profile_decode(torch, tri, synth, args.profile_launches)
         else:
             profile_c1(torch, tri, synth, args.profile_launches)
         return
@@ -474,7 +497,7 @@ def main():
             "tokens_per_s": hd["tokens_per_s"], "ms_per_step": hd["ms_per_step"],
             "roofline": {"bound": "hbm", "achieved": hd["bytes"] / (hd["ms_per_step"] * 1e-3) / 1e9,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": hd["hbm_frac"],
-                         "traffic": None},
+                         "traffic": load_traffic("decode_kernel<128,true,true>")},
             "variants": dec}
     if args.only in ("all", "c2"):
         out["wy"] = bench_wy(torch, tri, synth, max(5, args.steps // 5), 2)
