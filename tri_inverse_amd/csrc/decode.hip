@@ -15,9 +15,10 @@
 // one head, so they share the head's k and q lines in L1.  Lane l = 8 rg + cg holds
 // columns 4cg..4cg+3 of the wave's slice for rows RPL rg .. RPL rg + RPL - 1 of d_k
 // (RPL = d_k / 8), RPL x 4 fp32 values.  Every load of S moves 8 rows x 128 B with
-// 16-byte accesses; k and q are read as the lane's RPL contiguous elements (the 8
-// lanes of a row group read the same bytes).  The retrieval sums reduce over the
-// 8 row groups with a butterfly across lanes.
+// 16-byte accesses; S is read and written with non-temporal accesses (streamed once
+// per call).  k and q are read as the lane's RPL contiguous elements (the 8 lanes of
+// a row group read the same bytes).  The retrieval sums reduce over the 8 row groups
+// with a butterfly across lanes.
 #include "gdn_device.hpp"
 #include "gdn_kernels.hpp"
 
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
   if (a.S_in) {
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(a.S_in + sbase + (size_t)i * dv);
+      const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.S_in + sbase + (size_t)i * dv));
 #pragma unroll
       for (int c = 0; c < 4; ++c) s[i][c] = v[c];
     }
@@ -207,8 +208,8 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
 
 #pragma unroll
   for (int i = 0; i < RPL; ++i)
-    *reinterpret_cast<f32x4*>(a.S_out + sbase + (size_t)i * dv) =
-        f32x4{s[i][0], s[i][1], s[i][2], s[i][3]};
+    __builtin_nontemporal_store(f32x4{s[i][0], s[i][1], s[i][2], s[i][3]},
+                                reinterpret_cast<f32x4*>(a.S_out + sbase + (size_t)i * dv));
 }
 
 int launch_decode(const DecodeLaunch& p, hipStream_t s) {

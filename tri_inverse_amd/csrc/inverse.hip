@@ -22,7 +22,7 @@ struct BlockIn<NT, SRC_K_BF16, DK> {
   KBlock<NT, DK> k;
   __device__ __forceinline__ void load(const BlocksArgs& a, int64_t blk) {
     constexpr int C = 16 * NT;
-    load_kblock<NT, DK>(reinterpret_cast<const __bf16*>(a.K) + (size_t)blk * C * DK,
+    load_kblock<NT, DK, true>(reinterpret_cast<const __bf16*>(a.K) + (size_t)blk * C * DK,
                         a.beta + (size_t)blk * C, a.g + (size_t)blk * C, k);
   }
   template <int MAXD, bool BANDED>

@@ -104,7 +104,8 @@ __device__ __forceinline__ void gram_bf16(const __bf16* __restrict__ K, Mat<NT>&
   for (int I = 0; I < NT; ++I)
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-      kf[I][s] = *reinterpret_cast<const bf16x8*>(K + (size_t)(16 * I + c) * DK + 32 * s + 8 * g);
+      kf[I][s] = __builtin_nontemporal_load(
+          reinterpret_cast<const bf16x8*>(K + (size_t)(16 * I + c) * DK + 32 * s + 8 * g));
 #pragma unroll
   for (int I = 0; I < NT; ++I)
 #pragma unroll
@@ -131,7 +132,8 @@ __device__ __forceinline__ void gram_f32(const float* __restrict__ K, Mat<NT>& S
     f32x4 kf[NT];
 #pragma unroll
     for (int I = 0; I < NT; ++I)
-      kf[I] = *reinterpret_cast<const f32x4*>(K + (size_t)(16 * I + c) * DK + 16 * s + 4 * g);
+      kf[I] = __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4*>(K + (size_t)(16 * I + c) * DK + 16 * s + 4 * g));
 #pragma unroll
     for (int I = 0; I < NT; ++I)
 #pragma unroll
@@ -152,7 +154,7 @@ struct KBlock {
   float gl, bl;
 };
 
-template <int NT, int DK>
+template <int NT, int DK, bool NT_LOAD = false>
 __device__ __forceinline__ void load_kblock(const __bf16* __restrict__ K,
                                             const float* __restrict__ beta,
                                             const float* __restrict__ g, KBlock<NT, DK>& kb) {
@@ -162,7 +164,11 @@ __device__ __forceinline__ void load_kblock(const __bf16* __restrict__ K,
   for (int I = 0; I < NT; ++I)
 #pragma unroll
     for (int s = 0; s < DK / 32; ++s)
-      kb.kf[I][s] = *reinterpret_cast<const bf16x8*>(K + (size_t)(16 * I + c) * DK + 32 * s + 8 * grp);
+      {
+        const bf16x8* src = reinterpret_cast<const bf16x8*>(K + (size_t)(16 * I + c) * DK + 32 * s + 8 * grp);
+        // streaming (non-temporal) when nothing reads these rows again
+        kb.kf[I][s] = NT_LOAD ? __builtin_nontemporal_load(src) : *src;
+      }
   kb.gl = (l < C) ? g[l] : 0.f;
   kb.bl = (l < C) ? beta[l] : 0.f;
 }
@@ -800,6 +806,8 @@ __device__ __forceinline__ void doubling_T(const Mat<NT>& AD, const Mat<NT>& AT,
 // ---- stores ------------------------------------------------------------------
 // T-form tile (I,J): lane (g,c) holds row 16I + c, columns 16J + 4g .. +3.
 
+// T is written once per launch (and K read once): both use non-temporal accesses, the
+// streaming cache policy, so they do not displace other lines on their way to HBM.
 template <int NT, int MAXD = NT - 1>
 __device__ __forceinline__ void store_T_f32(float* __restrict__ out, const Mat<NT>& M) {
   constexpr int C = 16 * NT;
@@ -809,7 +817,7 @@ __device__ __forceinline__ void store_T_f32(float* __restrict__ out, const Mat<N
 #pragma unroll
     for (int J = 0; J < NT; ++J) {
       f32x4 v = (J <= I && I - J <= MAXD) ? M.t[I][J] : zero4();
-      *reinterpret_cast<f32x4*>(out + (size_t)(16 * I + c) * C + 16 * J + 4 * g) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(out + (size_t)(16 * I + c) * C + 16 * J + 4 * g));
     }
 }
 
@@ -822,7 +830,7 @@ __device__ __forceinline__ void store_T_bf16(__bf16* __restrict__ out, const Mat
 #pragma unroll
     for (int J = 0; J < NT; ++J) {
       f32x4 v = (J <= I && I - J <= MAXD) ? M.t[I][J] : zero4();
-      *reinterpret_cast<bf16x4*>(out + (size_t)(16 * I + c) * C + 16 * J + 4 * g) = pack4(v);
+      __builtin_nontemporal_store(pack4(v), reinterpret_cast<bf16x4*>(out + (size_t)(16 * I + c) * C + 16 * J + 4 * g));
     }
 }
 
