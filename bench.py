@@ -173,11 +173,12 @@ def bench_c1(torch, tri, synth, steps, warmup):
 
 def bench_fs_speedup(torch, tri, synth, steps, warmup):
     """The pages' headline metric: speedup of the multiplication-only inverses over
-    forward substitution, here both on MI355X.  B=1, H=16, seq 8192 at C = 32 and 64
-    (4096 / 2048 blocks), A built in-kernel from bf16 keys, T fp32; forward substitution
-    in fp32 (the sequential baseline), the masked N=3 sum and exact doubling in bf16."""
+    forward substitution, here both on MI355X.  B=1, H=16, seq 8192 at C = 32, 64 and
+    128 (4096 / 2048 / 1024 blocks), A built in-kernel from bf16 keys, T fp32; forward
+    substitution in fp32 (the sequential baseline), the masked N=3 sum and exact
+    doubling in bf16."""
     res = {}
-    for C in (32, 64):
+    for C in (32, 64, 128):
         nb = C1["B"] * C1["H"] * C1["T"] // C
         sets = [{k: v.cuda() for k, v in synth.blocks(1 if s == 0 else 1000 + s, nb, C, C1["d_k"],
                                                        k_dtype="bf16").items()} for s in range(N_SETS)]

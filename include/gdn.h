@@ -153,7 +153,8 @@ gdn_status gdn_tri_inverse_residual(const gdn_blocks* in, int32_t N, int32_t mas
 
 /* T = (I - A)^-1 by forward substitution, T = I + A T row by row ([GEO] problem
  * statement: the sequential baseline the multiplication-only inverses replace), in
- * fp32 with C (C-1)/2 dependent-row multiply-adds per block.  C in {16, 32, 64}.
+ * fp32 with C (C-1)/2 dependent-row multiply-adds per block.  C in {16, 32, 64}, and
+ * C = 128 with A given or bf16 keys (d_k 64 or 128); other C: GDN_ERR_UNSUPPORTED.
  * T_out [n_blocks][C][C], t_dtype GDN_F32 or GDN_BF16. */
 gdn_status gdn_tri_inverse_fs(const gdn_blocks* in, void* T_out, int32_t t_dtype, void* stream);
 

@@ -149,7 +149,9 @@ def test_fs_validation():
     assert fs(None) == 1
     assert fs(blocks(), T=None) == 1
     assert fs(blocks(), t=tri.GDN_FP8_E4M3) == 3
-    assert fs(blocks(C=128, n_blocks=0)) == 5
+    assert fs(blocks(C=128, n_blocks=0)) == 0
+    assert fs(blocks(C=256, n_blocks=0)) == 5
+    assert fs(blocks(C=128, d_k=256, n_blocks=0)) == 5
     assert fs(blocks(n_blocks=0)) == 0
     assert fs(blocks(), T=FAKE + 4) == 4
 

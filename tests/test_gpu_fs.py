@@ -14,9 +14,9 @@ pytestmark = pytest.mark.gpu
 tri = pytest.importorskip("tri_inverse_amd")
 
 
-@pytest.mark.parametrize("C", [16, 32, 64])
+@pytest.mark.parametrize("C", [16, 32, 64, 128])
 def test_fs_parity_from_keys(C):
-    nb = 45
+    nb = 45 if C <= 64 else 11
     say(f"fs from keys C={C}")
     inp = synth.blocks(51, nb, C, 128, k_dtype="bf16")
     T = f64(tri.gdn_tri_inverse_fs(K=cuda(inp["K"]), beta=cuda(inp["beta"]), g=cuda(inp["g"]), C=C))
@@ -42,3 +42,21 @@ def test_fs_from_given_A_matches_exact_products():
     Tr = oracle.fs_inverse(A32.astype(np.float64))
     assert relF(T, Tr) <= 1e-5
     assert relF(T, Tx) <= 2e-5
+
+
+@pytest.mark.parametrize("t_dtype", [torch.float32, torch.bfloat16])
+def test_fs128_from_given_A(t_dtype):
+    """C = 128 with A given in fp32 (the oracle's A rounded to fp32); bf16 output is the
+    rounded fp32 result."""
+    C, nb = 128, 7
+    say(f"fs128 from A t_dtype={t_dtype}")
+    inp = synth.blocks(3, nb, C, 128, k_dtype="f64")
+    A32 = oracle.build_A(inp["K"], inp["beta"], inp["g"]).astype(np.float32)
+    T = tri.gdn_tri_inverse_fs(A=cuda(torch.from_numpy(A32)), C=C, t_dtype=t_dtype)
+    torch.cuda.synchronize()
+    Tr = oracle.fs_inverse(A32.astype(np.float64))
+    tol = 1e-5 if t_dtype == torch.float32 else 4e-3
+    assert relF(f64(T), Tr) <= tol, relF(f64(T), Tr)
+    i, j = np.indices((C, C))
+    Tn = f64(T)
+    assert np.all(Tn[:, j > i] == 0) and np.all(Tn[:, i == j] == 1)

@@ -185,10 +185,15 @@ gdn_status gdn_tri_inverse_fs(const gdn_blocks* in, void* T_out, int32_t t_dtype
   gdn_status st = check_blocks(in, true, false, &src);
   if (st != GDN_OK) return st;
   if (t_dtype != GDN_F32 && t_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
-  if (!chunk_small(in->C)) return GDN_ERR_UNSUPPORTED;
+  const bool c128 = in->C == 128;
+  if (!chunk_small(in->C) && !c128) return GDN_ERR_UNSUPPORTED;
+  if (c128 && src == 2) return GDN_ERR_UNSUPPORTED;  // fp32 keys: C <= 64 only
+  if (c128 && src == 1 && !(in->d_k == 64 || in->d_k == 128)) return GDN_ERR_UNSUPPORTED;
   if (in->n_blocks == 0) return GDN_OK;
   if (!T_out) return GDN_ERR_NULL_POINTER;
   if (!aligned16(T_out)) return GDN_ERR_BAD_ALIGNMENT;
+  if (c128)
+    return launch_result(gdn::launch_fs128(to_args(in), src, T_out, t_dtype == GDN_BF16, as_stream(stream)));
   return launch_result(gdn::launch_fs(to_args(in), src, T_out, t_dtype == GDN_BF16, as_stream(stream)));
 }
 

@@ -32,6 +32,8 @@ int launch_residual(const BlocksArgs& a, int src, int N, int mask, int S, void* 
                     hipStream_t s);
 // forward substitution (fp32), the sequential baseline, C <= 64
 int launch_fs(const BlocksArgs& a, int src, void* T_out, int t_bf16, hipStream_t s);
+// forward substitution at C = 128 (A given in fp32, or built from bf16 keys, d_k 64 or 128)
+int launch_fs128(const BlocksArgs& a, int src, void* T_out, int t_bf16, hipStream_t s);
 
 // WY products; T given (t_bf16 selects its dtype) or formed with (mode, N, mask);
 // C in {32, 64}, d_k and d_v in {64, 128}
