@@ -195,3 +195,23 @@ def test_chunk_fwd_full_size_sampled_heads():
                                   N=3, mask=True)
         assert relF(O[b:b + 1, h:h + 1], Or) <= TOL["bf16"], relF(O[b:b + 1, h:h + 1], Or)
         assert relF(S[b:b + 1, h:h + 1], Sr) <= TOL["bf16"], relF(S[b:b + 1, h:h + 1], Sr)
+
+
+def test_chunk_fwd_fp8_full_size_sampled_heads():
+    """B=4, H=16, seq 32768 with the fp8 inverse (the launch the fp8 measurement times),
+    masked and unmasked: one head against the oracle, and no non-finite value or
+    dynamic-scale saturation anywhere."""
+    B, H, T, dk, dv = 4, 16, 32768, 128, 128
+    say("chunk fwd fp8 full size")
+    x = synth.prefill(3, B, H, T, dk, dv)
+    stats = torch.zeros(4, dtype=torch.int64, device="cuda")
+    sel = {k: f64(v[1:2, 7:8]) for k, v in x.items()}
+    for mask in (True, False):
+        O, S = _run_chunk(x, C=64, scale=dk ** -0.5, N=3, mask=mask, compute="fp8", stats=stats,
+                          o_dtype=torch.bfloat16)
+        s = stats.cpu().tolist()
+        assert s[0] == 0 and s[1] == 0
+        Or, Sr = oracle.chunk_fwd(sel["Q"], sel["K"], sel["V"], sel["beta"], sel["g"], 64, dk ** -0.5,
+                                  N=3, mask=mask)
+        assert relF(O[1:2, 7:8], Or) <= TOL["fp8"], relF(O[1:2, 7:8], Or)
+        assert relF(S[1:2, 7:8], Sr) <= TOL["fp8"], relF(S[1:2, 7:8], Sr)

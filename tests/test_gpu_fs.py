@@ -60,3 +60,17 @@ def test_fs128_from_given_A(t_dtype):
     i, j = np.indices((C, C))
     Tn = f64(T)
     assert np.all(Tn[:, j > i] == 0) and np.all(Tn[:, i == j] == 1)
+
+
+@pytest.mark.parametrize("C", [32, 64, 128])
+def test_fs_full_size_sampled_blocks(C):
+    """B=1, H=16, seq 8192 (4096 / 2048 / 1024 blocks): the launches the speedup
+    measurement times; 32 sampled blocks against the oracle."""
+    nb = 16 * 8192 // C
+    say(f"fs full size C={C}")
+    inp = synth.blocks(1, nb, C, 128, k_dtype="bf16")
+    T = f64(tri.gdn_tri_inverse_fs(K=cuda(inp["K"]), beta=cuda(inp["beta"]), g=cuda(inp["g"]), C=C))
+    torch.cuda.synchronize()
+    idx = np.random.default_rng(3).choice(nb, 32, replace=False)
+    Tr = oracle.fs_inverse(oracle.build_A(f64(inp["K"][idx]), f64(inp["beta"][idx]), f64(inp["g"][idx])))
+    assert relF(T[idx], Tr) <= 1e-5, relF(T[idx], Tr)

@@ -123,8 +123,14 @@ def test_full_size_batched_inverse_all_blocks():
     K, beta, g = cuda(inp["K"]), cuda(inp["beta"]), cuda(inp["g"])
     A64 = oracle.build_A(f64(inp["K"]), f64(inp["beta"]), f64(inp["g"]))
     for mode, N, mask, t_dtype in [("neumann", 3, True, torch.float32),
+                                   ("neumann", 2, True, torch.float32),
+                                   ("neumann", 4, True, torch.float32),
+                                   ("neumann", 2, False, torch.float32),
+                                   ("neumann", 3, False, torch.float32),
+                                   ("neumann", 4, False, torch.float32),
                                    ("neumann", 3, True, torch.bfloat16),
-                                   ("exact", 0, False, torch.float32)]:
+                                   ("exact", 0, False, torch.float32),
+                                   ("exact", 0, False, torch.bfloat16)]:
         say(f"full-size inverse {mode} N={N} mask={mask} {t_dtype}")
         if mode == "exact":
             T = tri.gdn_tri_inverse_exact(K=K, beta=beta, g=g, C=64, t_dtype=t_dtype)

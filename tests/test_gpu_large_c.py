@@ -112,6 +112,28 @@ def test_band_wy_full_size_sampled_blocks():
     assert relF(f64(U[idx]), Ur) <= TOL
 
 
+@pytest.mark.parametrize("variant", [("neumann", 3, True), ("neumann", 3, False), ("exact", 0, False)])
+def test_wy_full_size_C128_sampled_blocks(variant):
+    """B=2, H=16, seq 16384 at C = 128 (4096 blocks, bf16 outputs), the launches of the
+    chunk-size sweep: band kernel for the masked sum, full-triangle kernel otherwise;
+    24 sampled blocks against the oracle."""
+    mode, N, mask = variant
+    C = 128
+    nb = 2 * 16 * 16384 // C
+    say(f"wy full size C=128 {variant}")
+    inp = synth.blocks(4, nb, C, 128, k_dtype="bf16", d_v=128)
+    W, U = tri.gdn_wy(cuda(inp["K"]), cuda(inp["beta"]), cuda(inp["g"]), cuda(inp["V"]), C=C,
+                      mode=mode, N=max(N, 1), mask=mask, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    idx = np.random.default_rng(5).choice(nb, 24, replace=False)
+    sub = {k: v[idx] for k, v in inp.items()}
+    A64 = oracle.build_A(f64(sub["K"]), f64(sub["beta"]), f64(sub["g"]))
+    T64 = oracle.doubling(A64) if mode == "exact" else oracle.neumann(A64, N, mask)
+    Wr, Ur = oracle.wy(T64, f64(sub["K"]), f64(sub["V"]), f64(sub["beta"]), f64(sub["g"]), False)
+    assert relF(f64(W[idx]), Wr) <= TOL, relF(f64(W[idx]), Wr)
+    assert relF(f64(U[idx]), Ur) <= TOL, relF(f64(U[idx]), Ur)
+
+
 # ------------------------------------------------------------------ full lower triangle
 
 @pytest.mark.parametrize("C", [128, 256])

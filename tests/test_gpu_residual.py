@@ -62,3 +62,19 @@ def test_residual_from_given_A_bf16_out():
     torch.cuda.synchronize()
     Tr = oracle.residual(A32.astype(np.float64), 3, True, 8)
     assert relF(f64(T), Tr) <= 2e-3   # the bf16 rounding of T itself
+
+
+def test_residual_full_size_sampled_blocks():
+    """2048 blocks of 64 from bf16 keys, N = 3 masked, S = 8, T fp32: the launch the
+    benchmark times; 64 sampled blocks against the oracle."""
+    nb, C = 2048, 64
+    say("residual full size")
+    inp = synth.blocks(1, nb, C, 128, k_dtype="bf16")
+    T = tri.gdn_tri_inverse_residual(K=cuda(inp["K"]), beta=cuda(inp["beta"]), g=cuda(inp["g"]), C=C,
+                                     N=3, mask=True, S=8, compute="f32")
+    torch.cuda.synchronize()
+    idx = np.random.default_rng(2).choice(nb, 64, replace=False)
+    A = oracle.build_A(f64(inp["K"][idx]), f64(inp["beta"][idx]), f64(inp["g"][idx]))
+    Tr = oracle.residual(A, 3, True, 8)
+    Tg = f64(T)[idx]
+    assert relF(Tg, Tr) <= TOL32, relF(Tg, Tr)
