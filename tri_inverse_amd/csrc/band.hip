@@ -59,22 +59,30 @@ __device__ __forceinline__ bf16x8 window_colpack(const __bf16 (&X)[ROWS][D + BAN
 }
 
 // Z (T-form row tile) = R X over the window, R as a hi/lo pair of row packs; stored
-// row-major: row `row` of out, columns 16e + 4g .. +3
+// row-major at row `row` of out: fp32 as columns 16e + 4g .. +3, bf16 two column tiles
+// at a time with 16 contiguous bytes per lane (store_pair_bf16)
 template <int D, int ROWS>
 __device__ __forceinline__ void window_apply(const bf16x8& rh, const bf16x8& rl,
                                              const __bf16 (&X)[ROWS][D + BAND_PAD], int r0,
                                              void* __restrict__ out, int64_t row, bool obf16) {
+  static_assert(D % 32 == 0, "column tiles are stored in pairs");
   const int g = lane_id() >> 4;
 #pragma unroll
-  for (int e = 0; e < D / 16; ++e) {
-    const bf16x8 cp = window_colpack<D, ROWS>(X, r0, e);
-    f32x4 acc = mma_bf16(cp, rh, zero4());
-    acc = mma_bf16(cp, rl, acc);
-    const int64_t o = row * D + 16 * e + 4 * g;
-    if (obf16)
-      *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(out) + o) = pack4(acc);
-    else
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + o) = acc;
+  for (int e2 = 0; e2 < D / 32; ++e2) {
+    f32x4 acc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bf16x8 cp = window_colpack<D, ROWS>(X, r0, 2 * e2 + h);
+      acc[h] = mma_bf16(cp, rh, zero4());
+      acc[h] = mma_bf16(cp, rl, acc[h]);
+    }
+    if (obf16) {
+      store_pair_bf16(reinterpret_cast<__bf16*>(out) + row * D, 2 * e2, acc[0], acc[1]);
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + row * D + 16 * (2 * e2 + h) + 4 * g) = acc[h];
+    }
   }
 }
 

@@ -362,13 +362,16 @@ __global__ __launch_bounds__(NT * WAVE / 2, 1) void dense_kernel(DenseArgs p) {
           }
         }
       });
+      // bf16: two column tiles at a time, 16 contiguous bytes per lane (store_pair_bf16)
+      const int64_t ro = (b * C + 16 * I + c) * D;
+      if (p.out_bf16) {
 #pragma unroll
-      for (int e = 0; e < D / 16; ++e) {
-        const int64_t o = (b * C + 16 * I + c) * D + 16 * e + 4 * g;
-        if (p.out_bf16)
-          *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(out) + o) = pack4(acc[e]);
-        else
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + o) = acc[e];
+        for (int e2 = 0; e2 < D / 32; ++e2)
+          store_pair_bf16(reinterpret_cast<__bf16*>(out) + ro, 2 * e2, acc[2 * e2], acc[2 * e2 + 1]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < D / 16; ++e)
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + ro + 16 * e + 4 * g) = acc[e];
       }
     };
     using NJa = std::integral_constant<int, NT / 2>;

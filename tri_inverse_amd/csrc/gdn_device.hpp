@@ -122,6 +122,32 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// ---- 16-byte bf16 stores of MFMA output tiles -------------------------------------
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Two adjacent 16-column output tiles e, e + 1 of one row tile, bf16, stored with 16
+// contiguous bytes per lane.  Lane group g holds columns 4g .. 4g+3 of each tile;
+// v_permlane16_swap of (tile e, tile e+1) exchanges the odd groups' tile-e values with
+// the even groups' tile-(e+1) values, after which group g holds the 8 consecutive
+// columns 16 (e + g % 2) + 8 (g / 2) .. +7 of the pair.
+__device__ __forceinline__ void store_pair_bf16(__bf16* __restrict__ row, int e, const f32x4& a0,
+                                                const f32x4& a1) {
+  const int g = lane_id() >> 4;
+  const bf16x4 h0 = pack4(a0), h1 = pack4(a1);
+  const u32x2 w0 = __builtin_bit_cast(u32x2, h0), w1 = __builtin_bit_cast(u32x2, h1);
+  u32x4 out;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const unsigned x0 = w0[k], x1 = w1[k];  // vector elements to scalars before any bit cast
+    const auto sw = __builtin_amdgcn_permlane16_swap(x0, x1, false, false);
+    const unsigned y0 = sw[0], y1 = sw[1];
+    out[k] = y0;
+    out[2 + k] = y1;
+  }
+  *reinterpret_cast<u32x4*>(row + 16 * (e + (g & 1)) + 8 * (g >> 1)) = out;
+}
+
 // ---- wave-wide reductions and scans (wave64) ------------------------------------
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -10,68 +10,83 @@
 // registers exactly as in the inverse kernels.  The diagonal is folded into T's
 // columns in fp32, and T diag(s) enters the MFMAs as a bf16 hi/lo pair, so the
 // products (T diag(s)) K carry about 16 bits and the bf16 rounding of the outputs
-// dominates their error.  The contraction
-// runs over the chunk's tokens, so each wave stages K (then V) transposed in its own
-// LDS slice and reads the column fragments from there.
+// dominates their error.  The contraction runs over the chunk's tokens, so each wave
+// copies K (then V) row-major into its own LDS slice with 16-byte stores and reads the
+// column fragments back with the gfx950 transpose read.
 #include "gdn_kernels.hpp"
 #include "tri_block.hpp"
 
 namespace gdn {
 
 constexpr int WY_WAVES = 4;
-constexpr int XT_PAD = 8;
+constexpr int XR_PAD = 8;
 
 template <int NT, int D>
-struct WyLds {
-  __bf16 xt[D][16 * NT + XT_PAD];  // X^T for the block's [C][D] rows X
+struct alignas(16) WyLds {
+  __bf16 xr[16 * NT][D + XR_PAD];  // the block's [C][D] rows X, row-major (padded rows)
 };
 
-// stage rows X[C][D] (bf16, global) transposed into xt[d][token]
+// stage rows X[C][D] (bf16, global) into LDS row-major: consecutive lanes take
+// consecutive 16-byte pieces, so every load instruction covers whole rows
 template <int NT, int D>
-__device__ __forceinline__ void stage_transposed(const __bf16* __restrict__ X, WyLds<NT, D>& L) {
-  const int l = lane_id(), g = l >> 4, c = l & 15;
+__device__ __forceinline__ void stage_rows(const __bf16* __restrict__ X, WyLds<NT, D>& L) {
+  constexpr int SEG = D / 8, N = 16 * NT * SEG / WAVE;
+  const int l = lane_id();
 #pragma unroll
-  for (int I = 0; I < NT; ++I)
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(X + (size_t)(16 * I + c) * D + 32 * s + 8 * g);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) L.xt[32 * s + 8 * g + t][16 * I + c] = v[t];
-    }
+  for (int i = 0; i < N; ++i) {
+    const int e = i * WAVE + l;
+    *reinterpret_cast<bf16x8*>(&L.xr[e / SEG][8 * (e % SEG)]) =
+        *reinterpret_cast<const bf16x8*>(X + (size_t)8 * e);
+  }
 }
 
-// Z = Tc X in T-form tiles, Tc given as row packs, X read as column packs from LDS;
-// stored row-major [C][D] (4 consecutive columns per lane)
+// Z = Tc X in T-form tiles, Tc given as row packs, X's column packs read from the
+// row-major LDS copy with the transpose read: lane (g, j) addressing
+// xr[r0 + 4g + j/4][c0 + 4(j%4)] receives xr[r0 + 4g + k][c0 + j], k = 0..3, which is
+// the token pair p column fragment (slot t <-> token 32p + 16(t/4) + 4g + t%4) of
+// column c0 + j.  Stored row-major [C][D]: fp32 as 4 consecutive columns per lane,
+// bf16 as 8 (two column tiles at a time, store_pair_bf16).
 template <int NT, int D>
 __device__ __forceinline__ void apply_rows(const bf16x8 (&rp)[NT][(NT + 1) / 2],
                                            const bf16x8 (&rl)[NT][(NT + 1) / 2],
                                            const WyLds<NT, D>& L, void* __restrict__ out,
                                            bool out_bf16) {
   constexpr int C = 16 * NT, NP = (NT + 1) / 2;
+  static_assert(D % 32 == 0, "column tiles are stored in pairs");
   const int l = lane_id(), g = l >> 4, c = l & 15;
 #pragma unroll
-  for (int e = 0; e < D / 16; ++e) {
-    bf16x8 cp[NP];
+  for (int e2 = 0; e2 < D / 32; ++e2) {
+    bf16x8 cp[2][NP];
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const __bf16* src = &L.xt[16 * e + c][32 * p + 4 * g];
-      bf16x4 lo = *reinterpret_cast<const bf16x4*>(src);
-      bf16x4 hi = (32 * p + 16 < C) ? *reinterpret_cast<const bf16x4*>(src + 16) : bf16x4{};
-      cp[p] = join8(lo, hi);
-    }
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int e = 2 * e2 + h;
+        const bf16x4 lo = lds_read_tr4(&L.xr[32 * p + 4 * g + (c >> 2)][16 * e + 4 * (c & 3)]);
+        bf16x4 hi = bf16x4{};
+        if (32 * p + 16 < C) hi = lds_read_tr4(&L.xr[32 * p + 16 + 4 * g + (c >> 2)][16 * e + 4 * (c & 3)]);
+        cp[h][p] = join8(lo, hi);
+      }
 #pragma unroll
     for (int I = 0; I < NT; ++I) {
-      f32x4 acc = zero4();
+      f32x4 acc[2];
 #pragma unroll
-      for (int p = 0; p <= I / 2; ++p) {
-        acc = mma_bf16(cp[p], rp[I][p], acc);
-        acc = mma_bf16(cp[p], rl[I][p], acc);
+      for (int h = 0; h < 2; ++h) {
+        acc[h] = zero4();
+#pragma unroll
+        for (int p = 0; p <= I / 2; ++p) {
+          acc[h] = mma_bf16(cp[h][p], rp[I][p], acc[h]);
+          acc[h] = mma_bf16(cp[h][p], rl[I][p], acc[h]);
+        }
       }
-      const size_t o = (size_t)(16 * I + c) * D + 16 * e + 4 * g;
-      if (out_bf16)
-        *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(out) + o) = pack4(acc);
-      else
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + o) = acc;
+      const size_t rowo = (size_t)(16 * I + c) * D;
+      if (out_bf16) {
+        store_pair_bf16(reinterpret_cast<__bf16*>(out) + rowo, 2 * e2, acc[0], acc[1]);
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + rowo + 16 * (2 * e2 + h) + 4 * g) = acc[h];
+      }
     }
   }
 }
@@ -170,7 +185,7 @@ __global__ __launch_bounds__(256) void wy_kernel(BlocksArgs a, const void* __res
   scaled_row_packs<NT>(TT, fb, rpu, rlu);
 
   // W = (T diag(s)) K
-  stage_transposed<NT, DK>(reinterpret_cast<const __bf16*>(a.K) + (size_t)b * C * DK, LK);
+  stage_rows<NT, DK>(reinterpret_cast<const __bf16*>(a.K) + (size_t)b * C * DK, LK);
   __syncthreads();
   if (live) {
     void* wo = out_bf16 ? (void*)(reinterpret_cast<__bf16*>(W_out) + (size_t)b * C * DK)
@@ -179,7 +194,7 @@ __global__ __launch_bounds__(256) void wy_kernel(BlocksArgs a, const void* __res
   }
   __syncthreads();
   // U = (T diag(beta)) V
-  stage_transposed<NT, DV>(V + (size_t)b * C * DV, LV);
+  stage_rows<NT, DV>(V + (size_t)b * C * DV, LV);
   __syncthreads();
   if (live) {
     void* uo = out_bf16 ? (void*)(reinterpret_cast<__bf16*>(U_out) + (size_t)b * C * DV)
