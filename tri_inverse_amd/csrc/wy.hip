@@ -153,8 +153,22 @@ __global__ __launch_bounds__(256) void wy_kernel(BlocksArgs a, const void* __res
       }
   } else {  // formed here from K, beta, g
     KBlock<NT, DK> kb;
-    load_kblock<NT, DK>(reinterpret_cast<const __bf16*>(a.K) + (size_t)b * C * DK, a.beta + (size_t)b * C,
-                        a.g + (size_t)b * C, kb);
+    if constexpr (MODE == MODE_NEUMANN) {
+      // K is read from HBM once, into LDS; the Gram fragments and the W product both
+      // take it from there (measured faster for the truncated sums, slower for the
+      // doubling product, whose longer register lifetime then costs occupancy)
+      stage_rows<NT, DK>(reinterpret_cast<const __bf16*>(a.K) + (size_t)b * C * DK, LK);
+#pragma unroll
+      for (int I = 0; I < NT; ++I)
+#pragma unroll
+        for (int s = 0; s < DK / 32; ++s)
+          kb.kf[I][s] = *reinterpret_cast<const bf16x8*>(&LK.xr[16 * I + c][32 * s + 8 * g]);
+      kb.gl = (l < C) ? a.g[(size_t)b * C + l] : 0.f;
+      kb.bl = (l < C) ? a.beta[(size_t)b * C + l] : 0.f;
+    } else {
+      load_kblock<NT, DK>(reinterpret_cast<const __bf16*>(a.K) + (size_t)b * C * DK, a.beta + (size_t)b * C,
+                          a.g + (size_t)b * C, kb);
+    }
     Gates<NT> g2;
     gates_from_lanes<NT>(kb.gl, kb.bl, a.g_cumulative != 0, g2);
     Mat<NT> S, AD, AT;
@@ -185,7 +199,8 @@ __global__ __launch_bounds__(256) void wy_kernel(BlocksArgs a, const void* __res
   scaled_row_packs<NT>(TT, fb, rpu, rlu);
 
   // W = (T diag(s)) K
-  stage_rows<NT, DK>(reinterpret_cast<const __bf16*>(a.K) + (size_t)b * C * DK, LK);
+  if constexpr (TSRC != 2 || MODE != MODE_NEUMANN)  // (else K is in LDS already)
+    stage_rows<NT, DK>(reinterpret_cast<const __bf16*>(a.K) + (size_t)b * C * DK, LK);
   __syncthreads();
   if (live) {
     void* wo = out_bf16 ? (void*)(reinterpret_cast<__bf16*>(W_out) + (size_t)b * C * DK)
