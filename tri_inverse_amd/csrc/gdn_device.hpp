@@ -149,40 +149,107 @@ __device__ __forceinline__ void store_pair_bf16(__bf16* __restrict__ row, int e,
 }
 
 // ---- wave-wide reductions and scans (wave64) ------------------------------------
+// All in the VALU (no LDS round trip): DPP within each 16-lane row, then
+// v_permlane16_swap / v_permlane32_swap (or readlane) across the four rows.  Each swap
+// of a value with itself returns the two rows of every row pair, so combining both
+// results gives every lane the pair's value.
+
+// DPP controls: row_shr:k = 0x110 + k, row_ror:k = 0x120 + k.  Lanes whose source lies
+// outside their row read 0.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
+}
+
+// the two results of v_permlane16_swap (W = 16) or v_permlane32_swap (W = 32) of x
+// with itself: rows (0,0,2,2) and (1,1,3,3), or rows (0,1,0,1) and (2,3,2,3)
+template <int W>
+__device__ __forceinline__ void self_swap(uint32_t x, uint32_t& a, uint32_t& b) {
+  if constexpr (W == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    const uint32_t r0 = r[0], r1 = r[1];  // elements to scalars before use
+    a = r0;
+    b = r1;
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    a = r0;
+    b = r1;
+  }
+}
+template <int W>
+__device__ __forceinline__ void self_swap_f(float x, float& a, float& b) {
+  uint32_t ua, ub;
+  self_swap<W>(__builtin_bit_cast(uint32_t, x), ua, ub);
+  a = __builtin_bit_cast(float, ua);
+  b = __builtin_bit_cast(float, ub);
+}
+
+// reduce over the 16 lanes of each row (rotations by 8, 4, 2, 1), then over the rows
+template <typename F>
+__device__ __forceinline__ float wave_reduce(float v, F op) {
+  v = op(v, dpp_f<0x128>(v));
+  v = op(v, dpp_f<0x124>(v));
+  v = op(v, dpp_f<0x122>(v));
+  v = op(v, dpp_f<0x121>(v));
+  float a, b;
+  self_swap_f<16>(v, a, b);
+  v = op(a, b);
+  self_swap_f<32>(v, a, b);
+  return op(a, b);
+}
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
+  return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); });
 }
 
 __device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fminf(v, __shfl_xor(v, off, 64));
-  return v;
+  return wave_reduce(v, [](float x, float y) { return fminf(x, y); });
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  return wave_reduce(v, [](float x, float y) { return x + y; });
 }
 
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += (uint32_t)__shfl_xor((int)v, off, 64);
-  return v;
+  v += dpp_u<0x128>(v);
+  v += dpp_u<0x124>(v);
+  v += dpp_u<0x122>(v);
+  v += dpp_u<0x121>(v);
+  uint32_t a, b;
+  self_swap<16>(v, a, b);
+  v = a + b;
+  self_swap<32>(v, a, b);
+  return a + b;
 }
 
-// inclusive prefix sum over the first n lanes (n <= 64); lanes >= n get garbage
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 within each row (lanes
+// that would read across the row start add 0), then each row adds the totals of the
+// rows before it
 __device__ __forceinline__ float wave_inclusive_scan(float v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    float o = __shfl_up(v, off, 64);
-    if (l >= off) v += o;
-  }
-  return v;
+  v += dpp_f<0x111>(v);
+  v += dpp_f<0x112>(v);
+  v += dpp_f<0x114>(v);
+  v += dpp_f<0x118>(v);
+  const float t0 = readlane_f(v, 15), t1 = readlane_f(v, 31), t2 = readlane_f(v, 47);
+  const int row = lane_id() >> 4;
+  return v + ((row >= 1 ? t0 : 0.f) + (row >= 2 ? t1 : 0.f) + (row >= 3 ? t2 : 0.f));
+}
+
+// bc[X] = x of lane 16X + c, in every lane (g, c): the four row broadcasts
+__device__ __forceinline__ void row_broadcasts(float x, float (&bc)[4]) {
+  float a, b;
+  self_swap_f<16>(x, a, b);  // rows (0,0,2,2), (1,1,3,3)
+  self_swap_f<32>(a, bc[0], bc[2]);
+  self_swap_f<32>(b, bc[1], bc[3]);
 }
 
 }  // namespace gdn

@@ -64,11 +64,13 @@ __device__ __forceinline__ void gather_gates(float Gl, float bl, Gates<NT>& gt) 
   gt.bl = bl;
   gt.split = wave_min(Gl) >= -80.f;
   const float rl = -bl * __expf(Gl), nl = __expf(-Gl);
+  float rb[4], nb[4];
+  row_broadcasts(rl, rb);
+  row_broadcasts(nl, nb);
 #pragma unroll
   for (int X = 0; X < NT; ++X) {
-    const int ic = 16 * X + c;
-    gt.rc[X] = __shfl(rl, ic, 64);
-    gt.nc[X] = __shfl(nl, ic, 64);
+    gt.rc[X] = rb[X];
+    gt.nc[X] = nb[X];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int ir = 16 * X + 4 * grp + r;
