@@ -188,7 +188,7 @@ __device__ __forceinline__ void produce_T(const ChunkArgs& a, const ChunkIn<DK>&
     for (int p = 0; p < 2; ++p)
       if (2 * p <= I && I - (2 * p + 1) <= MAXD)
         trp[I][p][l] = pack8(tile_or_zero(TT, I, 2 * p), tile_or_zero(TT, I, 2 * p + 1));
-  const float GC = __shfl(gt.Gl, CH - 1, 64);
+  const float GC = readlane_f(gt.Gl, CH - 1);
   GT.beta[l] = bl;
   GT.eg[l] = __expf(gt.Gl);
   GT.eng[l] = __expf(-gt.Gl);

@@ -170,7 +170,7 @@ __global__ __launch_bounds__(NT * WAVE / 2, 1) void dense_kernel(DenseArgs p) {
     for (int s = 0; s < C; s += WAVE) {
       const float gv = a.g[b * C + s + l], bv = a.beta[b * C + s + l];
       const float Gv = a.g_cumulative ? gv : carry + wave_inclusive_scan(gv);
-      carry = __shfl(Gv, WAVE - 1, 64);
+      carry = readlane_f(Gv, WAVE - 1);
       gs.beta[s + l] = bv;
       gs.G[s + l] = Gv;
       gs.rowf[s + l] = -bv * __expf(Gv);
