@@ -62,12 +62,15 @@ def load_traffic(kernel_key: str):
     return ent.get("hbm_bytes_per_launch")
 
 
-def time_launches(torch, launch, n_sets, steps, warmup):
+def time_launches(torch, launch, n_sets, steps, warmup, repeats=7):
     """Run `launch(set_index)` `warmup` times eagerly, then capture exactly `steps`
-    launches (rotating buffer sets) in one HIP graph and time one replay with HIP
-    events on the replay stream.  Returns ms per step (= per launch).  Replaying a
-    graph keeps Python's per-call overhead out of the timed region, so back-to-back
-    kernels run without host-induced gaps."""
+    launches (rotating buffer sets) in one HIP graph.  The graph is replayed once
+    untimed, then `repeats` times, each replay timed on its own with HIP events on the
+    replay stream (each timed region holds exactly `steps` launches).  Returns the
+    median ms per launch and the list of all repeats.  Replaying a graph keeps Python's
+    per-call overhead out of the timed region, so back-to-back kernels run without
+    host-induced gaps; the median of several replays keeps clock ramps and one-off
+    stalls out of the figure."""
     for i in range(warmup):
         launch(i % n_sets)
     torch.cuda.synchronize()
@@ -78,15 +81,18 @@ def time_launches(torch, launch, n_sets, steps, warmup):
     graph.replay()  # untimed: first replay uploads the graph
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    graph.replay()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+    per = []
+    for _ in range(repeats):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        graph.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        per.append(t0.elapsed_time(t1) / steps)
     del graph
-    return ms, ms
+    ms = sorted(per)[len(per) // 2]
+    return ms, per
 
 
 # ------------------------------------------------------------------ c1: tri-inverse
@@ -154,7 +160,8 @@ def bench_c1(torch, tri, synth, steps, warmup):
             name = "N%d_%s_int8" % (v[1], "masked" if v[2] else "unmasked")
         name += "_T" + ("f32" if v[3] == torch.float32 else "bf16")
         st = steps if v == variants[0] else max(10, steps // 2)
-        ms_step, ms_kernel = time_launches(torch, mk(v, v[3]), N_SETS, st, warmup)
+        ms_step, reps = time_launches(torch, mk(v, v[3]), N_SETS, st, warmup)
+        ms_kernel = ms_step
         nb, by, fl = c1_bytes_flops(v, 4 if v[3] == torch.float32 else 2)
         if v[0] == "int8":  # bf16 Gram, int8 products: MFMA time at each one's peak
             gram = nb * 2 * C * C * C1["d_k"]
@@ -163,6 +170,7 @@ def bench_c1(torch, tri, synth, steps, warmup):
             t_mfma = fl / (BF16_PEAK_TFLOPS * 1e12)
         results[name] = {
             "ms_per_step": ms_step, "ms_kernel": ms_kernel,
+            "repeats_ms": [round(x, 5) for x in reps],
             "blocks_per_s": nb / (ms_step * 1e-3),
             "hbm_frac": by / (ms_kernel * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "mfma_frac": t_mfma / (ms_kernel * 1e-3),
@@ -508,6 +516,8 @@ def main():
                                "mask, fp32 accumulate, T fp32",
                    "n_blocks": 2048, "C": 64, "d_k": 128, "N": 3, "mask": True},
         "roofline": roofline,
+        "timing": "each leg: K launches captured in one HIP graph, replayed 7 times, each "
+                  "replay timed with HIP events on its stream; ms_per_step is the median",
         "variants": c1,
         "source_digest": source_digest(),
     }

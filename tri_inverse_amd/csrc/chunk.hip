@@ -22,14 +22,13 @@
 //   waves 0, 1  state waves: each owns 16 columns of S (fp32, in registers) and runs
 //               the sequential part of a chunk: K S, Y, U' = T Y and the state update.
 //               They hand S^T (bf16) and U' (hi/lo) to the output waves.
-//   waves 4, 5  output waves, one chunk behind, each on a state wave's SIMD: P and
-//               O = scale (e^G Q S + P U') for row tiles {0, 3} and {1, 2} of the chunk
-//               (equal shares of the triangular P), all 32 columns.  (Both output waves
-//               on one SIMD of their own measured 5 % slower.)
+//   waves 7, 4, 5, 3  output waves for row tiles 0, 1, 2, 3, one chunk behind: P and
+//               O = scale (e^G Q S + P U') for their 16 rows, all 32 columns.  Tiles 1
+//               and 2 share the state waves' SIMDs, tiles 0 and 3 (the lightest and the
+//               heaviest share of the triangular P) the fourth SIMD.
 //   wave 2      gates and T of the next chunk.
 //   wave 6      copies K rows, V columns, log-gates and beta of the chunk after next
 //               into a 4-deep LDS ring.
-//   waves 3, 7  only join the barriers.
 // One barrier per chunk hands every buffer over (schedule above the kernel).  The K
 // rows sit in LDS row-major; the K^T operand of the state update comes from the same
 // rows through the LDS transpose read.  Q is read once per workgroup, each lane taking
@@ -130,14 +129,14 @@ __device__ __forceinline__ bf16x8 rowfrag_nat(const ChunkIn<DK>& R, int row, int
   return *reinterpret_cast<const bf16x8*>(&R.k[row][32 * p + 8 * g]);
 }
 
-template <int DK, int I0, int I1>
-__device__ __forceinline__ void load_q_nat(const ChunkArgs& a, int64_t row0, bf16x8 (&q)[2][DK / 32]) {
+template <int DK, int NI, int I0, int I1>
+__device__ __forceinline__ void load_q_nat(const ChunkArgs& a, int64_t row0, bf16x8 (&q)[NI][DK / 32]) {
   const int l = lane_id(), g = l >> 4, c = l & 15;
   const __bf16* base = a.Q + (row0 + c) * DK + 8 * g;
 #pragma unroll
   for (int p = 0; p < DK / 32; ++p) {
     q[0][p] = *reinterpret_cast<const bf16x8*>(base + (16 * I0) * DK + 32 * p);
-    q[1][p] = *reinterpret_cast<const bf16x8*>(base + (16 * I1) * DK + 32 * p);
+    if constexpr (NI > 1) q[NI - 1][p] = *reinterpret_cast<const bf16x8*>(base + (16 * I1) * DK + 32 * p);
   }
 }
 
@@ -304,19 +303,20 @@ struct StateWave {
   }
 };
 
-// ---- waves 4, 5: P and O = scale (e^G Q S + P U') for row tiles I0, I1 -----------------
+// ---- output waves: P and O = scale (e^G Q S + P U') for NI row tiles I0 (, I1) --------
 // q holds the chunk's Q rows of those tiles (natural d order).
-template <int DK, int I0, int I1, bool OBF16>
+template <int DK, int NI, int I0, int I1, bool OBF16>
 __device__ __forceinline__ void emit_rows(const ChunkArgs& a, int64_t row0, int col0, const ChunkIn<DK>& R,
                                           const ChunkGates& GT, const ChunkBuf<DK>& B,
-                                          const bf16x8 (&q)[2][DK / 32]) {
+                                          const bf16x8 (&q)[NI][DK / 32]) {
   constexpr int NP = DK / 32;
-  constexpr int IS[2] = {I0, I1};
+  constexpr int IS[2] = {I0, NI > 1 ? I1 : I0};
+  constexpr int IMAX = IS[0] > IS[NI - 1] ? IS[0] : IS[NI - 1];
   const int l = lane_id(), g = l >> 4, c = l & 15;
   // Q S for both column halves (T-form: lane (g,c) reg r = row 16I + c, column 4g + r)
-  f32x4 acc[2][2];
+  f32x4 acc[NI][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int h = 0; h < 2; ++h) acc[i][h] = zero4();
 #pragma unroll
@@ -325,18 +325,18 @@ __device__ __forceinline__ void emit_rows(const ChunkArgs& a, int64_t row0, int 
     for (int h = 0; h < 2; ++h) {
       const bf16x8 sf = *reinterpret_cast<const bf16x8*>(&B.st[h][c][32 * p + 8 * g]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) acc[i][h] = mma_bf16(sf, q[i][p], acc[i][h]);
+      for (int i = 0; i < NI; ++i) acc[i][h] = mma_bf16(sf, q[i][p], acc[i][h]);
     }
   // raw P tiles (I, J), J <= I, one K tile-row at a time
-  f32x4 pt[2][CNT];
+  f32x4 pt[NI][CNT];
 #pragma unroll
   for (int J = 0; J < CNT; ++J) {
-    if (J > I0 && J > I1) continue;
+    if (J > IMAX) continue;
     bf16x8 kf[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) kf[p] = rowfrag_nat<DK>(R, 16 * J + c, p);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NI; ++i) {
       if (J > IS[i]) continue;
       f32x4 t = zero4();
 #pragma unroll
@@ -349,7 +349,7 @@ __device__ __forceinline__ void emit_rows(const ChunkArgs& a, int64_t row0, int 
   const bool split = __builtin_amdgcn_readfirstlane(GT.split) != 0;
   const int lo_ = 4 * g - c;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < NI; ++i) {
     const int I = IS[i];
     const float rowf = GT.eg[16 * I + c];
 #pragma unroll
@@ -387,7 +387,7 @@ __device__ __forceinline__ void emit_rows(const ChunkArgs& a, int64_t row0, int 
       ul[h][q2] = B.ul[h][q2][l];
     }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2) {
       if (2 * q2 > IS[i]) continue;
@@ -401,7 +401,7 @@ __device__ __forceinline__ void emit_rows(const ChunkArgs& a, int64_t row0, int 
       }
     }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const f32x4 o = acc[i][h] * a.scale;
@@ -439,7 +439,7 @@ __device__ __forceinline__ void lds_barrier() {
 //   wave 2      it: T, gates of chunk it+1  reads in         writes buf.trp, gr
 //   waves 0, 1  it: state step of chunk it  reads in, gr, buf.trp
 //                                           writes buf.st, buf.uh/ul
-//   waves 4, 5  it: P, O of chunk it-1      reads in, gr, buf.{st, uh, ul}
+//   waves 3-5, 7 it: P, O of chunk it-1     reads in, gr, buf.{st, uh, ul}
 // Every slot is written in one iteration and read only in later ones, and its next
 // write comes after its last read: in[j] is written at j-2, read at j-1 .. j+1 and
 // rewritten at j+2; gr[j] is read at j and j+1 and rewritten at j+2; buf[j].trp is read
@@ -448,7 +448,9 @@ __device__ __forceinline__ void lds_barrier() {
 // wave 2 writes that buffer's trp, a field they do not touch.  Global loads are issued
 // one iteration before their data is needed (register ping-pong, no loop-carried
 // copies, no conditional loads), so their latency overlaps a whole iteration.
-constexpr int W_STATE0 = 0, W_STATE1 = 1, W_T = 2, W_OUT0 = 4, W_STAGE = 6, W_OUT1 = 5;
+constexpr int W_STATE0 = 0, W_STATE1 = 1, W_T = 2, W_STAGE = 6;
+// output wave of row tile 0..3: tiles 1 and 2 beside the state waves, 0 and 3 together
+constexpr int W_OUT0 = 7, W_OUT1 = 4, W_OUT2 = 5, W_OUT3 = 3;
 
 template <int DK, int MODE, int CMP, int MAXD, bool OBF16>
 __global__ __launch_bounds__(NWAVES * WAVE, 1) void chunk_fwd_kernel(ChunkArgs a) {
@@ -551,33 +553,33 @@ __global__ __launch_bounds__(NWAVES * WAVE, 1) void chunk_fwd_kernel(ChunkArgs a
     }
     return;
   }
-  if (wave == W_OUT0 || wave == W_OUT1) {
-    // chunk ch = it - 1 in iteration it; that iteration also loads chunk ch + 1
-    auto out_loop = [&](auto i0, auto i1) {
-      constexpr int I0 = decltype(i0)::value, I1 = decltype(i1)::value;
+  if (wave == W_OUT0 || wave == W_OUT1 || wave == W_OUT2 || wave == W_OUT3) {
+    // chunk ch = it - 1 in iteration it; that iteration also loads chunk ch + 1's Q rows
+    auto out_loop = [&](auto i0) {
+      constexpr int I0 = decltype(i0)::value;
       auto clampc = [&](int ch) { return ch < 0 ? 0 : (ch < last ? ch : last); };
-      bf16x8 q0[2][DK / 32], q1[2][DK / 32];
-      auto work = [&](int ch, const bf16x8 (&q)[2][DK / 32]) {
-        emit_rows<DK, I0, I1, OBF16>(a, head_row0 + (int64_t)ch * CH, slice * DVS, ring(in, ch & 3),
-                                     ring(gr, ch % 3), ring(buf, ch & 1), q);
+      bf16x8 q0[1][DK / 32], q1[1][DK / 32];
+      auto work = [&](int ch, const bf16x8 (&q)[1][DK / 32]) {
+        emit_rows<DK, 1, I0, I0, OBF16>(a, head_row0 + (int64_t)ch * CH, slice * DVS, ring(in, ch & 3),
+                                        ring(gr, ch % 3), ring(buf, ch & 1), q);
       };
       lds_barrier();
       for (int it = -1; it <= nchunks; it += 2) {
         int ch = it - 1;  // even
-        load_q_nat<DK, I0, I1>(a, head_row0 + (int64_t)clampc(ch + 1) * CH, q1);
+        load_q_nat<DK, 1, I0, I0>(a, head_row0 + (int64_t)clampc(ch + 1) * CH, q1);
         if (ch >= 0 && ch < nchunks) work(ch, q0);
         lds_barrier();
         if (it + 1 > nchunks) break;
         ch += 1;  // odd
-        load_q_nat<DK, I0, I1>(a, head_row0 + (int64_t)clampc(ch + 1) * CH, q0);
+        load_q_nat<DK, 1, I0, I0>(a, head_row0 + (int64_t)clampc(ch + 1) * CH, q0);
         if (ch >= 0 && ch < nchunks) work(ch, q1);
         lds_barrier();
       }
     };
-    if (wave == W_OUT0)
-      out_loop(std::integral_constant<int, 0>{}, std::integral_constant<int, 3>{});
-    else
-      out_loop(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
+    if (wave == W_OUT0) out_loop(std::integral_constant<int, 0>{});
+    else if (wave == W_OUT1) out_loop(std::integral_constant<int, 1>{});
+    else if (wave == W_OUT2) out_loop(std::integral_constant<int, 2>{});
+    else out_loop(std::integral_constant<int, 3>{});
     return;
   }
   if (wave != W_STATE0 && wave != W_STATE1) {
