@@ -167,8 +167,37 @@ __device__ __forceinline__ void produce_T(const ChunkArgs& a, const ChunkIn<DK>&
     for (int p = 0; p < DK / 32; ++p) kb.kf[I][p] = rowfrag_nat<DK>(R, 16 * I + c, p);  // K K^T: any common d order
   kb.gl = gl;
   kb.bl = bl;
+  // Gates: G by the wave scan.  The per-position factors go to GT first (the other
+  // waves read them there anyway); the D-form row factors are read back with one
+  // 16-byte LDS read per tile and factor instead of a lane gather per value.
   Gates<CNT> gt;
-  gates_from_lanes<CNT>(gl, bl, false, gt);
+  gt.Gl = wave_inclusive_scan(gl);
+  gt.bl = bl;
+  gt.split = wave_min(gt.Gl) >= -80.f;
+  const float egl = __expf(gt.Gl), engl = __expf(-gt.Gl);
+  GT.beta[l] = bl;
+  GT.eg[l] = egl;
+  GT.eng[l] = engl;
+  GT.G[l] = gt.Gl;
+  {
+    const int g4 = 4 * (l >> 4);
+    float rb[4], nb[4];
+    row_broadcasts(-bl * egl, rb);
+    row_broadcasts(engl, nb);
+#pragma unroll
+    for (int X = 0; X < CNT; ++X) {
+      gt.rc[X] = rb[X];
+      gt.nc[X] = nb[X];
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(&GT.beta[16 * X + g4]);
+      const f32x4 e4 = *reinterpret_cast<const f32x4*>(&GT.eg[16 * X + g4]);
+      const f32x4 n4 = *reinterpret_cast<const f32x4*>(&GT.eng[16 * X + g4]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        gt.rr[X][r] = -b4[r] * e4[r];
+        gt.nr[X][r] = n4[r];
+      }
+    }
+  }
   Mat<CNT> S, AD, AT, TT;
   constexpr bool BANDED = (MODE == MODE_NEUMANN && CMP == CMP_FP8);
   gram_from_frags<CNT, DK, MAXD>(kb, S);
@@ -188,11 +217,7 @@ __device__ __forceinline__ void produce_T(const ChunkArgs& a, const ChunkIn<DK>&
       if (2 * p <= I && I - (2 * p + 1) <= MAXD)
         trp[I][p][l] = pack8(tile_or_zero(TT, I, 2 * p), tile_or_zero(TT, I, 2 * p + 1));
   const float GC = readlane_f(gt.Gl, CH - 1);
-  GT.beta[l] = bl;
-  GT.eg[l] = __expf(gt.Gl);
-  GT.eng[l] = __expf(-gt.Gl);
   GT.egcg[l] = __expf(GC - gt.Gl);
-  GT.G[l] = gt.Gl;
   if (l == 0) {
     GT.egc = __expf(GC);
     GT.split = gt.split ? 1 : 0;
