@@ -230,19 +230,32 @@ struct StateWave {
   static constexpr int NP = DK / 32;
   static constexpr int NA = DK / 16;
   f32x4 S[NA];  // D-form tiles: lane (g,c) reg r = S[sdim(a, g, r)][col0 + c]
+  bf16x8 kfn[CNT][NP];  // this chunk's K rows, read at the end of the previous step
+
+  // K rows of a chunk as the K S operand (natural d order, the state's d order)
+  __device__ __forceinline__ void read_k(const ChunkIn<DK>& R) {
+    const int c = lane_id() & 15;
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int I = 0; I < CNT; ++I) kfn[I][p] = rowfrag_nat<DK>(R, 16 * I + c, p);
+  }
 
   // one chunk: S^T out, K S, Y, U' = T Y (out), state update.  LDS operands are
   // requested in two batches, each ahead of the phase before the one that needs it, so
   // that the reads overlap MFMA and VALU work instead of sitting between them.
-  __device__ __forceinline__ void step(const ChunkIn<DK>& R, const ChunkGates& GT, ChunkBuf<DK>& B, int v) {
+  // Rn: the next chunk's inputs (already in LDS), whose K rows are read at the end of
+  // this step, off the dependency chain of the next one
+  __device__ __forceinline__ void step(const ChunkIn<DK>& R, const ChunkIn<DK>& Rn, const ChunkGates& GT,
+                                       ChunkBuf<DK>& B, int v) {
     const int l = lane_id(), g = l >> 4, c = l & 15;
-    // batch 1: K rows (natural d order, matching the state's d order), V tiles in
-    // D-form (rows 16I + 4g + r, column 16v + c) by the transpose read, beta and e^G
+    // batch 1: V tiles in D-form (rows 16I + 4g + r, column 16v + c) by the transpose
+    // read, beta and e^G (the K rows were read by the previous step)
     bf16x8 kf[CNT][NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
-      for (int I = 0; I < CNT; ++I) kf[I][p] = rowfrag_nat<DK>(R, 16 * I + c, p);
+      for (int I = 0; I < CNT; ++I) kf[I][p] = kfn[I][p];
     bf16x4 vt[CNT];
 #pragma unroll
     for (int I = 0; I < CNT; ++I) vt[I] = lds_read_tr4(&R.v[16 * I + 4 * g + (c >> 2)][16 * v + 4 * (c & 3)]);
@@ -325,6 +338,7 @@ struct StateWave {
       B.uh[v][p][l] = h;
       B.ul[v][p][l] = lw;
     }
+    read_k(Rn);
   }
 };
 
@@ -622,8 +636,12 @@ __global__ __launch_bounds__(NWAVES * WAVE, 1) void chunk_fwd_kernel(ChunkArgs a
     for (int r = 0; r < 4; ++r)
       sw.S[A][r] = a.S0 ? a.S0[((size_t)bh * DK + sdim(A, g, r)) * a.dv + col0 + c] : 0.f;
   lds_barrier();
+  sw.read_k(in[0]);  // chunk 0 is in LDS after the first barrier
   for (int it = -1; it <= nchunks; ++it) {
-    if (it >= 0 && it < nchunks) sw.step(ring(in, it & 3), ring(gr, it % 3), ring(buf, it & 1), v);
+    // the next chunk's slot: staged one iteration earlier, rewritten three later (past
+    // the end it holds stale rows, read but never used)
+    if (it >= 0 && it < nchunks)
+      sw.step(ring(in, it & 3), ring(in, (it + 1) & 3), ring(gr, it % 3), ring(buf, it & 1), v);
     lds_barrier();
   }
 #pragma unroll
