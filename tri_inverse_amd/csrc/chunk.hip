@@ -230,15 +230,25 @@ struct StateWave {
   static constexpr int NP = DK / 32;
   static constexpr int NA = DK / 16;
   f32x4 S[NA];  // D-form tiles: lane (g,c) reg r = S[sdim(a, g, r)][col0 + c]
-  bf16x8 kfn[CNT][NP];  // this chunk's K rows, read at the end of the previous step
+  // this chunk's K rows, V tiles and beta, read at the end of the previous step
+  bf16x8 kfn[CNT][NP];
+  bf16x4 vtn[CNT];
+  f32x4 b4n[CNT];
 
-  // K rows of a chunk as the K S operand (natural d order, the state's d order)
-  __device__ __forceinline__ void read_k(const ChunkIn<DK>& R) {
-    const int c = lane_id() & 15;
+  // a chunk's raw inputs as the step uses them: K rows as the K S operand (natural d
+  // order, the state's d order), V in D-form (rows 16I + 4g + r, column 16v + c) by the
+  // transpose read, beta at rows 16I + 4g + r
+  __device__ __forceinline__ void read_inputs(const ChunkIn<DK>& R, int v) {
+    const int l = lane_id(), g = l >> 4, c = l & 15;
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
       for (int I = 0; I < CNT; ++I) kfn[I][p] = rowfrag_nat<DK>(R, 16 * I + c, p);
+#pragma unroll
+    for (int I = 0; I < CNT; ++I) {
+      vtn[I] = lds_read_tr4(&R.v[16 * I + 4 * g + (c >> 2)][16 * v + 4 * (c & 3)]);
+      b4n[I] = *reinterpret_cast<const f32x4*>(&R.beta[16 * I + 4 * g]);
+    }
   }
 
   // one chunk: S^T out, K S, Y, U' = T Y (out), state update.  LDS operands are
@@ -249,20 +259,18 @@ struct StateWave {
   __device__ __forceinline__ void step(const ChunkIn<DK>& R, const ChunkIn<DK>& Rn, const ChunkGates& GT,
                                        ChunkBuf<DK>& B, int v) {
     const int l = lane_id(), g = l >> 4, c = l & 15;
-    // batch 1: V tiles in D-form (rows 16I + 4g + r, column 16v + c) by the transpose
-    // read, beta and e^G (the K rows were read by the previous step)
+    // batch 1: e^G (K rows, V tiles and beta were read by the previous step)
     bf16x8 kf[CNT][NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
       for (int I = 0; I < CNT; ++I) kf[I][p] = kfn[I][p];
     bf16x4 vt[CNT];
-#pragma unroll
-    for (int I = 0; I < CNT; ++I) vt[I] = lds_read_tr4(&R.v[16 * I + 4 * g + (c >> 2)][16 * v + 4 * (c & 3)]);
     f32x4 b4[CNT], e4[CNT];
 #pragma unroll
     for (int I = 0; I < CNT; ++I) {
-      b4[I] = *reinterpret_cast<const f32x4*>(&GT.beta[16 * I + 4 * g]);
+      vt[I] = vtn[I];
+      b4[I] = b4n[I];
       e4[I] = *reinterpret_cast<const f32x4*>(&GT.eg[16 * I + 4 * g]);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -338,7 +346,7 @@ struct StateWave {
       B.uh[v][p][l] = h;
       B.ul[v][p][l] = lw;
     }
-    read_k(Rn);
+    read_inputs(Rn, v);
   }
 };
 
@@ -636,7 +644,7 @@ __global__ __launch_bounds__(NWAVES * WAVE, 1) void chunk_fwd_kernel(ChunkArgs a
     for (int r = 0; r < 4; ++r)
       sw.S[A][r] = a.S0 ? a.S0[((size_t)bh * DK + sdim(A, g, r)) * a.dv + col0 + c] : 0.f;
   lds_barrier();
-  sw.read_k(in[0]);  // chunk 0 is in LDS after the first barrier
+  sw.read_inputs(in[0], v);  // chunk 0 is in LDS after the first barrier
   for (int it = -1; it <= nchunks; ++it) {
     // the next chunk's slot: staged one iteration earlier, rewritten three later (past
     // the end it holds stale rows, read but never used)
