@@ -351,11 +351,12 @@ struct StateWave {
 };
 
 // ---- output waves: P and O = scale (e^G Q S + P U') for NI row tiles I0 (, I1) --------
-// q holds the chunk's Q rows of those tiles (natural d order).
+// q holds the chunk's Q rows of those tiles, kr its K rows of tiles 0 .. max(I0, I1)
+// (natural d order).
 template <int DK, int NI, int I0, int I1, bool OBF16>
-__device__ __forceinline__ void emit_rows(const ChunkArgs& a, int64_t row0, int col0, const ChunkIn<DK>& R,
-                                          const ChunkGates& GT, const ChunkBuf<DK>& B,
-                                          const bf16x8 (&q)[NI][DK / 32]) {
+__device__ __forceinline__ void emit_rows(const ChunkArgs& a, int64_t row0, int col0,
+                                          const bf16x8 (&kr)[CNT][DK / 32], const ChunkGates& GT,
+                                          const ChunkBuf<DK>& B, const bf16x8 (&q)[NI][DK / 32]) {
   constexpr int NP = DK / 32;
   constexpr int IS[2] = {I0, NI > 1 ? I1 : I0};
   constexpr int IMAX = IS[0] > IS[NI - 1] ? IS[0] : IS[NI - 1];
@@ -379,15 +380,12 @@ __device__ __forceinline__ void emit_rows(const ChunkArgs& a, int64_t row0, int 
 #pragma unroll
   for (int J = 0; J < CNT; ++J) {
     if (J > IMAX) continue;
-    bf16x8 kf[NP];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) kf[p] = rowfrag_nat<DK>(R, 16 * J + c, p);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       if (J > IS[i]) continue;
       f32x4 t = zero4();
 #pragma unroll
-      for (int p = 0; p < NP; ++p) t = mma_bf16(kf[p], q[i][p], t);
+      for (int p = 0; p < NP; ++p) t = mma_bf16(kr[J][p], q[i][p], t);
       pt[i][J] = t;
     }
   }
@@ -606,20 +604,37 @@ __global__ __launch_bounds__(NWAVES * WAVE, 1) void chunk_fwd_kernel(ChunkArgs a
       constexpr int I0 = decltype(i0)::value;
       auto clampc = [&](int ch) { return ch < 0 ? 0 : (ch < last ? ch : last); };
       bf16x8 q0[1][DK / 32], q1[1][DK / 32];
+      // K rows of tiles 0..I0 of the chunk worked on next: read right after the
+      // current chunk's work (that chunk is already in LDS), off the next work's chain
+      bf16x8 kr[CNT][DK / 32];
+      auto read_k = [&](int ch) {
+        const ChunkIn<DK>& R = ring(in, ch & 3);
+#pragma unroll
+        for (int J = 0; J <= I0; ++J)
+#pragma unroll
+          for (int p = 0; p < DK / 32; ++p) kr[J][p] = rowfrag_nat<DK>(R, 16 * J + c, p);
+      };
       auto work = [&](int ch, const bf16x8 (&q)[1][DK / 32]) {
-        emit_rows<DK, 1, I0, I0, OBF16>(a, head_row0 + (int64_t)ch * CH, slice * DVS, ring(in, ch & 3),
-                                        ring(gr, ch % 3), ring(buf, ch & 1), q);
+        emit_rows<DK, 1, I0, I0, OBF16>(a, head_row0 + (int64_t)ch * CH, slice * DVS, kr, ring(gr, ch % 3),
+                                        ring(buf, ch & 1), q);
       };
       lds_barrier();
+      read_k(0);
       for (int it = -1; it <= nchunks; it += 2) {
         int ch = it - 1;  // even
         load_q_nat<DK, 1, I0, I0>(a, head_row0 + (int64_t)clampc(ch + 1) * CH, q1);
-        if (ch >= 0 && ch < nchunks) work(ch, q0);
+        if (ch >= 0 && ch < nchunks) {
+          work(ch, q0);
+          read_k(ch + 1);
+        }
         lds_barrier();
         if (it + 1 > nchunks) break;
         ch += 1;  // odd
         load_q_nat<DK, 1, I0, I0>(a, head_row0 + (int64_t)clampc(ch + 1) * CH, q0);
-        if (ch >= 0 && ch < nchunks) work(ch, q1);
+        if (ch >= 0 && ch < nchunks) {
+          work(ch, q1);
+          read_k(ch + 1);
+        }
         lds_barrier();
       }
     };
