@@ -230,10 +230,15 @@ struct StateWave {
   static constexpr int NP = DK / 32;
   static constexpr int NA = DK / 16;
   f32x4 S[NA];  // D-form tiles: lane (g,c) reg r = S[sdim(a, g, r)][col0 + c]
-  // this chunk's K rows, V tiles and beta, read at the end of the previous step
+  // this chunk's K rows, V tiles, beta and half of the K^T fragments, read at the end
+  // of the previous step
   bf16x8 kfn[CNT][NP];
   bf16x4 vtn[CNT];
   f32x4 b4n[CNT];
+  // K^T fragments of state tiles 0..KTP-1 read ahead as well (all eight measured no
+  // faster and leave no register headroom)
+  static constexpr int KTP = 4;
+  bf16x8 ktn[KTP][2];
 
   // a chunk's raw inputs as the step uses them: K rows as the K S operand (natural d
   // order, the state's d order), V in D-form (rows 16I + 4g + r, column 16v + c) by the
@@ -249,6 +254,10 @@ struct StateWave {
       vtn[I] = lds_read_tr4(&R.v[16 * I + 4 * g + (c >> 2)][16 * v + 4 * (c & 3)]);
       b4n[I] = *reinterpret_cast<const f32x4*>(&R.beta[16 * I + 4 * g]);
     }
+#pragma unroll
+    for (int A = 0; A < KTP; ++A)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) ktn[A][p] = ktpack_lds<DK>(R, A, p);
   }
 
   // one chunk: S^T out, K S, Y, U' = T Y (out), state update.  LDS operands are
@@ -306,7 +315,12 @@ struct StateWave {
 #pragma unroll
     for (int A = 0; A < NA; ++A)
 #pragma unroll
-      for (int p = 0; p < 2; ++p) kt[A][p] = ktpack_lds<DK>(R, A, p);
+      for (int p = 0; p < 2; ++p) {
+        if (A < KTP)
+          kt[A][p] = ktn[A][p];  // read at the end of the previous step
+        else
+          kt[A][p] = ktpack_lds<DK>(R, A, p);
+      }
     __builtin_amdgcn_sched_barrier(0);
     // Y = diag(beta) (V - diag(e^G) K S), D-form rows 16I + 4g + r
     f32x4 y[CNT];
