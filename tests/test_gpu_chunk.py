@@ -92,8 +92,8 @@ def _run_chunk(x, **kw):
     return f64(O), f64(S)
 
 
-@pytest.mark.parametrize("variant", [("neumann", 3, True), ("neumann", 3, False),
-                                     ("neumann", 2, True), ("exact", 0, False)])
+@pytest.mark.parametrize("variant", [("neumann", 3, True), ("neumann", 3, False), ("neumann", 2, True),
+                                     ("neumann", 1, True), ("neumann", 5, True), ("exact", 0, False)])
 def test_chunk_fwd_small(variant):
     mode, N, mask = variant
     B, H, T, dk, dv = 1, 3, 320, 128, 128   # 3 heads: the non-multiple-of-8 grid path
@@ -164,6 +164,24 @@ def test_chunk_fwd_special_cases():
     O0, S0o = tri.gdn_chunk_fwd(cuda(e["Q"]), cuda(e["K"]), cuda(e["V"]), cuda(e["beta"]),
                                 cuda(e["g"]), C=64)
     assert O0.shape == (B, H, 0, dv)
+
+
+@pytest.mark.parametrize("N,mask", [(3, True), (3, False)])
+def test_chunk_fwd_strong_gates(N, mask):
+    """Log-gates near -2.6 per token: G falls below -80 inside every chunk, so exp(-G)
+    would overflow fp32 and every gate factor is taken as exp of a difference."""
+    B, H, T, dk, dv = 1, 2, 256, 128, 128
+    say(f"chunk fwd strong gates N={N} mask={mask}")
+    x = synth.prefill(16, B, H, T, dk, dv)
+    x["g"] = (x["g"] - 2.5).contiguous()
+    x64 = {k: f64(v) for k, v in x.items()}
+    assert x64["g"][..., :32].sum(axis=-1).max() < -80.0
+    O, S = _run_chunk(x, C=64, scale=dk ** -0.5, N=N, mask=mask, o_dtype=torch.float32)
+    Or, Sr = oracle.chunk_fwd(x64["Q"], x64["K"], x64["V"], x64["beta"], x64["g"], 64, dk ** -0.5,
+                              N=N, mask=mask)
+    assert np.isfinite(O).all() and np.isfinite(S).all()
+    assert relF(O, Or) <= TOL["bf16"], relF(O, Or)
+    assert relF(S, Sr) <= TOL["bf16"], relF(S, Sr)
 
 
 def test_chunk_fwd_fp8_inverse():
