@@ -224,19 +224,12 @@ __device__ __forceinline__ void produce_T(const ChunkArgs& a, const ChunkIn<DK>&
   }
 }
 
-// Masked truncated sum with N <= 3 ([GEO] Methodologie SS2, the band mask): inside the
-// band (0 < i - j <= N) every chain i > m > ... > j of the power series has at most
-// i - j <= N steps, so there the masked sum is the exact inverse, and outside it T - I
-// is zero.  Its band follows from the three sub-diagonals a_d(i) = A[i][i - d] by
-//   t_1(i) = a_1(i)
-//   t_2(i) = a_2(i) + a_1(i) a_1(i-1)
-//   t_3(i) = a_3(i) + a_1(i) a_2(i-1) + a_2(i) a_1(i-2) + a_1(i) a_1(i-1) a_1(i-2),
-// element by element in fp32 (lane i = row i).  The Gram entries come from the MFMA
-// diagonal tiles and the last four columns of the tile left of each (T-form, through
-// LDS to the row lanes).  Only the band slots of the row packs are written: the rest
-// of both pack buffers is cleared once before the scan and stays zero.
+// Band-masked sum with N <= 3: the band of T - I by band3_from_subdiag (lane i = row
+// i).  The Gram entries come from the MFMA diagonal tiles and the last four columns of
+// the tile left of each (T-form, through LDS to the row lanes).  Only the band slots of
+// the row packs are written: the rest of both pack buffers is cleared once before the
+// scan and stays zero.
 constexpr int MODE_BAND = 16;  // chunk-only code next to the MODE_* values
-constexpr int XR_LD = 20;      // row of the Gram band buffer: 4 columns left + 16
 
 // row-pack slot (bf16 index into trp) of T - I at row i, column j
 __device__ __forceinline__ int trp_slot(int i, int j) {
@@ -244,16 +237,11 @@ __device__ __forceinline__ int trp_slot(int i, int j) {
   return ((I * 2 + p) * WAVE + 16 * gg + c) * 8 + (j & 3) + 4 * h;
 }
 
-// lane i receives lane i - 1's x (lane 0 receives 0): DPP wave_shr:1
-__device__ __forceinline__ float lane_shr1(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x138, 0xf, 0xf, false));
-}
-
 template <int DK>
 __device__ __forceinline__ void produce_T_band(const ChunkArgs& a, const ChunkIn<DK>& R,
                                                bf16x8 (&trp)[CNT][2][WAVE], ChunkGates& GT,
                                                float (&xr)[CH][XR_LD]) {
-  const int l = lane_id(), g = l >> 4, c = l & 15;
+  const int l = lane_id(), c = l & 15;
   const float gl = R.g[l], bl = R.beta[l];
   bf16x8 kf[CNT][DK / 32];
 #pragma unroll
@@ -266,36 +254,19 @@ __device__ __forceinline__ void produce_T_band(const ChunkArgs& a, const ChunkIn
   GT.eg[l] = __expf(Gl);
   GT.eng[l] = __expf(-Gl);
   GT.G[l] = Gl;
-  // Gram, T-form (lane (g,c) reg r: row 16I + c, column 16J + 4g + r): the diagonal
-  // tile to xr[row][4 ..], the tile left of it (its group g = 3: columns 16I - 4 ..
-  // 16I - 1) to xr[row][0 .. 3]
-#pragma unroll
-  for (int I = 0; I < CNT; ++I) {
-    f32x4 d = zero4();
-#pragma unroll
-    for (int p = 0; p < DK / 32; ++p) d = mma_bf16(kf[I][p], kf[I][p], d);
-    *reinterpret_cast<f32x4*>(&xr[16 * I + c][4 + 4 * g]) = d;
-    if (I > 0) {
-      f32x4 e = zero4();
-#pragma unroll
-      for (int p = 0; p < DK / 32; ++p) e = mma_bf16(kf[I - 1][p], kf[I][p], e);
-      if (g == 3) *reinterpret_cast<f32x4*>(&xr[16 * I + c][0]) = e;
-    }
-  }
+  float sv[4];
+  gram_band3<CNT, DK>(kf, xr, sv);
   // a_d(l) = -beta_l (k_l . k_{l-d}) exp(G_l - G_{l-d}), zero outside the chunk or band
   float ad[4];
+  ad[0] = 0.f;
+  float Gm = Gl;
 #pragma unroll
   for (int d = 1; d <= 3; ++d) {
-    const int j = l - d;
-    const float sv = xr[l][4 + c - d];
-    const float Gj = GT.G[j < 0 ? 0 : j];
-    ad[d] = (j >= 0 && d <= a.N) ? -bl * __expf(Gl - Gj) * sv : 0.f;
+    Gm = lane_shr1(Gm);
+    ad[d] = (l >= d && d <= a.N) ? -bl * __expf(Gl - Gm) * sv[d] : 0.f;
   }
-  const float a1m1 = lane_shr1(ad[1]), a1m2 = lane_shr1(a1m1), a2m1 = lane_shr1(ad[2]);
   float tv[4];
-  tv[1] = ad[1];
-  tv[2] = a.N >= 2 ? ad[2] + ad[1] * a1m1 : 0.f;
-  tv[3] = a.N >= 3 ? ad[3] + ad[1] * a2m1 + ad[2] * a1m2 + ad[1] * a1m1 * a1m2 : 0.f;
+  band3_from_subdiag(ad, a.N, tv);
   __bf16* tb = reinterpret_cast<__bf16*>(&trp[0][0][0]);
 #pragma unroll
   for (int d = 1; d <= 3; ++d)

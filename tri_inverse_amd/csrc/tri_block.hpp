@@ -280,6 +280,58 @@ __device__ __forceinline__ void ablock_to_A(const ABlock<NT>& ab, int band, Mat<
     }
 }
 
+// ---- band-masked sum with N <= 3 ([GEO] Methodologie SS2, the band mask) ---------
+// Inside the band (0 < i - j <= N) every chain i > m > ... > j of the power series has
+// at most i - j <= N steps, so there the masked truncated sum is the exact inverse, and
+// outside it T - I is zero.  With a_d(i) = A[i][i - d] (zero where i - d < 0 or d > N)
+// the band is
+//   t_1(i) = a_1(i)
+//   t_2(i) = a_2(i) + a_1(i) a_1(i-1)
+//   t_3(i) = a_3(i) + a_1(i) a_2(i-1) + a_2(i) a_1(i-2) + a_1(i) a_1(i-1) a_1(i-2),
+// formed element by element in fp32 with lane i holding row i.
+constexpr int XR_LD = 20;  // LDS row of the Gram band: 4 columns left of the tile + 16
+
+// lane i receives lane i - 1's x, lane 0 receives 0 (DPP wave_shr:1, across the rows)
+__device__ __forceinline__ float lane_shr1(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x138, 0xf, 0xf, false));
+}
+
+// ad[d] = a_d(lane) for d = 1..3 -> t[d] = t_d(lane); t_d = 0 for d > N
+__device__ __forceinline__ void band3_from_subdiag(const float (&ad)[4], int N, float (&t)[4]) {
+  const float a1m1 = lane_shr1(ad[1]), a1m2 = lane_shr1(a1m1), a2m1 = lane_shr1(ad[2]);
+  t[0] = 0.f;
+  t[1] = N >= 1 ? ad[1] : 0.f;
+  t[2] = N >= 2 ? ad[2] + ad[1] * a1m1 : 0.f;
+  t[3] = N >= 3 ? ad[3] + ad[1] * a2m1 + ad[2] * a1m2 + ad[1] * a1m1 * a1m2 : 0.f;
+}
+
+// Gram entries S[i][i - d] (d = 1..3, rows i < 16 NT) from preloaded fragments: the
+// diagonal tiles and the tile left of each in T-form (lane (g,c) reg r: row 16I + c,
+// column 16J + 4g + r; the left tile's group g = 3 holds columns 16I - 4 .. 16I - 1)
+// go to xr[row][4 ..] and xr[row][0 .. 3]; lane i then reads its row.  Entries with
+// i - d < 0 are garbage (never written) and must be discarded by the caller.
+template <int NT, int DK>
+__device__ __forceinline__ void gram_band3(const bf16x8 (&kf)[NT][DK / 32], float (&xr)[64][XR_LD],
+                                           float (&sv)[4]) {
+  const int l = lane_id(), g = l >> 4, c = l & 15;
+#pragma unroll
+  for (int I = 0; I < NT; ++I) {
+    f32x4 d = zero4();
+#pragma unroll
+    for (int p = 0; p < DK / 32; ++p) d = mma_bf16(kf[I][p], kf[I][p], d);
+    *reinterpret_cast<f32x4*>(&xr[16 * I + c][4 + 4 * g]) = d;
+    if (I > 0) {
+      f32x4 e = zero4();
+#pragma unroll
+      for (int p = 0; p < DK / 32; ++p) e = mma_bf16(kf[I - 1][p], kf[I][p], e);
+      if (g == 3) *reinterpret_cast<f32x4*>(&xr[16 * I + c][0]) = e;
+    }
+  }
+  sv[0] = 0.f;
+#pragma unroll
+  for (int d = 1; d <= 3; ++d) sv[d] = xr[l][4 + c - d];
+}
+
 // A from the Gram tiles: AD (D-form) and AT (T-form), strictly lower.  With BANDED
 // the band mask (keep i - j <= band, band < 0 = none) is applied too.  The gate factor
 // is split as exp(G_i - G_j) = exp(G_i) exp(-G_j) when every exp(-G) of the block is
