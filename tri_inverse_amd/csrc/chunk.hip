@@ -22,13 +22,15 @@
 //   waves 0, 1  state waves: each owns 16 columns of S (fp32, in registers) and runs
 //               the sequential part of a chunk: K S, Y, U' = T Y and the state update.
 //               They hand S^T (bf16) and U' (hi/lo) to the output waves.
-//   waves 7, 4, 5, 3  output waves for row tiles 0, 1, 2, 3, one chunk behind: P and
-//               O = scale (e^G Q S + P U') for their 16 rows, all 32 columns.  Tiles 1
-//               and 2 share the state waves' SIMDs, tiles 0 and 3 (the lightest and the
-//               heaviest share of the triangular P) the fourth SIMD.
-//   wave 2      gates and T of the next chunk.
-//   wave 6      copies K rows, V columns, log-gates and beta of the chunk after next
-//               into a 4-deep LDS ring.
+//   waves 2, 3, 6, 7  output waves for row tiles 0, 1, 2, 3, one chunk behind: P and
+//               O = scale (e^G Q S + P U') for their 16 rows, all 32 columns.  Tiles 0
+//               and 2 share one SIMD, tiles 1 and 3 another (equal shares of the
+//               triangular P).
+//   wave 5      gates and T of the next chunk (beside state wave 1).
+//   wave 4      copies K rows, V columns, log-gates and beta of the chunk after next
+//               into a 4-deep LDS ring (beside state wave 0).
+// The state waves, heavy on MFMA and on the sequential chain, share their SIMDs only
+// with the two light roles.
 // One barrier per chunk hands every buffer over (schedule above the kernel).  The K
 // rows sit in LDS row-major; the K^T operand of the state update comes from the same
 // rows through the LDS transpose read.  Q is read once per workgroup, each lane taking
@@ -153,7 +155,7 @@ __device__ __forceinline__ void pack8_hilo(const f32x4& a, const f32x4& b, bf16x
   lo = pack8(a - unpack_lo(hi), b - unpack_hi(hi));
 }
 
-// ---- wave 2: gates, A, T ------------------------------------------------------------
+// ---- T wave: gates, A, T -------------------------------------------------------------
 template <int DK, int MODE, int CMP, int MAXD>
 __device__ __forceinline__ void produce_T(const ChunkArgs& a, const ChunkIn<DK>& R,
                                           bf16x8 (&trp)[CNT][2][WAVE], ChunkGates& GT, Fp8Counts& cnt,
@@ -549,22 +551,22 @@ __device__ __forceinline__ void lds_barrier() {
 // Schedule: iterations it = -1 .. nchunks with one barrier at the end of each, and one
 // barrier before the loop.  Rings: raw inputs of chunk j in in[j % 4], gate factors in
 // gr[j % 3], the other products of chunk j in buf[j % 2].
-//   wave 6      it: stores chunk it+2 into in (loaded at it-1), loads chunk it+3
-//   wave 2      it: T, gates of chunk it+1  reads in         writes buf.trp, gr
+//   wave 4      it: stores chunk it+2 into in (loaded at it-1), loads chunk it+3
+//   wave 5      it: T, gates of chunk it+1  reads in         writes buf.trp, gr
 //   waves 0, 1  it: state step of chunk it  reads in, gr, buf.trp
 //                                           writes buf.st, buf.uh/ul
-//   waves 3-5, 7 it: P, O of chunk it-1     reads in, gr, buf.{st, uh, ul}
+//   waves 2, 3, 6, 7 it: P, O of chunk it-1 reads in, gr, buf.{st, uh, ul}
 // Every slot is written in one iteration and read only in later ones, and its next
 // write comes after its last read: in[j] is written at j-2, read at j-1 .. j+1 and
 // rewritten at j+2; gr[j] is read at j and j+1 and rewritten at j+2; buf[j].trp is read
 // at j and rewritten at j+1, the other buf[j] fields are read at j+1 and rewritten at
 // j+2.  In iteration it, the output waves read buf[(it-1) % 2] = buf[(it+1) % 2] while
-// wave 2 writes that buffer's trp, a field they do not touch.  Global loads are issued
+// the T wave writes that buffer's trp, a field they do not touch.  Global loads are issued
 // one iteration before their data is needed (register ping-pong, no loop-carried
 // copies, no conditional loads), so their latency overlaps a whole iteration.
-constexpr int W_STATE0 = 0, W_STATE1 = 1, W_T = 2, W_STAGE = 6;
-// output wave of row tile 0..3: tiles 1 and 2 beside the state waves, 0 and 3 together
-constexpr int W_OUT0 = 7, W_OUT1 = 4, W_OUT2 = 5, W_OUT3 = 3;
+constexpr int W_STATE0 = 0, W_STATE1 = 1, W_T = 5, W_STAGE = 4;
+// output wave of row tile 0..3
+constexpr int W_OUT0 = 2, W_OUT1 = 3, W_OUT2 = 6, W_OUT3 = 7;
 
 template <int DK, int MODE, int CMP, int MAXD, bool OBF16>
 __global__ __launch_bounds__(NWAVES * WAVE, 1) void chunk_fwd_kernel(ChunkArgs a) {
