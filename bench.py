@@ -532,7 +532,7 @@ def main():
             "tokens_per_s": h3["tokens_per_s"], "ms_per_step": h3["ms_per_step"],
             "roofline": {"bound": "hbm", "achieved": h3["bytes"] / (h3["ms_per_step"] * 1e-3) / 1e9,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": h3["hbm_frac"],
-                         "traffic": load_traffic("chunk_fwd_kernel<128,0,1,1,true>")},
+                         "traffic": load_traffic("chunk_fwd_kernel<128,16,1,1,true>")},
             "variants": c3}
     if args.only in ("all", "fs"):
         out["fs_speedup"] = bench_fs_speedup(torch, tri, synth, max(10, args.steps // 2), 3)
