@@ -186,6 +186,29 @@ def test_masked_equals_band_of_exact(N):
         np.testing.assert_allclose(H, Tm[b], rtol=0, atol=1e-15)
 
 
+@pytest.mark.parametrize("N", [1, 2, 3])
+def test_band_recurrence_from_subdiagonals(N):
+    """The band of the masked sum for N <= 3 from A's first three sub-diagonals alone
+    (every chain from i down to j has at most i - j steps), the form the chunk forward
+    evaluates element by element:
+    t1 = a1(i), t2 = a2(i) + a1(i) a1(i-1),
+    t3 = a3(i) + a1(i) a2(i-1) + a2(i) a1(i-2) + a1(i) a1(i-1) a1(i-2)."""
+    A = _rand_A(23, 5, 64)
+    Tm = oracle.neumann(A, N, True)
+    for b in range(A.shape[0]):
+        a = {d: np.array([A[b, i, i - d] if i >= d and d <= N else 0.0 for i in range(64)])
+             for d in (1, 2, 3)}
+        sh = lambda x, k: np.concatenate([np.zeros(k), x[:-k]])  # x(i - k), 0 before row 0
+        t = {1: a[1],
+             2: a[2] + a[1] * sh(a[1], 1),
+             3: a[3] + a[1] * sh(a[2], 1) + a[2] * sh(a[1], 2) + a[1] * sh(a[1], 1) * sh(a[1], 2)}
+        T = np.eye(64)
+        for d in range(1, N + 1):
+            for i in range(d, 64):
+                T[i, i - d] = t[d][i]
+        np.testing.assert_allclose(T, Tm[b], rtol=0, atol=1e-14)
+
+
 @pytest.mark.parametrize("rho", [0.25, 0.5])
 def test_correlated_keys_closed_form(rho):
     """keys with k_i.k_j = rho, beta = 1, g = 0 give A = -rho L.  Then
