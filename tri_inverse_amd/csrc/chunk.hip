@@ -26,9 +26,10 @@
 //               O = scale (e^G Q S + P U') for their 16 rows, all 32 columns.  Tiles 0
 //               and 2 share one SIMD, tiles 1 and 3 another (equal shares of the
 //               triangular P).
-//   wave 5      gates and T of the next chunk (beside state wave 1).
+//   wave 5      T of the next chunk (beside state wave 1).
 //   wave 4      copies K rows, V columns, log-gates and beta of the chunk after next
-//               into a 4-deep LDS ring (beside state wave 0).
+//               into a 4-deep LDS ring and forms that chunk's gate factors (beside
+//               state wave 0).
 // The state waves, heavy on MFMA and on the sequential chain, share their SIMDs only
 // with the two light roles.
 // One barrier per chunk hands every buffer over (schedule above the kernel).  The K
@@ -155,32 +156,43 @@ __device__ __forceinline__ void pack8_hilo(const f32x4& a, const f32x4& b, bf16x
   lo = pack8(a - unpack_lo(hi), b - unpack_hi(hi));
 }
 
-// ---- T wave: gates, A, T -------------------------------------------------------------
+// Gate factors of one chunk from its raw log-gates and beta (lane l = position l),
+// formed by the stager as it stages the chunk: G = in-chunk cumsum by the wave scan.
+__device__ __forceinline__ void write_gates(float gl, float bl, ChunkGates& GT) {
+  const int l = lane_id();
+  const float Gl = wave_inclusive_scan(gl);
+  const bool split = wave_min(Gl) >= -80.f;
+  GT.beta[l] = bl;
+  GT.eg[l] = __expf(Gl);
+  GT.eng[l] = __expf(-Gl);
+  GT.G[l] = Gl;
+  const float GC = readlane_f(Gl, CH - 1);
+  GT.egcg[l] = __expf(GC - Gl);
+  if (l == 0) {
+    GT.egc = __expf(GC);
+    GT.split = split ? 1 : 0;
+  }
+}
+
+// ---- T wave: A, T ---------------------------------------------------------------------
 template <int DK, int MODE, int CMP, int MAXD>
 __device__ __forceinline__ void produce_T(const ChunkArgs& a, const ChunkIn<DK>& R,
-                                          bf16x8 (&trp)[CNT][2][WAVE], ChunkGates& GT, Fp8Counts& cnt,
+                                          bf16x8 (&trp)[CNT][2][WAVE], const ChunkGates& GT, Fp8Counts& cnt,
                                           bool count) {
   const int l = lane_id(), c = l & 15;
-  const float gl = R.g[l], bl = R.beta[l];
+  const float bl = R.beta[l];
   KBlock<CNT, DK> kb;
 #pragma unroll
   for (int I = 0; I < CNT; ++I)
 #pragma unroll
     for (int p = 0; p < DK / 32; ++p) kb.kf[I][p] = rowfrag_nat<DK>(R, 16 * I + c, p);  // K K^T: any common d order
-  kb.gl = gl;
-  kb.bl = bl;
-  // Gates: G by the wave scan.  The per-position factors go to GT first (the other
-  // waves read them there anyway); the D-form row factors are read back with one
-  // 16-byte LDS read per tile and factor instead of a lane gather per value.
+  // Gates (formed by the stager): the per-position factors from GT, the D-form row
+  // factors with one 16-byte LDS read per tile and factor.
   Gates<CNT> gt;
-  gt.Gl = wave_inclusive_scan(gl);
+  gt.Gl = GT.G[l];
   gt.bl = bl;
-  gt.split = wave_min(gt.Gl) >= -80.f;
-  const float egl = __expf(gt.Gl), engl = __expf(-gt.Gl);
-  GT.beta[l] = bl;
-  GT.eg[l] = egl;
-  GT.eng[l] = engl;
-  GT.G[l] = gt.Gl;
+  gt.split = GT.split != 0;
+  const float egl = GT.eg[l], engl = GT.eng[l];
   {
     const int g4 = 4 * (l >> 4);
     float rb[4], nb[4];
@@ -218,12 +230,6 @@ __device__ __forceinline__ void produce_T(const ChunkArgs& a, const ChunkIn<DK>&
     for (int p = 0; p < 2; ++p)
       if (2 * p <= I && I - (2 * p + 1) <= MAXD)
         trp[I][p][l] = pack8(tile_or_zero(TT, I, 2 * p), tile_or_zero(TT, I, 2 * p + 1));
-  const float GC = readlane_f(gt.Gl, CH - 1);
-  GT.egcg[l] = __expf(GC - gt.Gl);
-  if (l == 0) {
-    GT.egc = __expf(GC);
-    GT.split = gt.split ? 1 : 0;
-  }
 }
 
 // Band-masked sum with N <= 3: the band of T - I by band3_from_subdiag (lane i = row
@@ -241,21 +247,16 @@ __device__ __forceinline__ int trp_slot(int i, int j) {
 
 template <int DK>
 __device__ __forceinline__ void produce_T_band(const ChunkArgs& a, const ChunkIn<DK>& R,
-                                               bf16x8 (&trp)[CNT][2][WAVE], ChunkGates& GT,
+                                               bf16x8 (&trp)[CNT][2][WAVE], const ChunkGates& GT,
                                                float (&xr)[CH][XR_LD]) {
   const int l = lane_id(), c = l & 15;
-  const float gl = R.g[l], bl = R.beta[l];
+  const float bl = R.beta[l];
   bf16x8 kf[CNT][DK / 32];
 #pragma unroll
   for (int I = 0; I < CNT; ++I)
 #pragma unroll
     for (int p = 0; p < DK / 32; ++p) kf[I][p] = rowfrag_nat<DK>(R, 16 * I + c, p);
-  const float Gl = wave_inclusive_scan(gl);
-  const bool split = wave_min(Gl) >= -80.f;
-  GT.beta[l] = bl;
-  GT.eg[l] = __expf(Gl);
-  GT.eng[l] = __expf(-Gl);
-  GT.G[l] = Gl;
+  const float Gl = GT.G[l];  // the gates were formed by the stager
   float sv[4];
   gram_band3<CNT, DK>(kf, xr, sv);
   // a_d(l) = -beta_l (k_l . k_{l-d}) exp(G_l - G_{l-d}), zero outside the chunk or band
@@ -273,12 +274,6 @@ __device__ __forceinline__ void produce_T_band(const ChunkArgs& a, const ChunkIn
 #pragma unroll
   for (int d = 1; d <= 3; ++d)
     if (l - d >= 0) tb[trp_slot(l, l - d)] = (__bf16)tv[d];
-  const float GC = readlane_f(Gl, CH - 1);
-  GT.egcg[l] = __expf(GC - Gl);
-  if (l == 0) {
-    GT.egc = __expf(GC);
-    GT.split = split ? 1 : 0;
-  }
 }
 
 // ---- waves 0, 1: the state scan -------------------------------------------------------
@@ -550,15 +545,16 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Schedule: iterations it = -1 .. nchunks with one barrier at the end of each, and one
 // barrier before the loop.  Rings: raw inputs of chunk j in in[j % 4], gate factors in
-// gr[j % 3], the other products of chunk j in buf[j % 2].
-//   wave 4      it: stores chunk it+2 into in (loaded at it-1), loads chunk it+3
-//   wave 5      it: T, gates of chunk it+1  reads in         writes buf.trp, gr
+// gr[j % 4], the other products of chunk j in buf[j % 2].
+//   wave 4      it: stores chunk it+2 into in and its gate factors into gr (loaded at
+//               it-1), loads chunk it+3
+//   wave 5      it: T of chunk it+1         reads in, gr     writes buf.trp
 //   waves 0, 1  it: state step of chunk it  reads in, gr, buf.trp
 //                                           writes buf.st, buf.uh/ul
 //   waves 2, 3, 6, 7 it: P, O of chunk it-1 reads in, gr, buf.{st, uh, ul}
 // Every slot is written in one iteration and read only in later ones, and its next
-// write comes after its last read: in[j] is written at j-2, read at j-1 .. j+1 and
-// rewritten at j+2; gr[j] is read at j and j+1 and rewritten at j+2; buf[j].trp is read
+// write comes after its last read: in[j] and gr[j] are written at j-2, read at
+// j-1 .. j+1 and rewritten at j+2; buf[j].trp is read
 // at j and rewritten at j+1, the other buf[j] fields are read at j+1 and rewritten at
 // j+2.  In iteration it, the output waves read buf[(it-1) % 2] = buf[(it+1) % 2] while
 // the T wave writes that buffer's trp, a field they do not touch.  Global loads are issued
@@ -571,7 +567,7 @@ constexpr int W_OUT0 = 2, W_OUT1 = 3, W_OUT2 = 6, W_OUT3 = 7;
 template <int DK, int MODE, int CMP, int MAXD, bool OBF16>
 __global__ __launch_bounds__(NWAVES * WAVE, 1) void chunk_fwd_kernel(ChunkArgs a) {
   __shared__ ChunkIn<DK> in[4];
-  __shared__ ChunkGates gr[3];
+  __shared__ ChunkGates gr[4];
   __shared__ ChunkBuf<DK> buf[2];
   __shared__ float xr[CH][XR_LD];  // Gram band rows (band mode, T wave only)
   // wave index as a uniform (scalar) value: role branches and loop counters stay scalar
@@ -631,16 +627,23 @@ __global__ __launch_bounds__(NWAVES * WAVE, 1) void chunk_fwd_kernel(ChunkArgs a
     load(0, r0);
     load(clampc(1), r1);
     store(r0, in[0]);
+    write_gates(r0.g, r0.b, gr[0]);
     lds_barrier();
     for (int it = -1; it <= nchunks; it += 2) {
       // iteration it (odd): chunk it+3 (even) -> r0, chunk it+2 (odd) r1 -> LDS
       load(clampc(it + 3), r0);
-      if (it + 2 < nchunks) store(r1, ring(in, (it + 2) & 3));
+      if (it + 2 < nchunks) {
+        store(r1, ring(in, (it + 2) & 3));
+        write_gates(r1.g, r1.b, ring(gr, (it + 2) & 3));
+      }
       lds_barrier();
       if (it + 1 > nchunks) break;
       // iteration it+1 (even): chunk it+4 (odd) -> r1, chunk it+3 (even) r0 -> LDS
       load(clampc(it + 4), r1);
-      if (it + 3 < nchunks) store(r0, ring(in, (it + 3) & 3));
+      if (it + 3 < nchunks) {
+        store(r0, ring(in, (it + 3) & 3));
+        write_gates(r0.g, r0.b, ring(gr, (it + 3) & 3));
+      }
       lds_barrier();
     }
     return;
@@ -665,9 +668,9 @@ __global__ __launch_bounds__(NWAVES * WAVE, 1) void chunk_fwd_kernel(ChunkArgs a
       const int ch = it + 1;
       if (ch < nchunks) {
         if constexpr (MODE == MODE_BAND)
-          produce_T_band<DK>(a, ring(in, ch & 3), ring(buf, ch & 1).trp, ring(gr, ch % 3), xr);
+          produce_T_band<DK>(a, ring(in, ch & 3), ring(buf, ch & 1).trp, ring(gr, ch & 3), xr);
         else
-          produce_T<DK, MODE, CMP, MAXD>(a, ring(in, ch & 3), ring(buf, ch & 1).trp, ring(gr, ch % 3), cnt,
+          produce_T<DK, MODE, CMP, MAXD>(a, ring(in, ch & 3), ring(buf, ch & 1).trp, ring(gr, ch & 3), cnt,
                                          count);
       }
       lds_barrier();
@@ -703,7 +706,7 @@ __global__ __launch_bounds__(NWAVES * WAVE, 1) void chunk_fwd_kernel(ChunkArgs a
           for (int p = 0; p < DK / 32; ++p) kr[J][p] = rowfrag_nat<DK>(R, 16 * J + c, p);
       };
       auto work = [&](int ch, const bf16x8 (&q)[1][DK / 32]) {
-        emit_rows<DK, 1, I0, I0, OBF16>(a, head_row0 + (int64_t)ch * CH, slice * DVS, kr, ring(gr, ch % 3),
+        emit_rows<DK, 1, I0, I0, OBF16>(a, head_row0 + (int64_t)ch * CH, slice * DVS, kr, ring(gr, ch & 3),
                                         ring(buf, ch & 1), q);
       };
       lds_barrier();
@@ -753,7 +756,7 @@ __global__ __launch_bounds__(NWAVES * WAVE, 1) void chunk_fwd_kernel(ChunkArgs a
     // the next chunk's slot: staged one iteration earlier, rewritten three later (past
     // the end it holds stale rows, read but never used)
     if (it >= 0 && it < nchunks)
-      sw.step(ring(in, it & 3), ring(in, (it + 1) & 3), ring(gr, it % 3), ring(buf, it & 1), v);
+      sw.step(ring(in, it & 3), ring(in, (it + 1) & 3), ring(gr, it & 3), ring(buf, it & 1), v);
     lds_barrier();
   }
 #pragma unroll
