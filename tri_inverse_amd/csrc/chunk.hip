@@ -649,9 +649,9 @@ __global__ __launch_bounds__(NWAVES * WAVE, 1) void chunk_fwd_kernel(ChunkArgs a
     return;
   }
   if (wave == W_T) {
-    // issue priority on the shared SIMD: the T wave above state wave 1 (it is the last
-    // to reach the barrier otherwise); the state waves above the stager
-    __builtin_amdgcn_s_setprio(3);
+    // issue priority on the shared SIMDs: the T wave level with state wave 1, the
+    // state waves above the stager
+    __builtin_amdgcn_s_setprio(2);
     Fp8Counts cnt{0, 0, 0, 0};
     const bool count = (CMP == CMP_FP8) && a.stats != nullptr;
     if constexpr (MODE == MODE_BAND) {
