@@ -586,6 +586,7 @@ __global__ __launch_bounds__(NWAVES * WAVE, 1) void chunk_fwd_kernel(ChunkArgs a
   const int last = nchunks - 1;  // >= 0: the launcher is never called with T = 0
 
   if (wave == W_STAGE) {
+    __builtin_amdgcn_s_setprio(1);
     // K: the chunk's rows are contiguous, 16 bytes per lane and instruction; V: this
     // workgroup's 32 columns (64 bytes) of each row, 4 lanes per row
     constexpr int SEG = DK / 8;
@@ -650,7 +651,7 @@ __global__ __launch_bounds__(NWAVES * WAVE, 1) void chunk_fwd_kernel(ChunkArgs a
   }
   if (wave == W_T) {
     // issue priority on the shared SIMDs: the T wave level with state wave 1, the
-    // state waves above the stager
+    // stager one level below state wave 0 (it mostly waits on its loads)
     __builtin_amdgcn_s_setprio(2);
     Fp8Counts cnt{0, 0, 0, 0};
     const bool count = (CMP == CMP_FP8) && a.stats != nullptr;
