@@ -166,6 +166,21 @@ def test_chunk_fwd_special_cases():
     assert O0.shape == (B, H, 0, dv)
 
 
+@pytest.mark.parametrize("T", [64, 192])
+@pytest.mark.parametrize("N,mask", [(3, True), (3, False)])
+def test_chunk_fwd_short_sequences(T, N, mask):
+    """One and three chunks: the staging, gate and product rings run their first and
+    last iterations back to back."""
+    B, H, dk, dv = 1, 2, 128, 128
+    say(f"chunk fwd T={T} N={N} mask={mask}")
+    x, x64 = _chunk_case(17, B, H, T, dk, dv)
+    O, S = _run_chunk(x, C=64, scale=dk ** -0.5, N=N, mask=mask, o_dtype=torch.float32)
+    Or, Sr = oracle.chunk_fwd(x64["Q"], x64["K"], x64["V"], x64["beta"], x64["g"], 64, dk ** -0.5,
+                              N=N, mask=mask)
+    assert relF(O, Or) <= TOL["bf16"], relF(O, Or)
+    assert relF(S, Sr) <= TOL["bf16"], relF(S, Sr)
+
+
 @pytest.mark.parametrize("N,mask", [(3, True), (3, False)])
 def test_chunk_fwd_strong_gates(N, mask):
     """Log-gates near -2.6 per token: G falls below -80 inside every chunk, so exp(-G)
