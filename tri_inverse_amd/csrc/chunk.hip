@@ -334,6 +334,7 @@ struct StateWave {
       b4[I] = b4n[I];
       e4[I] = *reinterpret_cast<const f32x4*>(&GT.eg[16 * I + 4 * g]);
     }
+    const float egc = GT.egc;
     __builtin_amdgcn_sched_barrier(0);
     // S as bf16: column packs for K S here (slot t <-> d = 32p + 8g + t), which are
     // also S^T rows (8 consecutive d per lane) for the output waves
@@ -351,6 +352,9 @@ struct StateWave {
     for (int p = 0; p < NP; ++p)
 #pragma unroll
       for (int I = 0; I < CNT; ++I) ks[I] = mma_bf16(kf[I][p], cps[p], ks[I]);
+    // e^{G_C} S while the K S products run (S itself is free once packed)
+#pragma unroll
+    for (int A = 0; A < NA; ++A) S[A] = S[A] * egc;
     __builtin_amdgcn_sched_barrier(0);
     // batch 2: T row packs, e^{G_C - G}, e^{G_C}, K^T packs
     bf16x8 tf[CNT][2];
@@ -362,7 +366,6 @@ struct StateWave {
     f32x4 w4[CNT];
 #pragma unroll
     for (int I = 0; I < CNT; ++I) w4[I] = *reinterpret_cast<const f32x4*>(&GT.egcg[16 * I + 4 * g]);
-    const float egc = GT.egc;
     bf16x8 kt[NA][2];
 #pragma unroll
     for (int A = 0; A < NA; ++A)
@@ -396,8 +399,6 @@ struct StateWave {
     bf16x8 cth[2], ctl[2];
     pack8_hilo(ut[0], ut[1], cth[0], ctl[0]);
     pack8_hilo(ut[2], ut[3], cth[1], ctl[1]);
-#pragma unroll
-    for (int A = 0; A < NA; ++A) S[A] = S[A] * egc;
 #pragma unroll
     for (int p = 0; p < 2; ++p)
 #pragma unroll
