@@ -29,6 +29,7 @@ _lib = None
 INV_NEUMANN = 0
 INV_EXACT = 1
 INV_FS = 2
+INV_FP8 = 3
 
 
 def build(force: bool = True) -> str:
@@ -60,12 +61,16 @@ def _load():
     lib.oracle_neumann.argtypes = [i64, i32, P, i32, i32, P]
     lib.oracle_doubling.argtypes = [i64, i32, P, P]
     lib.oracle_neumann_int8.argtypes = [i64, i32, P, i32, i32, P]
+    U64P = ctypes.POINTER(ctypes.c_uint64)
+    lib.oracle_neumann_fp8.argtypes = [i64, i32, P, i32, i32, P, U64P, P]
+    lib.oracle_e4m3_round.argtypes = [i64, P, P]
     lib.oracle_residual.argtypes = [i64, i32, P, i32, i32, i32, P]
     lib.oracle_wy.argtypes = [i64, i32, i32, i32, P, P, P, P, P, i32, i32, P, P]
     lib.oracle_chunk_fwd.argtypes = [i32, i32, i64, i32, i32, i32, P, P, P, P, P, P, f64,
                                      i32, i32, i32, P, P]
     lib.oracle_recurrence.argtypes = [i32, i32, i64, i32, i32, P, P, P, P, P, P, f64, P, P]
     for fn in ("oracle_build_A", "oracle_fs_inverse", "oracle_neumann", "oracle_neumann_int8",
+               "oracle_neumann_fp8", "oracle_e4m3_round",
                "oracle_doubling",
                "oracle_residual", "oracle_wy", "oracle_chunk_fwd", "oracle_recurrence",
                "oracle_set_threads"):
@@ -129,6 +134,29 @@ def neumann_int8(A, N: int, mask: bool) -> np.ndarray:
     T = np.empty_like(A)
     _load().oracle_neumann_int8(nb, C, _ptr(A), int(N), int(bool(mask)), _ptr(T))
     return T
+
+
+def e4m3_round(y) -> np.ndarray:
+    """Nearest OCP e4m3 value of each element (|y| <= 448), ties to the even code."""
+    y = _f64(y)
+    q = np.empty_like(y)
+    _load().oracle_e4m3_round(y.size, _ptr(y), _ptr(q))
+    return q
+
+
+def neumann_fp8(A, N: int, mask: bool):
+    """The Horner chain on fp8 e4m3 operands with per-block absmax/448 scales ([GEO]
+    "Adaptation a la Quantification"; reading in gdn_oracle.c).  A holds fp32 values.
+    Returns (T [nb,C,C], counts [nb,4] uint64: non-finite, dynamic-scale saturations,
+    static-scale saturations, underflows; amax [nb,N+1]: absmax of A, X_1..X_{N-1}, X_N)."""
+    A = _f64(A)
+    nb, C, _ = A.shape
+    T = np.empty_like(A)
+    counts = np.zeros((nb, 4), dtype=np.uint64)
+    amax = np.zeros((nb, int(N) + 1))
+    _load().oracle_neumann_fp8(nb, C, _ptr(A), int(N), int(bool(mask)), _ptr(T),
+                               counts.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), _ptr(amax))
+    return T, counts, amax
 
 
 def doubling(A) -> np.ndarray:

@@ -240,6 +240,167 @@ void oracle_neumann_int8(int64_t nb, int C, const double* A, int N, int mask, do
   }
 }
 
+/* ---- a8: the power chain on fp8 (OCP e4m3) operands --------------------------
+ * [GEO] "Adaptation a la Quantification": the power chain of Methodologie SS1 runs on
+ * low-bit operands, and the mask of SS2 exists to keep the intermediates inside their
+ * range.  The pages name no fp8 format, scaling or rounding rule; the reading taken:
+ *   - e4m3 is the OCP 8-bit float: sign, 4 exponent bits (bias 7), 3 mantissa bits,
+ *     subnormals m 2^-9, largest finite value 448, no infinity.  A value is rounded to
+ *     the nearest e4m3 value, ties to the value whose code is even; it is clamped to
+ *     +-448 first, so nothing becomes NaN (a NaN input is clamped to -448).
+ *   - Each quantised tensor of a block gets one scale s = absmax / 448 (1 for an
+ *     all-zero or non-finite absmax).  The code of x is e4m3(clamp(x * (1 / s))).  The
+ *     scale, its reciprocal and the product are fp32 operations (the working
+ *     precision of the kernel's scalars); here they are written as C float arithmetic,
+ *     which is IEEE single precision with correct rounding.
+ *   - Horner runs on X = H - I, so that the identity never enters a quantised tensor
+ *     (its 1s would otherwise set the scales and sit on the diagonal of every operand):
+ *       A' = s_A q(A),  X_1 = A',  X_{k+1} = A' + s_A s_X (q(A) q(X_k))  (k < N),
+ *       T = I + s_T q(X_N)   (N >= 2),   T = I + A'   (N = 1).
+ *     The product of codes is exact; it is rounded once to fp32 (the accumulator),
+ *     multiplied by s_A s_X and added to A' with one rounding (a fused multiply-add).
+ *   - With mask != 0, A and every X_{k+1} are band-masked (i - j <= N) before they are
+ *     quantised, so out-of-band values never set a scale.
+ *   - Counters over every quantised tensor Y of the chain (A; the right operands X_1 ..
+ *     X_{N-1}; X_N for N >= 2), with its own scale s_Y and the static scale s_A:
+ *       [0] non-finite values;  [1] |x| (1 / s_Y) >= 464 (a saturation under the dynamic
+ *       scale: 464 is the rounding boundary between 448 and the next step, 480, of
+ *       that binade);  [2] |x| (1 / s_A) >= 464 (a saturation had A's scale been used
+ *       for every power: the fixed-range regime the mask is meant for);
+ *       [3] x != 0 with |x| (1 / s_Y) <= 2^-10 (rounds to zero: half the smallest
+ *       subnormal rounds to the even code 0).
+ * Every value returned is an fp32 value, given in fp64. */
+
+/* nearest e4m3 value to y (|y| <= 448), ties to the even code.  Inside the binade
+ * [2^E, 2^(E+1)) (E >= -6; below 2^-6 the subnormals continue the step of E = -6) the
+ * values are the multiples k 2^(E-3), k = 8..15, and the code's last bit is k's, so
+ * rounding to the nearest multiple with ties to even k is rounding to the even code
+ * (k = 16 is the first value of the next binade, code mantissa 0). */
+static double e4m3_round(double y) {
+  const double a = fabs(y);
+  if (a == 0.0) return 0.0;
+  int e;
+  (void)frexp(a, &e); /* a = m 2^e, m in [0.5, 1): the binade is E = e - 1 */
+  int E = e - 1;
+  if (E < -6) E = -6;
+  const double step = ldexp(1.0, E - 3);
+  return copysign(nearbyint(a / step) * step, y);
+}
+
+/* element-wise e4m3 rounding, exposed for the tests */
+void oracle_e4m3_round(int64_t n, const double* y, double* q) {
+  for (int64_t i = 0; i < n; ++i) q[i] = e4m3_round(y[i]);
+}
+
+static float fp8_block_scale(float amax) {
+  return (amax > 0.0f && isfinite(amax)) ? amax / 448.0f : 1.0f;
+}
+
+static float fp8_absmax(int n, const float* X) {
+  float m = 0.0f;
+  for (int i = 0; i < n; ++i)
+    if (fabsf(X[i]) > m) m = fabsf(X[i]); /* a NaN never becomes the maximum */
+  return m;
+}
+
+/* value of the e4m3 code of x under the reciprocal scale inv (before scaling back) */
+static double fp8_code_value(float x, float inv) {
+  float y = x * inv;
+  y = fminf(fmaxf(y, -448.0f), 448.0f);
+  return e4m3_round((double)y);
+}
+
+static void fp8_count_tensor(int n, const float* X, float s, float s_static, uint64_t* cnt) {
+  const float inv = 1.0f / s, inv_st = 1.0f / s_static;
+  for (int i = 0; i < n; ++i) {
+    const float x = X[i];
+    if (!isfinite(x)) {
+      cnt[0]++;
+      continue;
+    }
+    const float a = fabsf(x);
+    if (a * inv >= 464.0f) cnt[1]++;
+    if (a * inv_st >= 464.0f) cnt[2]++;
+    if (x != 0.0f && a * inv <= 0x1p-10f) cnt[3]++;
+  }
+}
+
+static void band_mask_f(int C, int N, float* X) {
+  for (int i = 0; i < C; ++i)
+    for (int j = 0; j < C; ++j)
+      if (i - j > N) X[(size_t)i * C + j] = 0.0f;
+}
+
+/* A: [nb][C][C] fp32 values (strictly lower part read).  T: [nb][C][C].
+ * counts: [nb][4] per-block counters (NULL: not returned).
+ * amax: [nb][N + 1] absmax of A, of X_1 .. X_{N-1} and of X_N before its quantisation
+ * (for N = 1 the second entry is that of A'), NULL: not returned.  1 <= N < C. */
+void oracle_neumann_fp8(int64_t nb, int C, const double* A, int N, int mask, double* T,
+                        uint64_t* counts, double* amax) {
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < nb; ++b) {
+    const size_t CC = (size_t)C * C;
+    float* Af = (float*)malloc(sizeof(float) * CC);
+    float* Ad = (float*)malloc(sizeof(float) * CC); /* A' */
+    float* X = (float*)malloc(sizeof(float) * CC);
+    float* Xn = (float*)malloc(sizeof(float) * CC);
+    double* qa = (double*)malloc(sizeof(double) * CC);
+    double* qx = (double*)malloc(sizeof(double) * CC);
+    uint64_t cnt[4] = {0, 0, 0, 0};
+    double* am = amax ? amax + (size_t)b * (N + 1) : NULL;
+    for (int i = 0; i < C; ++i)
+      for (int j = 0; j < C; ++j)
+        Af[(size_t)i * C + j] = (i > j) ? (float)A[(size_t)b * CC + (size_t)i * C + j] : 0.0f;
+    if (mask) band_mask_f(C, N, Af);
+    const float mA = fp8_absmax((int)CC, Af), sA = fp8_block_scale(mA);
+    if (am) am[0] = mA;
+    fp8_count_tensor((int)CC, Af, sA, sA, cnt);
+    const float invA = 1.0f / sA;
+    for (size_t e = 0; e < CC; ++e) {
+      qa[e] = fp8_code_value(Af[e], invA);
+      Ad[e] = (float)qa[e] * sA;
+    }
+    memcpy(X, Ad, sizeof(float) * CC); /* X_1 = A' */
+    if (N >= 2) {
+      for (int k = 1; k < N; ++k) {
+        const float mX = fp8_absmax((int)CC, X), sX = fp8_block_scale(mX);
+        if (am) am[k] = mX;
+        fp8_count_tensor((int)CC, X, sX, sA, cnt);
+        const float invX = 1.0f / sX, sxy = sA * sX;
+        for (size_t e = 0; e < CC; ++e) qx[e] = fp8_code_value(X[e], invX);
+        for (int i = 0; i < C; ++i)
+          for (int j = 0; j < C; ++j) {
+            double p = 0.0; /* products of e4m3 values are exact, and so is this sum */
+            for (int m = 0; m < C; ++m) p += qa[(size_t)i * C + m] * qx[(size_t)m * C + j];
+            Xn[(size_t)i * C + j] = fmaf((float)p, sxy, Ad[(size_t)i * C + j]);
+          }
+        if (mask) band_mask_f(C, N, Xn);
+        memcpy(X, Xn, sizeof(float) * CC);
+      }
+      /* T - I = X_N, quantised with its own scale */
+      const float mT = fp8_absmax((int)CC, X), sT = fp8_block_scale(mT);
+      if (am) am[N] = mT;
+      fp8_count_tensor((int)CC, X, sT, sA, cnt);
+      const float invT = 1.0f / sT;
+      for (size_t e = 0; e < CC; ++e) X[e] = (float)fp8_code_value(X[e], invT) * sT;
+    } else if (am) {
+      am[1] = fp8_absmax((int)CC, Ad); /* N = 1: T - I = A' */
+    }
+    double* Tb = T + (size_t)b * CC;
+    for (int i = 0; i < C; ++i)
+      for (int j = 0; j < C; ++j)
+        Tb[(size_t)i * C + j] = (double)X[(size_t)i * C + j] + (i == j ? 1.0 : 0.0);
+    if (counts)
+      for (int q = 0; q < 4; ++q) counts[(size_t)b * 4 + q] = cnt[q];
+    free(Af);
+    free(Ad);
+    free(X);
+    free(Xn);
+    free(qa);
+    free(qx);
+  }
+}
+
 /* ---- O5: exact multiplication-only doubling product --------------------------
  * T = prod_{i=0}^{m-1} (I + A^(2^i)),  m = ceil(log2 C).
  * Valid because A is nilpotent: by Lemma 3.1 of [GEO] (Methodologie SS1), A^n is
@@ -359,7 +520,9 @@ void oracle_wy(int64_t nb, int C, int dk, int dv, const double* T, const double*
 /* inverse of one block by the selected variant (see the functions above) */
 static void block_inverse(int C, const double* A, int inv_mode, int N, int mask,
                           double* T) {
-  if (inv_mode == 1)
+  if (inv_mode == 3)
+    oracle_neumann_fp8(1, C, A, N, mask, T, NULL, NULL);
+  else if (inv_mode == 1)
     oracle_doubling(1, C, A, T);
   else if (inv_mode == 2)
     oracle_fs_inverse(1, C, A, T);
@@ -378,7 +541,8 @@ static void block_inverse(int C, const double* A, int inv_mode, int N, int mask,
  * [GEO] Enonce du Probleme: the chunk-wise form needs T = (I - A)^-1 per chunk and
  * keeps a fixed-size recurrent state across chunks.
  * inv_mode: 0 = truncated Neumann (N, mask), 1 = exact doubling, 2 = forward
- * substitution.  Layouts: Q, K [B][H][Tn][dk]; V, O [B][H][Tn][dv];
+ * substitution, 3 = the truncated Neumann chain on fp8 e4m3 operands (N, mask; A is
+ * rounded to fp32 first, the precision in which the GPU forms it).  Layouts: Q, K [B][H][Tn][dk]; V, O [B][H][Tn][dv];
  * beta, g [B][H][Tn]; S0, S_out [B][H][dk][dv].  Tn % C == 0. */
 void oracle_chunk_fwd(int Bn, int Hn, int64_t Tn, int dk, int dv, int C, const double* Q,
                       const double* K, const double* V, const double* beta,

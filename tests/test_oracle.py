@@ -458,3 +458,119 @@ def test_int8_chain_close_to_fp64_on_c1_inputs():
     assert _relF(T8 - I, Tf - I) < 2e-2
     assert np.all(np.diagonal(T8, axis1=1, axis2=2) == 1.0)
     assert np.all(np.triu(T8, 1) == 0.0)
+
+
+# ---------------------------------------------------------------- fp8 (e4m3) chain
+# [GEO] "Adaptation a la Quantification" runs the power chain on low-bit operands; the
+# e4m3 reading (format, rounding, scales, counters) is stated in oracle/gdn_oracle.c.
+# These pins are independent of the oracle's arithmetic: the e4m3 value set is decoded
+# from the bit layout and searched exhaustively, and the chain is checked on
+# A = -(7/16) L, whose scales are powers of two, against closed forms derived by hand.
+
+def _e4m3_table():
+    """All finite non-negative e4m3 values with their codes, decoded from the bits
+    (sign | 4 exponent bits, bias 7 | 3 mantissa bits; code 0x7f is NaN)."""
+    vals, codes = [], []
+    for code in range(0x7f):
+        e, m = code >> 3, code & 7
+        vals.append(m / 8 * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+        codes.append(code)
+    return np.array(vals), np.array(codes)
+
+
+def _e4m3_nearest(y):
+    """Exhaustive nearest e4m3 value, ties to the even code."""
+    vals, codes = _e4m3_table()
+    y = np.asarray(y, dtype=np.float64)
+    d = np.abs(np.abs(y)[..., None] - vals)
+    dmin = d.min(axis=-1, keepdims=True)
+    # among the nearest, prefer the even code (there are at most two candidates)
+    score = np.where(d == dmin, (codes & 1).astype(np.float64), np.inf)
+    pick = vals[np.argmin(score, axis=-1)]
+    return np.copysign(pick, y)
+
+
+def test_e4m3_value_set_and_rounding_match_the_code_table():
+    vals, _ = _e4m3_table()
+    assert vals.max() == 448.0 and vals[1] == 2.0 ** -9 and len(np.unique(vals)) == 127
+    # every representable value rounds to itself
+    np.testing.assert_array_equal(oracle.e4m3_round(vals), vals)
+    np.testing.assert_array_equal(oracle.e4m3_round(-vals), -vals)
+    # midpoints between neighbours are ties: they go to the even code
+    mids = (vals[1:] + vals[:-1]) / 2
+    np.testing.assert_array_equal(oracle.e4m3_round(mids), _e4m3_nearest(mids))
+    rng = np.random.default_rng(7)
+    y = np.sign(rng.standard_normal(20000)) * np.exp(rng.uniform(np.log(2.0 ** -12), np.log(448.0), 20000))
+    np.testing.assert_array_equal(oracle.e4m3_round(y), _e4m3_nearest(y))
+    # hand values: 2^-10 is half the smallest subnormal (tie -> code 0); 1.0625 lies
+    # between 1 (code 0x38) and 1.125 (0x39): tie -> 1; 17 -> 16 (0x58) over 18 (0x59)
+    np.testing.assert_array_equal(oracle.e4m3_round([2.0 ** -10, 1.5 * 2.0 ** -10, 1.0625, 1.1875, -17.0]),
+                                  [0.0, 2.0 ** -9, 1.0, 1.25, -16.0])
+
+
+def _rho_L(C, rho):
+    return (-rho * np.tril(np.ones((C, C)), -1))[None]
+
+
+def _f32_quant_dequant(x, s):
+    """s * e4m3(clamp(x * (1/s))) with every scalar step in fp32 (the stated reading)."""
+    s = np.float32(s)
+    inv = np.float32(1.0) / s
+    y = (np.asarray(x, dtype=np.float32) * inv).astype(np.float32)
+    y = np.clip(y, np.float32(-448), np.float32(448))
+    return (_e4m3_nearest(y).astype(np.float32) * s).astype(np.float32)
+
+
+def test_fp8_chain_closed_form_rho_7_16():
+    """A = -(7/16) L (L strictly lower, all ones), C = 64.  absmax(A) = 7/16 = 448 2^-10, so
+    s_A = 2^-10, every code of A is -448 and A' = A.  X_1 = A', so its codes are -448 too,
+    and the first product is exact: X_2(d) = -7/16 + (49/256)(d - 1) on subdiagonal d.
+    Static saturations of X_2: |X_2| 2^10 >= 464 iff d >= 6, i.e. sum_{d=6}^{63}(64 - d)
+    = 1711 entries; the mask (N = 2) keeps d <= 2, where |X_2| <= 7/16: none."""
+    C = 64
+    A = _rho_L(C, 7 / 16)
+    d = np.subtract.outer(np.arange(C), np.arange(C))
+    x2 = np.where(d >= 1, -7 / 16 + 49 / 256 * (d - 1), 0.0)
+    # N = 1: T = I + A' = I + A (A is exactly representable)
+    T, cnt, am = oracle.neumann_fp8(A, 1, False)
+    np.testing.assert_array_equal(T[0], np.eye(C) + A[0])
+    np.testing.assert_array_equal(cnt[0], [0, 0, 0, 0])
+    # N = 2, unmasked: T - I = s_T e4m3(X_2 / s_T), s_T = absmax(X_2) / 448
+    T, cnt, am = oracle.neumann_fp8(A, 2, False)
+    assert am[0].tolist() == [7 / 16, 7 / 16, -7 / 16 + 49 / 256 * 62]
+    sT = np.float32(np.float32(am[0][2]) / np.float32(448.0))
+    np.testing.assert_array_equal(T[0], np.eye(C) + _f32_quant_dequant(x2, sT))
+    np.testing.assert_array_equal(cnt[0], [0, 0, 1711, 0])
+    # N = 2, masked: band d <= 2 of X_2 = {-7/16, -63/256}; s_T = 2^-10 again, and
+    # -63/256 * 2^10 = -252 rounds to -256 (step 16 in [128, 256)): T - I = -1/4 there
+    T, cnt, _ = oracle.neumann_fp8(A, 2, True)
+    expect = np.where(d == 1, -7 / 16, np.where(d == 2, -0.25, 0.0))
+    np.testing.assert_array_equal(T[0], np.eye(C) + expect)
+    np.testing.assert_array_equal(cnt[0], [0, 0, 0, 0])
+
+
+@pytest.mark.parametrize("N", [2, 3, 4])
+def test_fp8_mask_keeps_the_static_range(N):
+    """With the mask, T - I of A = -rho L is -rho (1 - rho)^(d-1) on d <= N: no entry
+    exceeds rho = absmax(A), so under A's (static) scale nothing saturates; unmasked,
+    the powers' binomial growth saturates it ([GEO] Methodologie 2)."""
+    A = _rho_L(64, 7 / 16)
+    _, cm, _ = oracle.neumann_fp8(A, N, True)
+    _, cu, _ = oracle.neumann_fp8(A, N, False)
+    assert cm[0].tolist() == [0, 0, 0, 0]
+    assert cu[0][2] >= 1711 and cu[0][0] == 0 and cu[0][1] == 0
+
+
+@pytest.mark.parametrize("mask", [True, False])
+def test_fp8_chain_close_to_fp64_on_c1_inputs(mask):
+    """Within the fp8 tolerance of the unquantised sum on c1-like blocks: e4m3 keeps 3
+    mantissa bits (relative step 2^-3, rounding error <= 2^-4 per quantisation)."""
+    A = _rand_A(31, 48, 64).astype(np.float32).astype(np.float64)
+    T8, cnt, am = oracle.neumann_fp8(A, 3, mask)
+    T64 = oracle.neumann(A, 3, mask)
+    assert _relF(T8, T64) <= 5e-2
+    eye = np.eye(64)
+    assert _relF(T8 - eye, T64 - eye) <= 6e-2
+    assert np.all(np.triu(T8[:, :, :], 1) == 0) and np.all(np.diagonal(T8, axis1=1, axis2=2) == 1)
+    assert cnt[:, 0].sum() == 0 and cnt[:, 1].sum() == 0
+    assert np.all(am[:, 0] > 0)

@@ -655,7 +655,9 @@ __global__ __launch_bounds__(NWAVES * WAVE, 1) void chunk_fwd_kernel(ChunkArgs a
     // stager one level below state wave 0 (it mostly waits on its loads)
     __builtin_amdgcn_s_setprio(2);
     Fp8Counts cnt{0, 0, 0, 0};
-    const bool count = (CMP == CMP_FP8) && a.stats != nullptr;
+    // every d_v slice of a head forms the same T: only slice 0 counts, so each block
+    // is counted once
+    const bool count = (CMP == CMP_FP8) && a.stats != nullptr && slice == 0;
     if constexpr (MODE == MODE_BAND) {
       const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 #pragma unroll

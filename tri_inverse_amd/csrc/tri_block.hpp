@@ -554,42 +554,6 @@ __device__ __forceinline__ float fp8_scale(float amax) {
   return (amax > 0.f && __builtin_isfinite(amax)) ? amax / FP8_MAX : 1.f;
 }
 
-// Z = sx * sy * (Xq Yq) with Xq, Yq the e4m3 codes of X / sx and Y / sy
-template <int NT, bool TFORM, int MAXD = NT - 1>
-__device__ __forceinline__ void lmul_fp8(const Mat<NT>& XT, float sx, const Mat<NT>& YD,
-                                         float sy, Mat<NT>& Z) {
-  constexpr int NP = (NT + 1) / 2;
-  long rp[NT][NP], cp[NP][NT];
-  const float ix = 1.f / sx, iy = 1.f / sy;
-#pragma unroll
-  for (int I = 0; I < NT; ++I)
-#pragma unroll
-    for (int p = 0; p < NP; ++p)
-      if (2 * p <= I && I - (2 * p + 1) <= MAXD)
-        rp[I][p] = quant8(tile_or_zero(XT, I, 2 * p), tile_or_zero(XT, I, 2 * p + 1), ix);
-#pragma unroll
-  for (int p = 0; p < NP; ++p)
-#pragma unroll
-    for (int J = 0; J < NT; ++J)
-      if (J <= 2 * p + 1 && 2 * p - J <= MAXD)
-        cp[p][J] = quant8(tile_or_zero(YD, 2 * p, J), tile_or_zero(YD, 2 * p + 1, J), iy);
-  const float sxy = sx * sy;
-#pragma unroll
-  for (int I = 0; I < NT; ++I)
-#pragma unroll
-    for (int J = 0; J <= I; ++J) {
-      if (I - J > MAXD) {
-        Z.t[I][J] = zero4();
-        continue;
-      }
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int p = J / 2; p <= I / 2; ++p)
-        acc = TFORM ? mma_fp8(cp[p][J], rp[I][p], acc) : mma_fp8(rp[I][p], cp[p][J], acc);
-      Z.t[I][J] = acc * sxy;
-    }
-}
-
 // fake-quantise the lower tiles of M (x -> s * q(x / s)); returns nothing, M updated
 template <int NT>
 __device__ __forceinline__ void fp8_roundtrip(Mat<NT>& M, float s) {
@@ -734,56 +698,112 @@ __device__ __forceinline__ void neumann_T_i8(Mat<NT>& AD, Mat<NT>& AT, int N, bo
 // N <= 16 (every tile two or more tile-diagonals below the main one is then zero in
 // A, in every intermediate and in T).
 
+// fp8 chain on X = H - I ([GEO] "Adaptation a la Quantification"): the identity never
+// enters a quantised tensor, so the scales follow A's powers alone.
+//   A' = s_A q(A),  X_1 = A',  X_{k+1} = A' + s_A s_X (q(A) q(X_k)),  T = I + s_T q(X_N)
+// (T = I + A' for N = 1).  q() are e4m3 codes under the tensor's absmax/448 scale; the
+// MFMA sums the code products in fp32 and one fused multiply-add scales and adds A'.
+// A's left-operand codes are formed once for all products.  AD, AT arrive band-masked
+// when the mask is on, and every X_{k+1} is masked before it is quantised.  Counters:
+// A under its own scale, each right operand X_1 .. X_{N-1} and X_N under theirs and
+// under A's (the static scale).
+template <int NT, int MAXD = NT - 1>
+__device__ __forceinline__ void neumann_T_fp8(const Mat<NT>& AD, const Mat<NT>& AT, int N, bool mask,
+                                              Mat<NT>& TT, Fp8Counts& cnt, bool count) {
+  constexpr int NP = (NT + 1) / 2;
+  const int band = mask ? N : (1 << 30);
+  const float sA = fp8_scale(absmax(AT));
+  if (count) fp8_count(AT, sA, sA, cnt);
+  if (N <= 1) {
+    TT = AT;
+    fp8_roundtrip(TT, sA);
+    add_eye(TT);
+    return;
+  }
+  const float iA = 1.f / sA;
+  long ra[NT][NP];
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      if (2 * p <= I && I - (2 * p + 1) <= MAXD)
+        ra[I][p] = quant8(tile_or_zero(AT, I, 2 * p), tile_or_zero(AT, I, 2 * p + 1), iA);
+  Mat<NT> AqD = AD, AqT = AT;  // A' in both forms
+  fp8_roundtrip(AqD, sA);
+  fp8_roundtrip(AqT, sA);
+  Mat<NT> X = AqD;  // X_1 (D-form)
+  for (int k = 1; k < N; ++k) {
+    const float sX = fp8_scale(absmax(X));
+    if (count) fp8_count(X, sX, sA, cnt);
+    const float iX = 1.f / sX, sxy = sA * sX;
+    long cx[NP][NT];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int J = 0; J < NT; ++J)
+        if (J <= 2 * p + 1 && 2 * p - J <= MAXD)
+          cx[p][J] = quant8(tile_or_zero(X, 2 * p, J), tile_or_zero(X, 2 * p + 1, J), iX);
+    const bool last = (k == N - 1);
+#pragma unroll
+    for (int I = 0; I < NT; ++I)
+#pragma unroll
+      for (int J = 0; J <= I; ++J) {
+        if (I - J > MAXD) {
+          (last ? TT : X).t[I][J] = zero4();
+          continue;
+        }
+        f32x4 acc = zero4();
+        if (last) {  // T-form: operands swapped
+#pragma unroll
+          for (int p = J / 2; p <= I / 2; ++p) acc = mma_fp8(cx[p][J], ra[I][p], acc);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) TT.t[I][J][r] = __builtin_fmaf(acc[r], sxy, AqT.t[I][J][r]);
+        } else {
+#pragma unroll
+          for (int p = J / 2; p <= I / 2; ++p) acc = mma_fp8(ra[I][p], cx[p][J], acc);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) X.t[I][J][r] = __builtin_fmaf(acc[r], sxy, AqD.t[I][J][r]);
+        }
+      }
+    if (mask) {
+      if (last)
+        mask_T(TT, band);
+      else
+        mask_D(X, band);
+    }
+  }
+  const float sT = fp8_scale(absmax(TT));
+  if (count) fp8_count(TT, sT, sA, cnt);
+  fp8_roundtrip(TT, sT);
+  add_eye(TT);
+}
+
 template <int NT, int CMP, int MAXD = NT - 1>
 __device__ __forceinline__ void neumann_T(const Mat<NT>& AD, const Mat<NT>& AT, int N, bool mask,
                                           Mat<NT>& TT, Fp8Counts& cnt, bool count) {
+  if constexpr (CMP == CMP_FP8) {
+    neumann_T_fp8<NT, MAXD>(AD, AT, N, mask, TT, cnt, count);
+    return;
+  }
   const int band = mask ? N : (1 << 30);
   if (N <= 1) {
     TT = AT;
-    if constexpr (CMP == CMP_FP8) {
-      // T - I is A itself: quantise it like every other operand
-      float sA = fp8_scale(absmax(AT));
-      if (count) fp8_count(AT, sA, sA, cnt);
-      fp8_roundtrip(TT, sA);
-    }
     if (mask) mask_T(TT, band);
     add_eye(TT);
     return;
   }
   Mat<NT> H = AD;  // H_1 = I + A (D-form)
   add_eye(H);
-  if constexpr (CMP == CMP_FP8) {
-    const float sA = fp8_scale(absmax(AT));
-    if (count) fp8_count(AT, sA, sA, cnt);
-    for (int k = 2; k < N; ++k) {
-      const float sH = fp8_scale(absmax(H));
-      if (count) fp8_count(H, sH, sA, cnt);
-      Mat<NT> Z;
-      lmul_fp8<NT, false, MAXD>(AT, sA, H, sH, Z);
-      add_eye(Z);
-      if (mask) mask_D(Z, band);
-      H = Z;
-    }
-    const float sH = fp8_scale(absmax(H));
-    if (count) fp8_count(H, sH, sA, cnt);
-    lmul_fp8<NT, true, MAXD>(AT, sA, H, sH, TT);  // T - I = A H_{N-1}
-    if (mask) mask_T(TT, band);
-    const float sT = fp8_scale(absmax(TT));
-    if (count) fp8_count(TT, sT, sA, cnt);
-    fp8_roundtrip(TT, sT);
-    add_eye(TT);
-  } else {
-    // Entries inside the band of a product of lower-triangular matrices only involve
-    // entries inside the band of the factors, so masking the final sum gives exactly
-    // (bit for bit) what masking A and every intermediate would.
-    for (int k = 2; k < N; ++k) {
-      Mat<NT> Z;
-      lmul<NT, CMP, false, MAXD, true>(AT, H, Z);
-      H = Z;
-    }
-    lmul<NT, CMP, true, MAXD, true>(AT, H, TT);
-    if (mask) mask_T(TT, band);
+  // Entries inside the band of a product of lower-triangular matrices only involve
+  // entries inside the band of the factors, so masking the final sum gives exactly
+  // (bit for bit) what masking A and every intermediate would.
+  for (int k = 2; k < N; ++k) {
+    Mat<NT> Z;
+    lmul<NT, CMP, false, MAXD, true>(AT, H, Z);
+    H = Z;
   }
+  lmul<NT, CMP, true, MAXD, true>(AT, H, TT);
+  if (mask) mask_T(TT, band);
 }
 
 // ---- parallel residual correction ([GEO] Methodologie SS3) ----------------------
