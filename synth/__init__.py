@@ -108,3 +108,30 @@ def correlated_keys(n_blocks: int, C: int, d_k: int, rho: float):
     beta = np.ones((n_blocks, C), dtype=np.float32)
     gamma = np.zeros((n_blocks, C), dtype=np.float32)
     return {"K64": K, "K": _bf16(K), "beta": torch.from_numpy(beta), "g": torch.from_numpy(gamma)}
+
+
+def dyadic_keys(n_blocks: int, C: int, d_k: int, a: float, b: float, beta: float):
+    """Deterministic keys exact in bf16: k_i = a e_0 + b e_{i+1} (a, b dyadic), so
+    k_i . k_j = a^2 for i != j; beta constant, gamma = 0.  Needs d_k >= C + 1."""
+    if d_k < C + 1:
+        raise ValueError("dyadic keys need d_k >= C + 1")
+    K = np.zeros((n_blocks, C, d_k), dtype=np.float32)
+    K[:, :, 0] = a
+    for i in range(C):
+        K[:, i, i + 1] = b
+    return {"K": _bf16(K), "beta": torch.full((n_blocks, C), float(beta)),
+            "g": torch.zeros((n_blocks, C))}
+
+
+def dyadic_prefill(seed: int, B: int, H: int, T: int, C: int, d_k: int, d_v: int,
+                   a: float, b: float, beta: float):
+    """Prefill inputs whose keys repeat the dyadic pattern of dyadic_keys in every chunk
+    (position r of a chunk: a e_0 + b e_{r+1}), beta constant, gamma = 0; Q unit rows
+    and V ~ N(0, 1) drawn as in prefill (bf16)."""
+    rng = np.random.default_rng(seed)
+    kb = dyadic_keys(1, C, d_k, a, b, beta)["K"][0]
+    K = kb.repeat(T // C, 1).expand(B, H, T, d_k).contiguous()
+    V = _bf16(rng.standard_normal(size=(B, H, T, d_v), dtype=np.float32))
+    Q = _bf16(_unit_rows(rng, (B, H, T, d_k)))
+    return {"Q": Q, "K": K, "V": V, "beta": torch.full((B, H, T), float(beta)),
+            "g": torch.zeros((B, H, T))}

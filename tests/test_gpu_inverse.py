@@ -4,6 +4,8 @@ same inputs).  Tolerances (relative Frobenius error over the whole output):
 Structural exactness is checked bit for bit: the upper triangle of T is exactly 0 and
 its diagonal exactly 1 (the products of lower-triangular operands add exact zeros).
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -28,6 +30,22 @@ def _structure_exact(T):
 
 def _oracle_T(A64, mode, N, mask):
     return oracle.doubling(A64) if mode == "exact" else oracle.neumann(A64, N, mask)
+
+
+# The identity dominates relF over T (|I|_F = 8 at C = 64), so T - I and each of its
+# first sub-diagonals are checked on their own.  Bar for bf16 operands: 2.2e-3, the
+# error of T - I when every MFMA operand is rounded to bf16 (RNE) and accumulated
+# exactly, on c1-like blocks (the rounding emulation of the scope table's error model).
+TOL_TI = {"f32": 1e-5, "bf16": 2.2e-3, "bf16_out": 3.3e-3}
+
+
+def _band_checks(Tg, Tr, compute, dmax):
+    eye = np.eye(Tg.shape[-1])
+    assert relF(Tg - eye, Tr - eye) <= TOL_TI[compute], relF(Tg - eye, Tr - eye)
+    for d in range(1, dmax + 1):
+        eg = np.diagonal(Tg, offset=-d, axis1=1, axis2=2)
+        er = np.diagonal(Tr, offset=-d, axis1=1, axis2=2)
+        assert relF(eg, er) <= TOL_TI[compute], (d, relF(eg, er))
 
 
 def _fp32_A_workload(nb=256, C=64, seed=0):
@@ -82,6 +100,42 @@ def test_inverse_from_bf16_K(C, variant):
     Tg = f64(T)
     _structure_exact(Tg)
     assert relF(Tg, Tr) <= TOL["bf16"], relF(Tg, Tr)
+    _band_checks(Tg, Tr, "bf16", min(N if mode == "neumann" else 3, C - 1))
+
+
+@pytest.mark.parametrize("C", [16, 32, 64])
+@pytest.mark.parametrize("N", [2, 3, 4])
+@pytest.mark.parametrize("mask", [True, False])
+@pytest.mark.parametrize("ab_beta", [(0.5, 0.5, 1.0), (1.0, 1.0, 0.5)])
+def test_inverse_dyadic_correlated_keys_closed_form(C, N, mask, ab_beta):
+    """Keys k_i = a e_0 + b e_{i+1} (exact in bf16), beta constant, no gate: A = -rho L
+    with rho = beta a^2 (1/4 and 1/2), so every power's cross terms are O(1).  Closed
+    forms ([GEO] Methodologie 1-2, pinned on the CPU): the truncated sum has
+    sum_{n=1}^{N} (-rho)^n binom(d-1, n-1) on sub-diagonal d; the masked one is the exact
+    inverse -rho (1 - rho)^(d-1) for d <= N and zero beyond.  Every operand the bf16
+    products meet is then exactly representable (masked, and unmasked for N <= 3), so T
+    must equal the closed form bit for bit; unmasked N = 4 rounds the third power's
+    sum to bf16 and is held to the bf16 bar."""
+    a, b, beta = ab_beta
+    rho = beta * a * a
+    say(f"dyadic keys C={C} N={N} mask={mask} rho={rho}")
+    inp = synth.dyadic_keys(5, C, 128, a, b, beta)
+    T = tri.gdn_tri_inverse_neumann(K=cuda(inp["K"]), beta=cuda(inp["beta"]), g=cuda(inp["g"]), C=C,
+                                    N=N, mask=mask, compute="bf16")
+    torch.cuda.synchronize()
+    d = np.subtract.outer(np.arange(C), np.arange(C))
+    if mask:
+        ref = np.where((d >= 1) & (d <= N), -rho * (1 - rho) ** np.maximum(d - 1, 0), 0.0)
+    else:
+        ref = sum((-rho) ** n * np.where(d >= 1, np.vectorize(math.comb)(np.maximum(d - 1, 0), n - 1), 0)
+                  for n in range(1, N + 1))
+    ref = np.eye(C) + ref
+    Tg = f64(T)
+    _structure_exact(Tg)
+    if mask or N <= 3:
+        np.testing.assert_array_equal(Tg, np.broadcast_to(ref, Tg.shape))
+    else:
+        _band_checks(Tg, np.broadcast_to(ref, Tg.shape), "bf16", N)
 
 
 @pytest.mark.parametrize("k_dtype", ["bf16", "f32"])
@@ -141,6 +195,10 @@ def test_full_size_batched_inverse_all_blocks():
         Tg = f64(T)
         _structure_exact(Tg)
         assert relF(Tg, Tr) <= TOL["bf16"]
+        # T stored as bf16 adds its own rounding (at most 2^-9 relative, RMS about
+        # 1.1e-3): the bar for T - I grows by that much
+        _band_checks(Tg, Tr, "bf16" if t_dtype == torch.float32 else "bf16_out",
+                     N if mode == "neumann" else 3)
 
 
 def test_fp8_inverse_and_counters():
