@@ -247,12 +247,15 @@ def bench_chunk(torch, tri, synth, cfg, variants, steps, warmup, n_sets=2, stats
     res = {}
     for v in variants:
         mode, N, mask, compute = v
+        # one workspace for every launch: they run one after another on one stream
+        need = tri.gdn_chunk_fwd_workspace_bytes(B, H, T, dk, dv, C, mode, N, mask, compute)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
 
         def launch(i):
             x = sets[i]
             tri.gdn_chunk_fwd(x["Q"], x["K"], x["V"], x["beta"], x["g"], C=C, scale=dk ** -0.5,
                               mode=mode, N=N, mask=mask, compute=compute, O=outs[i][0],
-                              S_out=outs[i][1], stats=st)
+                              S_out=outs[i][1], stats=st, workspace=ws)
         ms, _ = time_launches(torch, launch, n_sets, steps, warmup)
         tok, by, fl = chunk_bytes_flops(cfg, v)
         name = ("exact" if mode == "exact" else "N%d_%s" % (N, "masked" if mask else "unmasked")) + "_" + compute

@@ -30,7 +30,9 @@
  *     enqueued on it and the call returns without synchronising.  Argument errors
  *     and launch errors are returned synchronously; device faults surface at the
  *     caller's next synchronisation.  No C++ exception crosses the ABI.
- *   - The library allocates nothing, keeps no per-call state and is reentrant.
+ *   - The library allocates nothing, keeps no per-call state and is reentrant.  Where
+ *     a call needs device scratch memory (gdn_chunk_fwd for most inverse variants),
+ *     the caller passes it in and a query states its size.
  *   - n_blocks == 0 (or B*H == 0, T == 0) is valid and enqueues nothing.
  *   - Supported chunk sizes C: 16, 32, 64 (all entry points); 128 and 256 for the
  *     inverse entry points and gdn_wy with bf16 keys and bf16 products (compute =
@@ -47,7 +49,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -56,7 +58,8 @@ typedef enum gdn_status {
   GDN_ERR_BAD_DTYPE = 3,     /* dtype code not accepted for that argument           */
   GDN_ERR_BAD_ALIGNMENT = 4, /* a tensor pointer is not 16-byte aligned             */
   GDN_ERR_UNSUPPORTED = 5,   /* valid request this build does not implement         */
-  GDN_ERR_HIP = 6            /* the HIP runtime reported an error at launch         */
+  GDN_ERR_WORKSPACE = 6,     /* workspace missing or smaller than the query returned */
+  GDN_ERR_HIP = 7            /* the HIP runtime reported an error at launch         */
 } gdn_status;
 
 /* element types (int32 codes in every signature) */
@@ -107,12 +110,21 @@ typedef struct gdn_blocks {
   int32_t d_k;
 } gdn_blocks;
 
-/* fp8 diagnostics, accumulated on the device by the fp8 paths (uint64_t[4]):
- *   [0] non-finite values met when quantising
- *   [1] saturations (|x| / scale rounds beyond 448, i.e. >= 464) under the dynamic per-block absmax scale
- *   [2] saturations under a static per-block scale (A's scale reused for its powers
- *       and for T): the fixed-range regime in which high powers overflow
- *   [3] non-zero values that quantise to zero (underflow)                          */
+/* fp8 diagnostics of the e4m3 power chain ([GEO] "Adaptation a la Quantification"),
+ * a DEVICE struct accumulated by the fp8 paths.  The chain runs on X = H - I:
+ * A' = s_A q(A), X_1 = A', X_{k+1} = A' + s_A s_X (q(A) q(X_k)), T = I + s_T q(X_N),
+ * q() the e4m3 codes under the tensor's own absmax/448 scale.  Counted over every
+ * quantised tensor of every block, once per block: A, the right operands X_1..X_{N-1}
+ * and X_N (N >= 2).  x counts as
+ *   nonfinite    not finite;
+ *   sat_dynamic  |x| / s_Y >= 464 under its own scale s_Y (it would round beyond 448;
+ *                0 by construction of an absmax scale, kept as a check);
+ *   sat_static   |x| / s_A >= 464 under A's scale: had A's range been fixed for its
+ *                powers and T, this value would overflow (the regime the mask is for);
+ *   underflow    x != 0 and |x| / s_Y <= 2^-10 (rounds to the code 0).            */
+typedef struct gdn_fp8_stats {
+  unsigned long long nonfinite, sat_dynamic, sat_static, underflow;
+} gdn_fp8_stats;
 #define GDN_FP8_STATS_COUNT 4
 
 int gdn_abi_version(void);
@@ -129,12 +141,12 @@ gdn_status gdn_build_A(const gdn_blocks* in, float* A_out, void* stream);
  * given fp32 A the result is exactly determined: every scaling is by a power of two,
  * integer products are exact and each intermediate sum is rounded once to fp32.
  * T_out [n_blocks][C][C], t_dtype GDN_F32
- * or GDN_BF16.  stats: device uint64_t[4] (see above) or NULL; when given it is
+ * or GDN_BF16.  stats: device gdn_fp8_stats (see above) or NULL; when given it is
  * zeroed on `stream` and then accumulated (fp8 compute only; other computes write
  * zeros). */
 gdn_status gdn_tri_inverse_neumann(const gdn_blocks* in, int32_t N, int32_t mask,
                                    int32_t compute, void* T_out, int32_t t_dtype,
-                                   uint64_t* stats, void* stream);
+                                   gdn_fp8_stats* stats, void* stream);
 
 /* T = prod_{i=0}^{m-1} (I + A^(2^i)), m = ceil(log2 C): the exact inverse by
  * multiplications only.  compute GDN_F32 or GDN_BF16. */
@@ -168,20 +180,36 @@ gdn_status gdn_wy(const gdn_blocks* in, const void* T, int32_t t_dtype,
                   const gdn_inverse_cfg* inv, const void* V, int32_t d_v, int32_t gate_k,
                   void* W_out, void* U_out, int32_t out_dtype, void* stream);
 
-/* Chunk-wise gated delta rule forward over whole sequences.  Per (b, h), chunks
- * in order, state S [d_k][d_v] fp32 starting at S0 (zeros if NULL):
+/* Device workspace, in bytes, that gdn_chunk_fwd needs for these arguments.  The
+ * band-masked truncated sum with N <= 3 on bf16 operands forms T inside the scan and
+ * needs none (0).  Every other inverse variant forms T - I of all B*H*T/C chunks in a
+ * batched pre-pass and hands it to the scan through the workspace: 6144 bytes per
+ * chunk at C = 64.  Returns 0 as well for arguments gdn_chunk_fwd rejects (it then
+ * reports why).  No HIP call is made. */
+size_t gdn_chunk_fwd_workspace_bytes(int32_t B, int32_t H, int64_t T, int32_t d_k, int32_t d_v,
+                                     int32_t C, const gdn_inverse_cfg* inv);
+
+/* Chunk-wise gated delta rule forward over whole sequences ([GEO] problem statement:
+ * the chunk-wise form inverts I - A per chunk and carries a fixed-size state; [PSDA]
+ * section 2.A: the state stays on chip).  Per (b, h), chunks in order, state S
+ * [d_k][d_v] fp32 starting at S0 (zeros if NULL):
  *   T from A (inv); U' = T diag(beta) (V - diag(exp(G)) K S)   (= U - W S, W gated)
  *   O  = scale (diag(exp(G)) Q S + (Q K^T .* exp(G_i - G_j) .* [i >= j]) U')
  *   S <- exp(G_C) S + K^T diag(exp(G_C - G)) U'
  * Q, K [B][H][T][d_k] and V [B][H][T][d_v] in qkv_dtype (GDN_BF16); beta, g
  * [B][H][T] fp32 (g per-token log-gates); S0, S_out [B][H][d_k][d_v] fp32;
- * O [B][H][T][d_v] in o_dtype (GDN_BF16 or GDN_F32).  T % C == 0.  stats as for
- * gdn_tri_inverse_neumann (fp8 compute). */
+ * O [B][H][T][d_v] in o_dtype (GDN_BF16 or GDN_F32).  T % C == 0; C = 64.
+ * workspace: device memory of at least gdn_chunk_fwd_workspace_bytes(...) bytes,
+ * 16-byte aligned (GDN_ERR_WORKSPACE if it is needed and NULL or smaller; may be NULL
+ * when none is needed).  Its contents are scratch: overwritten by the call and read
+ * back by it on `stream`, so one workspace must not serve two calls in flight at
+ * once.  stats as for gdn_tri_inverse_neumann (fp8 compute, each chunk counted once). */
 gdn_status gdn_chunk_fwd(const void* Q, const void* K, const void* V, int32_t qkv_dtype,
                          const float* beta, const float* g, const float* S0, void* O,
                          int32_t o_dtype, float* S_out, int32_t B, int32_t H, int64_t T,
                          int32_t d_k, int32_t d_v, int32_t C, float scale,
-                         const gdn_inverse_cfg* inv, uint64_t* stats, void* stream);
+                         const gdn_inverse_cfg* inv, void* workspace, size_t workspace_bytes,
+                         gdn_fp8_stats* stats, void* stream);
 
 /* The gated delta rule one token at a time (decode).  Per (b, h), tokens t = 0..n-1 in
  * order, a = exp(g_t), state S [d_k][d_v] fp32 entering as S_in (zeros if NULL):

@@ -28,8 +28,8 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert tri.gdn_abi_version() == 1
-    for s in range(7):
+    assert tri.gdn_abi_version() == 2
+    for s in range(8):
         assert tri.gdn_status_string(s).startswith("GDN_")
     assert "unknown" in tri.gdn_status_string(99)
 
@@ -185,3 +185,56 @@ def test_int8_compute_routing():
                                       tri.GDN_F32, None) == 5
     assert lib.gdn_tri_inverse_residual(ctypes.byref(blocks(n_blocks=0)), 3, 1, 8, tri.GDN_INT8,
                                         FAKE, tri.GDN_F32, None) == 5
+
+
+def _inv(mode=tri.GDN_INV_NEUMANN, N=3, mask=1, compute=tri.GDN_BF16):
+    c = tri.gdn_inverse_cfg()
+    c.mode, c.N, c.mask, c.compute = mode, N, mask, compute
+    return c
+
+
+def test_chunk_fwd_workspace_query():
+    """The band path (N <= 3, masked, bf16 products) needs no workspace; every other
+    variant needs 6144 bytes per chunk for the pre-pass's T - I packs; arguments the
+    call would reject query as 0."""
+    q = lambda inv, B=4, H=16, T=8192, dk=128, dv=128, C=64: lib.gdn_chunk_fwd_workspace_bytes(
+        B, H, T, dk, dv, C, ctypes.byref(inv) if inv is not None else None)
+    chunks = 4 * 16 * 8192 // 64
+    assert q(_inv()) == 0
+    assert q(_inv(N=2)) == 0
+    assert q(_inv(N=4)) == chunks * 6144
+    assert q(_inv(mask=0)) == chunks * 6144
+    assert q(_inv(mode=tri.GDN_INV_EXACT)) == chunks * 6144
+    assert q(_inv(compute=tri.GDN_FP8_E4M3)) == chunks * 6144
+    assert q(None) == 0
+    assert q(_inv(), T=100) == 0                     # T % C != 0
+    assert q(_inv(), C=32) == 0                      # unsupported chunk size
+    assert q(_inv(compute=tri.GDN_F32)) == 0
+    assert tri.gdn_chunk_fwd_workspace_bytes(1, 2, 256, 128, 128, mask=False) == 2 * 4 * 6144
+
+
+def test_chunk_fwd_validation():
+    def cf(inv, ws=None, ws_bytes=0, B=1, H=2, T=256, dk=128, dv=128, C=64, Q=FAKE, qd=tri.GDN_BF16,
+           od=tri.GDN_BF16, stats=None):
+        return lib.gdn_chunk_fwd(Q, FAKE, FAKE, qd, FAKE, FAKE, None, FAKE, od, FAKE, B, H, T, dk, dv, C,
+                                 0.1, ctypes.byref(inv) if inv is not None else None, ws, ws_bytes, stats,
+                                 None)
+    need = 2 * 4 * 6144
+    assert cf(None) == 1
+    assert cf(_inv(), T=100) == 2
+    assert cf(_inv(), qd=tri.GDN_F32) == 5
+    assert cf(_inv(), qd=9) == 3
+    assert cf(_inv(), C=32) == 5
+    assert cf(_inv(), dk=96) == 5
+    assert cf(_inv(compute=tri.GDN_FP8_E4M3, mode=tri.GDN_INV_EXACT)) == 5
+    assert cf(_inv(), Q=None) == 1
+    assert cf(_inv(), stats=FAKE + 8) == 4
+    # workspace: needed and missing or short -> GDN_ERR_WORKSPACE (6); misaligned -> 4
+    unmasked = _inv(mask=0)
+    assert cf(unmasked) == 6
+    assert cf(unmasked, ws=FAKE, ws_bytes=need - 1) == 6
+    assert cf(unmasked, ws=FAKE + 8, ws_bytes=need) == 4
+    assert cf(_inv(compute=tri.GDN_FP8_E4M3)) == 6
+    # empty problems enqueue nothing and need no workspace
+    assert cf(unmasked, B=0) == 0
+    assert cf(unmasked, T=0) == 0

@@ -28,6 +28,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 GDN_F32, GDN_BF16, GDN_FP8_E4M3, GDN_INT8 = 0, 1, 2, 3
 GDN_INV_NEUMANN, GDN_INV_EXACT = 0, 1
 GDN_OK = 0
+GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = 5, 6, 7
 FP8_STATS_FIELDS = ("nonfinite", "sat_dynamic", "sat_static", "underflow")
 
 _COMPUTE = {"f32": GDN_F32, "fp32": GDN_F32, "bf16": GDN_BF16, "fp8": GDN_FP8_E4M3,
@@ -65,16 +66,19 @@ _lib.gdn_tri_inverse_fs.argtypes = [_P(gdn_blocks), _vp, _i32, _vp]
 _lib.gdn_wy.restype = _i32
 _lib.gdn_wy.argtypes = [_P(gdn_blocks), _vp, _i32, _P(gdn_inverse_cfg), _vp, _i32, _i32, _vp, _vp,
                         _i32, _vp]
+_lib.gdn_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
+_lib.gdn_chunk_fwd_workspace_bytes.argtypes = [_i32, _i32, _i64, _i32, _i32, _i32, _P(gdn_inverse_cfg)]
 _lib.gdn_chunk_fwd.restype = _i32
 _lib.gdn_chunk_fwd.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
-                               _i64, _i32, _i32, _i32, _f32, _P(gdn_inverse_cfg), _vp, _vp]
+                               _i64, _i32, _i32, _i32, _f32, _P(gdn_inverse_cfg), _vp, ctypes.c_size_t,
+                               _vp, _vp]
 _lib.gdn_decode.restype = _i32
 _lib.gdn_decode.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                             _i32, _i32, _f32, _vp]
 
 EXPORTED = ("gdn_abi_version", "gdn_status_string", "gdn_build_A", "gdn_tri_inverse_neumann",
             "gdn_tri_inverse_exact", "gdn_tri_inverse_residual", "gdn_tri_inverse_fs", "gdn_wy",
-            "gdn_chunk_fwd", "gdn_decode")
+            "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_decode")
 
 
 class GdnError(RuntimeError):
@@ -265,11 +269,22 @@ def gdn_wy(K, beta, g, V, C: int = 64, T=None, mode="neumann", N: int = 3, mask:
     return W_out, U_out
 
 
+def gdn_chunk_fwd_workspace_bytes(B: int, H: int, T: int, d_k: int, d_v: int, C: int = 64,
+                                  mode="neumann", N: int = 3, mask: bool = True, compute="bf16") -> int:
+    """Device workspace (bytes) gdn_chunk_fwd needs for these arguments (0: none)."""
+    cfg = _inv_cfg(mode, N, mask, compute)
+    return int(_lib.gdn_chunk_fwd_workspace_bytes(int(B), int(H), int(T), int(d_k), int(d_v), int(C),
+                                                  ctypes.byref(cfg)))
+
+
 def gdn_chunk_fwd(Q, K, V, beta, g, C: int = 64, scale: float | None = None, S0=None,
                   mode="neumann", N: int = 3, mask: bool = True, compute="bf16",
-                  o_dtype=torch.bfloat16, stats=None, O=None, S_out=None, stream=None):
+                  o_dtype=torch.bfloat16, stats=None, O=None, S_out=None, workspace=None, stream=None):
     """Chunk-wise gated delta rule forward.  Q, K [B,H,T,d_k], V [B,H,T,d_v] bf16;
-    beta, g [B,H,T] fp32 -> (O [B,H,T,d_v], S_out [B,H,d_k,d_v] fp32)."""
+    beta, g [B,H,T] fp32 -> (O [B,H,T,d_v], S_out [B,H,d_k,d_v] fp32).
+
+    workspace: a CUDA uint8 tensor of at least gdn_chunk_fwd_workspace_bytes(...) bytes,
+    or None to have one allocated here (through torch) when the variant needs it."""
     for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
         _dev(t, n, (torch.bfloat16,))
     _dev(beta, "beta", (torch.float32,))
@@ -292,12 +307,21 @@ def gdn_chunk_fwd(Q, K, V, beta, g, C: int = 64, scale: float | None = None, S0=
     _dev(S_out, "S_out", (torch.float32,))
     if stats is not None:
         _dev(stats, "stats", (torch.int64,))
+        if stats.numel() < 4:
+            raise ValueError("stats needs 4 elements")
     if scale is None:
         scale = dk ** -0.5
     cfg = _inv_cfg(mode, N, mask, compute)
+    need = int(_lib.gdn_chunk_fwd_workspace_bytes(B, H, T, dk, dv, C, ctypes.byref(cfg)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=K.device, dtype=torch.uint8)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = _lib.gdn_chunk_fwd(_ptr(Q), _ptr(K), _ptr(V), GDN_BF16, _ptr(beta), _ptr(g), _ptr(S0),
                             _ptr(O), _TORCH_DTYPE[O.dtype], _ptr(S_out), B, H, T, dk, dv, C,
-                            float(scale), ctypes.byref(cfg), _ptr(stats), _stream(stream))
+                            float(scale), ctypes.byref(cfg), _ptr(workspace), ws_bytes, _ptr(stats),
+                            _stream(stream))
     _check(st, "gdn_chunk_fwd")
     return O, S_out
 

@@ -86,6 +86,7 @@ const char* gdn_status_string(int32_t s) {
     case GDN_ERR_BAD_DTYPE: return "GDN_ERR_BAD_DTYPE: dtype code not accepted for this argument";
     case GDN_ERR_BAD_ALIGNMENT: return "GDN_ERR_BAD_ALIGNMENT: a tensor pointer is not 16-byte aligned";
     case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: configuration not implemented by this build";
+    case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or smaller than the query returned";
     case GDN_ERR_HIP: return "GDN_ERR_HIP: the HIP runtime reported an error at launch";
     default: return "unknown gdn_status";
   }
@@ -104,7 +105,7 @@ gdn_status gdn_build_A(const gdn_blocks* in, float* A_out, void* stream) {
 }
 
 gdn_status gdn_tri_inverse_neumann(const gdn_blocks* in, int32_t N, int32_t mask, int32_t compute,
-                                   void* T_out, int32_t t_dtype, uint64_t* stats, void* stream) {
+                                   void* T_out, int32_t t_dtype, gdn_fp8_stats* stats, void* stream) {
   int src = 0;
   gdn_status st = check_blocks(in, true, false, &src);
   if (st != GDN_OK) return st;
@@ -243,11 +244,9 @@ gdn_status gdn_wy(const gdn_blocks* in, const void* T, int32_t t_dtype, const gd
                                       as_stream(stream)));
 }
 
-gdn_status gdn_chunk_fwd(const void* Q, const void* K, const void* V, int32_t qkv_dtype,
-                         const float* beta, const float* g, const float* S0, void* O,
-                         int32_t o_dtype, float* S_out, int32_t B, int32_t H, int64_t T,
-                         int32_t d_k, int32_t d_v, int32_t C, float scale,
-                         const gdn_inverse_cfg* inv, uint64_t* stats, void* stream) {
+// argument checks of gdn_chunk_fwd that need no pointer (shared with the workspace query)
+static gdn_status check_chunk_args(int32_t qkv_dtype, int32_t o_dtype, int32_t B, int32_t H, int64_t T, int32_t d_k,
+                            int32_t d_v, int32_t C, const gdn_inverse_cfg* inv) {
   if (!inv) return GDN_ERR_NULL_POINTER;
   if (B < 0 || H < 0 || T < 0 || d_k <= 0 || d_v <= 0 || C <= 0) return GDN_ERR_BAD_SHAPE;
   if (qkv_dtype != GDN_BF16) return (qkv_dtype == GDN_F32) ? GDN_ERR_UNSUPPORTED : GDN_ERR_BAD_DTYPE;
@@ -265,21 +264,63 @@ gdn_status gdn_chunk_fwd(const void* Q, const void* K, const void* V, int32_t qk
   if (C != 64) return GDN_ERR_UNSUPPORTED;
   if (!(d_k == 64 || d_k == 128)) return GDN_ERR_UNSUPPORTED;
   if (d_v % 32 != 0 || d_v > 256) return GDN_ERR_UNSUPPORTED;
+  return GDN_OK;
+}
+
+static size_t chunk_workspace(int32_t B, int32_t H, int64_t T, int32_t C, const gdn_inverse_cfg* inv) {
+  if (gdn::chunk_fwd_band_path(inv->mode, inv->N, inv->mask, inv->compute)) return 0;
+  return (size_t)B * (size_t)H * (size_t)(T / C) * gdn::T_PACK_BYTES;
+}
+
+size_t gdn_chunk_fwd_workspace_bytes(int32_t B, int32_t H, int64_t T, int32_t d_k, int32_t d_v,
+                                     int32_t C, const gdn_inverse_cfg* inv) {
+  if (check_chunk_args(GDN_BF16, GDN_BF16, B, H, T, d_k, d_v, C, inv) != GDN_OK) return 0;
+  return chunk_workspace(B, H, T, C, inv);
+}
+
+gdn_status gdn_chunk_fwd(const void* Q, const void* K, const void* V, int32_t qkv_dtype,
+                         const float* beta, const float* g, const float* S0, void* O,
+                         int32_t o_dtype, float* S_out, int32_t B, int32_t H, int64_t T,
+                         int32_t d_k, int32_t d_v, int32_t C, float scale,
+                         const gdn_inverse_cfg* inv, void* workspace, size_t workspace_bytes,
+                         gdn_fp8_stats* stats, void* stream) {
+  gdn_status st = check_chunk_args(qkv_dtype, o_dtype, B, H, T, d_k, d_v, C, inv);
+  if (st != GDN_OK) return st;
   if (stats && !aligned16(stats)) return GDN_ERR_BAD_ALIGNMENT;
   hipStream_t s = as_stream(stream);
   auto* st64 = reinterpret_cast<unsigned long long*>(stats);
   const bool empty = (int64_t)B * H == 0 || T == 0;
+  const size_t need = empty ? 0 : chunk_workspace(B, H, T, C, inv);
   if (!empty) {
     if (!Q || !K || !V || !beta || !g || !O || !S_out) return GDN_ERR_NULL_POINTER;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(beta) || !aligned16(g) ||
         !aligned16(O) || !aligned16(S_out) || (S0 && !aligned16(S0)))
       return GDN_ERR_BAD_ALIGNMENT;
+    if (need > 0) {
+      if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
+      if (!aligned16(workspace)) return GDN_ERR_BAD_ALIGNMENT;
+    }
   }
   if (st64) {
     gdn::launch_zero_stats(st64, s);
     if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;
   }
   if (empty) return GDN_OK;
+  if (need > 0) {
+    // pre-pass: T - I of every chunk as row packs, each chunk a block of the keys
+    gdn::BlocksArgs ba;
+    ba.A = nullptr;
+    ba.K = K;
+    ba.beta = beta;
+    ba.g = g;
+    ba.n_blocks = (int64_t)B * H * (T / C);
+    ba.C = C;
+    ba.d_k = d_k;
+    ba.g_cumulative = 0;
+    const gdn_status pre =
+        launch_result(gdn::launch_T_packs(ba, inv->mode, inv->N, inv->mask, inv->compute, workspace, st64, s));
+    if (pre != GDN_OK) return pre;
+  }
   gdn::ChunkLaunch p;
   p.Q = Q;
   p.K = K;
@@ -289,7 +330,7 @@ gdn_status gdn_chunk_fwd(const void* Q, const void* K, const void* V, int32_t qk
   p.S0 = S0;
   p.O = O;
   p.S_out = S_out;
-  p.stats = st64;
+  p.packs = need > 0 ? workspace : nullptr;
   p.T = T;
   p.B = B;
   p.H = H;

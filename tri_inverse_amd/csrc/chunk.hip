@@ -26,7 +26,9 @@
 //               O = scale (e^G Q S + P U') for their 16 rows, all 32 columns.  Tiles 0
 //               and 2 share one SIMD, tiles 1 and 3 another (equal shares of the
 //               triangular P).
-//   wave 5      T of the next chunk (beside state wave 1).
+//   wave 5      T - I of the next chunk (beside state wave 1): formed here on the band
+//               path (N <= 3 with the mask, bf16), else streamed from the row packs a
+//               batched pre-pass wrote (every other inverse variant, fp8 included).
 //   wave 4      copies K rows, V columns, log-gates and beta of the chunk after next
 //               into a 4-deep LDS ring and forms that chunk's gate factors (beside
 //               state wave 0).
@@ -63,7 +65,7 @@ struct ChunkArgs {
   const float* S0;
   void* O;
   float* S_out;
-  unsigned long long* stats;
+  const bf16x8* packs;  // T - I row packs of every chunk (pre-pass), MODE_LOAD only
   int64_t T;
   int BH;
   int dv;
@@ -174,70 +176,17 @@ __device__ __forceinline__ void write_gates(float gl, float bl, ChunkGates& GT) 
   }
 }
 
-// ---- T wave: A, T ---------------------------------------------------------------------
-template <int DK, int MODE, int CMP, int MAXD>
-__device__ __forceinline__ void produce_T(const ChunkArgs& a, const ChunkIn<DK>& R,
-                                          bf16x8 (&trp)[CNT][2][WAVE], const ChunkGates& GT, Fp8Counts& cnt,
-                                          bool count) {
-  const int l = lane_id(), c = l & 15;
-  const float bl = R.beta[l];
-  KBlock<CNT, DK> kb;
-#pragma unroll
-  for (int I = 0; I < CNT; ++I)
-#pragma unroll
-    for (int p = 0; p < DK / 32; ++p) kb.kf[I][p] = rowfrag_nat<DK>(R, 16 * I + c, p);  // K K^T: any common d order
-  // Gates (formed by the stager): the per-position factors from GT, the D-form row
-  // factors with one 16-byte LDS read per tile and factor.
-  Gates<CNT> gt;
-  gt.Gl = GT.G[l];
-  gt.bl = bl;
-  gt.split = GT.split != 0;
-  const float egl = GT.eg[l], engl = GT.eng[l];
-  {
-    const int g4 = 4 * (l >> 4);
-    float rb[4], nb[4];
-    row_broadcasts(-bl * egl, rb);
-    row_broadcasts(engl, nb);
-#pragma unroll
-    for (int X = 0; X < CNT; ++X) {
-      gt.rc[X] = rb[X];
-      gt.nc[X] = nb[X];
-      const f32x4 b4 = *reinterpret_cast<const f32x4*>(&GT.beta[16 * X + g4]);
-      const f32x4 e4 = *reinterpret_cast<const f32x4*>(&GT.eg[16 * X + g4]);
-      const f32x4 n4 = *reinterpret_cast<const f32x4*>(&GT.eng[16 * X + g4]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        gt.rr[X][r] = -b4[r] * e4[r];
-        gt.nr[X][r] = n4[r];
-      }
-    }
-  }
-  Mat<CNT> S, AD, AT, TT;
-  constexpr bool BANDED = (MODE == MODE_NEUMANN && CMP == CMP_FP8);
-  gram_from_frags<CNT, DK, MAXD>(kb, S);
-  const int band = a.mask ? a.N : -1;
-  gram_to_A<CNT, MAXD, BANDED>(S, gt, BANDED ? band : -1, AD, AT);
-  if constexpr (MODE == MODE_EXACT)
-    doubling_T<CNT, CMP_BF16>(AD, AT, TT);
-  else
-    neumann_T<CNT, CMP, MAXD>(AD, AT, a.N, a.mask != 0, TT, cnt, count);
-  // T - I (exact in fp32): the state step adds the identity part of T Y in fp32
-#pragma unroll
-  for (int I = 0; I < CNT; ++I) TT.t[I][I] = TT.t[I][I] - eye_tile();
-#pragma unroll
-  for (int I = 0; I < CNT; ++I)
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-      if (2 * p <= I && I - (2 * p + 1) <= MAXD)
-        trp[I][p][l] = pack8(tile_or_zero(TT, I, 2 * p), tile_or_zero(TT, I, 2 * p + 1));
-}
-
+// ---- T wave -----------------------------------------------------------------------------
 // Band-masked sum with N <= 3: the band of T - I by band3_from_subdiag (lane i = row
 // i).  The Gram entries come from the MFMA diagonal tiles and the last four columns of
 // the tile left of each (T-form, through LDS to the row lanes).  Only the band slots of
 // the row packs are written: the rest of both pack buffers is cleared once before the
 // scan and stays zero.
-constexpr int MODE_BAND = 16;  // chunk-only code next to the MODE_* values
+constexpr int MODE_BAND = 16;  // chunk-only codes next to the MODE_* values
+// Every other variant (the truncated sum on bf16 or fp8 operands, masked or not, and the
+// exact product) has its T - I formed by the batched pre-pass, one wave per block, as
+// the row packs the state step reads; the T wave only streams them into LDS.
+constexpr int MODE_LOAD = 17;
 
 // row-pack slot (bf16 index into trp) of T - I at row i, column j
 __device__ __forceinline__ int trp_slot(int i, int j) {
@@ -549,7 +498,7 @@ __device__ __forceinline__ void lds_barrier() {
 // gr[j % 4], the other products of chunk j in buf[j % 2].
 //   wave 4      it: stores chunk it+2 into in and its gate factors into gr (loaded at
 //               it-1), loads chunk it+3
-//   wave 5      it: T of chunk it+1         reads in, gr     writes buf.trp
+//   wave 5      it: T of chunk it+1         reads in, gr (or the packs) writes buf.trp
 //   waves 0, 1  it: state step of chunk it  reads in, gr, buf.trp
 //                                           writes buf.st, buf.uh/ul
 //   waves 2, 3, 6, 7 it: P, O of chunk it-1 reads in, gr, buf.{st, uh, ul}
@@ -654,10 +603,6 @@ __global__ __launch_bounds__(NWAVES * WAVE, 1) void chunk_fwd_kernel(ChunkArgs a
     // issue priority on the shared SIMDs: the T wave level with state wave 1, the
     // stager one level below state wave 0 (it mostly waits on its loads)
     __builtin_amdgcn_s_setprio(2);
-    Fp8Counts cnt{0, 0, 0, 0};
-    // every d_v slice of a head forms the same T: only slice 0 counts, so each block
-    // is counted once
-    const bool count = (CMP == CMP_FP8) && a.stats != nullptr && slice == 0;
     if constexpr (MODE == MODE_BAND) {
       const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
@@ -666,29 +611,42 @@ __global__ __launch_bounds__(NWAVES * WAVE, 1) void chunk_fwd_kernel(ChunkArgs a
         for (int I = 0; I < CNT; ++I)
 #pragma unroll
           for (int p = 0; p < 2; ++p) buf[b].trp[I][p][l] = z;
-    }
-    lds_barrier();
-    for (int it = -1; it <= nchunks; ++it) {
-      const int ch = it + 1;
-      if (ch < nchunks) {
-        if constexpr (MODE == MODE_BAND)
-          produce_T_band<DK>(a, ring(in, ch & 3), ring(buf, ch & 1).trp, ring(gr, ch & 3), xr);
-        else
-          produce_T<DK, MODE, CMP, MAXD>(a, ring(in, ch & 3), ring(buf, ch & 1).trp, ring(gr, ch & 3), cnt,
-                                         count);
-      }
       lds_barrier();
-    }
-    if constexpr (CMP == CMP_FP8) {
-      if (count) {
-        uint32_t v0 = wave_sum_u32(cnt.nonfinite), v1 = wave_sum_u32(cnt.sat_dyn);
-        uint32_t v2 = wave_sum_u32(cnt.sat_static), v3 = wave_sum_u32(cnt.underflow);
-        if (l == 0) {
-          if (v0) atomicAdd(a.stats + 0, (unsigned long long)v0);
-          if (v1) atomicAdd(a.stats + 1, (unsigned long long)v1);
-          if (v2) atomicAdd(a.stats + 2, (unsigned long long)v2);
-          if (v3) atomicAdd(a.stats + 3, (unsigned long long)v3);
-        }
+      for (int it = -1; it <= nchunks; ++it) {
+        const int ch = it + 1;
+        if (ch < nchunks) produce_T_band<DK>(a, ring(in, ch & 3), ring(buf, ch & 1).trp, ring(gr, ch & 3), xr);
+        lds_barrier();
+      }
+    } else {
+      // the pre-pass's packs of chunk ch sit at packs[(bh * nchunks + ch) * 6 * 64]; chunk
+      // it + 1 goes to LDS in iteration it, loaded one iteration earlier (register
+      // ping-pong, every load unconditional with the chunk index clamped, as the stager)
+      const bf16x8* hp = a.packs + (size_t)bh * nchunks * T_PACKS * WAVE + l;
+      auto clampc = [&](int ch) { return ch < last ? ch : last; };
+      auto load = [&](int ch, bf16x8 (&r)[T_PACKS]) {
+#pragma unroll
+        for (int k = 0; k < T_PACKS; ++k) r[k] = hp[((size_t)ch * T_PACKS + k) * WAVE];
+      };
+      auto store = [&](const bf16x8 (&r)[T_PACKS], bf16x8 (&trp)[CNT][2][WAVE]) {
+#pragma unroll
+        for (int I = 0; I < CNT; ++I)
+#pragma unroll
+          for (int p = 0; p < 2; ++p)
+            if (2 * p <= I) trp[I][p][l] = r[t_pack_index(I, p)];
+      };
+      bf16x8 r0[T_PACKS], r1[T_PACKS];
+      load(0, r0);
+      lds_barrier();
+      for (int it = -1; it <= nchunks; it += 2) {
+        // iteration it: chunk it + 1 (even) from r0, chunk it + 2 (odd) -> r1
+        load(clampc(it + 2), r1);
+        if (it + 1 < nchunks) store(r0, ring(buf, (it + 1) & 1).trp);
+        lds_barrier();
+        if (it + 1 > nchunks) break;
+        // iteration it + 1: chunk it + 2 (odd) from r1, chunk it + 3 (even) -> r0
+        load(clampc(it + 3), r0);
+        if (it + 2 < nchunks) store(r1, ring(buf, (it + 2) & 1).trp);
+        lds_barrier();
       }
     }
     return;
@@ -770,6 +728,10 @@ __global__ __launch_bounds__(NWAVES * WAVE, 1) void chunk_fwd_kernel(ChunkArgs a
       a.S_out[((size_t)bh * DK + sdim(A, g, r)) * a.dv + col0 + c] = sw.S[A][r];
 }
 
+bool chunk_fwd_band_path(int mode, int N, int mask, int cmp) {
+  return mode == MODE_NEUMANN && mask && N <= 3 && cmp == CMP_BF16;
+}
+
 int launch_chunk_fwd(const ChunkLaunch& p, hipStream_t s) {
   ChunkArgs a;
   a.Q = reinterpret_cast<const __bf16*>(p.Q);
@@ -780,7 +742,7 @@ int launch_chunk_fwd(const ChunkLaunch& p, hipStream_t s) {
   a.S0 = p.S0;
   a.O = p.O;
   a.S_out = p.S_out;
-  a.stats = p.stats;
+  a.packs = reinterpret_cast<const bf16x8*>(p.packs);
   a.T = p.T;
   a.BH = p.B * p.H;
   a.dv = p.d_v;
@@ -789,30 +751,26 @@ int launch_chunk_fwd(const ChunkLaunch& p, hipStream_t s) {
   a.scale = p.scale;
   const dim3 grid((unsigned)(a.BH * (p.d_v / DVS)));
   const dim3 block(NWAVES * WAVE);
-  const bool narrow = p.mode == 0 && p.mask && p.N <= 16;
-  const bool band = p.mode == 0 && p.mask && p.N <= 3;
-  auto go = [&](auto dk, auto mode, auto cmp, auto maxd) {
+  const bool band = chunk_fwd_band_path(p.mode, p.N, p.mask, p.cmp);
+  // with the band mask and N <= 16 the packs below the first sub-tile-diagonal are zero
+  const bool narrow = p.mode == MODE_NEUMANN && p.mask && p.N <= 16;
+  if (!band && !p.packs) return -1;
+  auto go = [&](auto dk, auto mode, auto maxd) {
     if (p.o_bf16)
-      hipLaunchKernelGGL((chunk_fwd_kernel<dk.value, mode.value, cmp.value, maxd.value, true>), grid,
-                         block, 0, s, a);
+      hipLaunchKernelGGL((chunk_fwd_kernel<dk.value, mode.value, CMP_BF16, maxd.value, true>), grid, block,
+                         0, s, a);
     else
-      hipLaunchKernelGGL((chunk_fwd_kernel<dk.value, mode.value, cmp.value, maxd.value, false>), grid,
-                         block, 0, s, a);
+      hipLaunchKernelGGL((chunk_fwd_kernel<dk.value, mode.value, CMP_BF16, maxd.value, false>), grid, block,
+                         0, s, a);
     return 0;
   };
-  using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
+  using MB = std::integral_constant<int, MODE_BAND>;
+  using ML = std::integral_constant<int, MODE_LOAD>;
   auto with_dk = [&](auto dk) -> int {
-    if (p.mode == 1) return go(dk, std::integral_constant<int, MODE_EXACT>{}, I1{}, I3{});
-    if (p.cmp == CMP_FP8)
-      return narrow ? go(dk, I0{}, I2{}, I1{}) : go(dk, I0{}, I2{}, I3{});
-    if (p.cmp == CMP_BF16) {
-      if (band) return go(dk, std::integral_constant<int, MODE_BAND>{}, I1{}, I1{});
-      return narrow ? go(dk, I0{}, I1{}, I1{}) : go(dk, I0{}, I1{}, I3{});
-    }
-    return -1;
+    if (band) return go(dk, MB{}, I1{});
+    return narrow ? go(dk, ML{}, I1{}) : go(dk, ML{}, I3{});
   };
   switch (p.d_k) {
     case 64: return with_dk(std::integral_constant<int, 64>{});

@@ -54,6 +54,12 @@ int launch_dense(const BlocksArgs& a, const void* T_in, int t_in_bf16, int mode,
                  const void* V, int d_v, int gate_k, void* T_out, int t_bf16, void* W_out, void* U_out,
                  int out_bf16, hipStream_t s);
 
+// T - I of every 64 x 64 block as the chunk forward's row packs (6 x 64 x 16 bytes per
+// block, store_T_packs): the pre-pass of every chunk-forward variant but the band path
+int launch_T_packs(const BlocksArgs& a, int mode, int N, int mask, int cmp, void* packs,
+                   unsigned long long* stats, hipStream_t s);
+constexpr size_t T_PACK_BYTES = 6 * 64 * 16;
+
 struct ChunkLaunch {
   const void* Q;
   const void* K;
@@ -63,14 +69,17 @@ struct ChunkLaunch {
   const float* S0;
   void* O;
   float* S_out;
-  unsigned long long* stats;
+  const void* packs;  // T - I row packs from the pre-pass (NULL on the band path)
   int64_t T;
   int B, H, d_k, d_v;
   int o_bf16;
   int mode, N, mask, cmp;
   float scale;
 };
-// chunk-wise forward, C = 64; d_k in {64, 128}; d_v a multiple of 32
+// chunk-wise forward, C = 64; d_k in {64, 128}; d_v a multiple of 32.  The band path
+// (Neumann, mask, N <= 3, bf16) forms T - I itself; every other variant reads the row
+// packs the pre-pass wrote (p.packs).
+bool chunk_fwd_band_path(int mode, int N, int mask, int cmp);
 int launch_chunk_fwd(const ChunkLaunch& p, hipStream_t s);
 
 struct DecodeLaunch {

@@ -77,7 +77,8 @@ __global__ __launch_bounds__(256) void build_A_kernel(BlocksArgs a, float* __res
 
 // The inverse: one wave per block.  MAXD is the largest tile distance I - J kept
 // (NT - 1 in general, 1 for the band-masked sum with N <= 16).
-template <int NT, int SRC, int DK, int CMP, int MODE, int MAXD>
+// PK: write T - I as the chunk forward's row packs (store_T_packs) instead of T.
+template <int NT, int SRC, int DK, int CMP, int MODE, int MAXD, bool PK = false>
 __global__ __launch_bounds__(256) void inverse_kernel(BlocksArgs a, int N, int mask, void* T_out,
                                                       int t_bf16, unsigned long long* stats, int S) {
   constexpr int C = 16 * NT;
@@ -101,10 +102,14 @@ __global__ __launch_bounds__(256) void inverse_kernel(BlocksArgs a, int N, int m
     neumann_T_i8<NT, MAXD>(AD, AT, N, mask != 0, TT);
   else
     neumann_T<NT, CMP, MAXD>(AD, AT, N, mask != 0, TT, cnt, count);
-  if (t_bf16)
+  if constexpr (PK) {
+    static_assert(NT == 4, "row packs of 64 x 64 blocks");
+    store_T_packs(reinterpret_cast<bf16x8*>(T_out) + (size_t)blk * T_PACKS * WAVE, TT);
+  } else if (t_bf16) {
     store_T_bf16<NT, MAXD>(reinterpret_cast<__bf16*>(T_out) + (size_t)blk * C * C, TT);
-  else
+  } else {
     store_T_f32<NT, MAXD>(reinterpret_cast<float*>(T_out) + (size_t)blk * C * C, TT);
+  }
   if constexpr (CMP == CMP_FP8) {
     if (count) flush_counts(cnt, stats);
   }
@@ -271,6 +276,43 @@ int launch_exact(const BlocksArgs& a, int src, int cmp, void* T_out, int t_bf16,
       default: return -1;
     }
   });
+}
+
+// T - I of every 64 x 64 block as row packs (the chunk forward's pre-pass): bf16 keys,
+// d_k 64 or 128; mode 0 (Neumann, bf16 or fp8 products) or 1 (exact doubling, bf16)
+int launch_T_packs(const BlocksArgs& a, int mode, int N, int mask, int cmp, void* packs,
+                   unsigned long long* stats, hipStream_t s) {
+  if (a.C != 64) return -1;
+  auto go = [&](auto dk, auto cm, auto md, auto maxd) {
+    hipLaunchKernelGGL((inverse_kernel<4, SRC_K_BF16, dk.value, cm.value, md.value, maxd.value, true>),
+                       grid_for(a.n_blocks), dim3(WAVE * WAVES_PER_WG), 0, s, a, N, mask, packs, 0,
+                       stats, 0);
+    return 0;
+  };
+  using M1 = std::integral_constant<int, 1>;
+  using M3 = std::integral_constant<int, 3>;
+  auto with_dk = [&](auto dk) -> int {
+    if (mode == 1) {
+      if (cmp != CMP_BF16) return -1;
+      return go(dk, std::integral_constant<int, CMP_BF16>{}, std::integral_constant<int, MODE_EXACT>{}, M3{});
+    }
+    const bool narrow = mask && N <= 16;
+    using MN = std::integral_constant<int, MODE_NEUMANN>;
+    if (cmp == CMP_BF16) {
+      using CB = std::integral_constant<int, CMP_BF16>;
+      return narrow ? go(dk, CB{}, MN{}, M1{}) : go(dk, CB{}, MN{}, M3{});
+    }
+    if (cmp == CMP_FP8) {
+      using CF = std::integral_constant<int, CMP_FP8>;
+      return narrow ? go(dk, CF{}, MN{}, M1{}) : go(dk, CF{}, MN{}, M3{});
+    }
+    return -1;
+  };
+  switch (a.d_k) {
+    case 64: return with_dk(std::integral_constant<int, 64>{});
+    case 128: return with_dk(std::integral_constant<int, 128>{});
+    default: return -1;
+  }
 }
 
 // parallel residual correction on the Neumann sum: fp32 products throughout

@@ -908,4 +908,26 @@ __device__ __forceinline__ void store_T_bf16(__bf16* __restrict__ out, const Mat
     }
 }
 
+// T - I of a 64 x 64 block as the six left-operand row packs of the chunk forward's
+// product (T - I) Y: pack k <-> (I, p) in the order (0,0) (1,0) (2,0) (2,1) (3,0) (3,1),
+// tiles (I, 2p) and (I, 2p + 1) in T-form, 16 bytes per lane at out[64 k + lane].  The
+// packs with 2p > I lie above the diagonal and are not stored.
+constexpr int T_PACKS = 6;
+
+__device__ __forceinline__ int t_pack_index(int I, int p) { return I <= 1 ? I : 2 * I - 2 + p; }
+
+__device__ __forceinline__ void store_T_packs(bf16x8* __restrict__ out, const Mat<4>& TT) {
+  const int l = lane_id();
+  const f32x4 e = eye_tile();
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      if (2 * p > I) continue;
+      const f32x4 t0 = (2 * p == I) ? TT.t[I][2 * p] - e : TT.t[I][2 * p];
+      const f32x4 t1 = (2 * p + 1 == I) ? TT.t[I][2 * p + 1] - e : tile_or_zero(TT, I, 2 * p + 1);
+      out[WAVE * t_pack_index(I, p) + l] = pack8(t0, t1);
+    }
+}
+
 }  // namespace gdn
