@@ -211,6 +211,24 @@ gdn_status gdn_chunk_fwd(const void* Q, const void* K, const void* V, int32_t qk
                          const gdn_inverse_cfg* inv, void* workspace, size_t workspace_bytes,
                          gdn_fp8_stats* stats, void* stream);
 
+/* gdn_chunk_fwd without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The workspace the variant needs (gdn_chunk_fwd_workspace_bytes) comes
+ * from a fixed device array inside the library, GDN_NOALLOC_SCRATCH_BYTES per GPU,
+ * held from library load until the process ends; a call needing more returns
+ * GDN_ERR_WORKSPACE before enqueuing anything (64 MiB covers 10922 chunks of 64, e.g.
+ * B*H = 64 heads of 8192 tokens).  The call allocates nothing.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (concurrent streams or
+ * threads) race on it and must be serialised by the caller.  Arguments, results and
+ * errors otherwise as gdn_chunk_fwd (GDN_ERR_HIP if the array's device address
+ * cannot be obtained). */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+gdn_status gdn_chunk_fwd_noalloc(const void* Q, const void* K, const void* V, int32_t qkv_dtype,
+                                 const float* beta, const float* g, const float* S0, void* O,
+                                 int32_t o_dtype, float* S_out, int32_t B, int32_t H, int64_t T,
+                                 int32_t d_k, int32_t d_v, int32_t C, float scale,
+                                 const gdn_inverse_cfg* inv, gdn_fp8_stats* stats, void* stream);
+
 /* The gated delta rule one token at a time (decode).  Per (b, h), tokens t = 0..n-1 in
  * order, a = exp(g_t), state S [d_k][d_v] fp32 entering as S_in (zeros if NULL):
  *   r = S^T k_t, p = S^T q_t;  u = beta_t (v_t - a r);  S <- a S + k_t u^T;

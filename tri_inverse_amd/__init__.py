@@ -72,13 +72,17 @@ _lib.gdn_chunk_fwd.restype = _i32
 _lib.gdn_chunk_fwd.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
                                _i64, _i32, _i32, _i32, _f32, _P(gdn_inverse_cfg), _vp, ctypes.c_size_t,
                                _vp, _vp]
+_lib.gdn_chunk_fwd_noalloc.restype = _i32
+_lib.gdn_chunk_fwd_noalloc.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
+                                       _i64, _i32, _i32, _i32, _f32, _P(gdn_inverse_cfg), _vp, _vp]
 _lib.gdn_decode.restype = _i32
 _lib.gdn_decode.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                             _i32, _i32, _f32, _vp]
 
 EXPORTED = ("gdn_abi_version", "gdn_status_string", "gdn_build_A", "gdn_tri_inverse_neumann",
             "gdn_tri_inverse_exact", "gdn_tri_inverse_residual", "gdn_tri_inverse_fs", "gdn_wy",
-            "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_decode")
+            "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_decode")
+GDN_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class GdnError(RuntimeError):
@@ -323,6 +327,42 @@ def gdn_chunk_fwd(Q, K, V, beta, g, C: int = 64, scale: float | None = None, S0=
                             float(scale), ctypes.byref(cfg), _ptr(workspace), ws_bytes, _ptr(stats),
                             _stream(stream))
     _check(st, "gdn_chunk_fwd")
+    return O, S_out
+
+
+def gdn_chunk_fwd_noalloc(Q, K, V, beta, g, C: int = 64, scale: float | None = None, S0=None,
+                          mode="neumann", N: int = 3, mask: bool = True, compute="bf16",
+                          o_dtype=torch.bfloat16, stats=None, O=None, S_out=None, stream=None):
+    """gdn_chunk_fwd with the library's fixed device scratch instead of a workspace
+    (for callers that cannot allocate).  Arguments and results as gdn_chunk_fwd; O and
+    S_out are still the caller's (pass them to allocate nothing here either)."""
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
+        _dev(t, n, (torch.bfloat16,))
+    _dev(beta, "beta", (torch.float32,))
+    _dev(g, "g", (torch.float32,))
+    if K.dim() != 4 or Q.shape != K.shape:
+        raise ValueError("Q and K must both be [B, H, T, d_k]")
+    B, H, T, dk = K.shape
+    dv = V.shape[-1]
+    if V.shape[:3] != (B, H, T) or beta.shape != (B, H, T) or g.shape != (B, H, T):
+        raise ValueError("V, beta, g must match Q/K in [B, H, T]")
+    if S0 is not None:
+        _dev(S0, "S0", (torch.float32,))
+    if O is None:
+        O = torch.empty((B, H, T, dv), device=K.device, dtype=o_dtype)
+    if S_out is None:
+        S_out = torch.empty((B, H, dk, dv), device=K.device, dtype=torch.float32)
+    _dev(O, "O", (torch.float32, torch.bfloat16))
+    _dev(S_out, "S_out", (torch.float32,))
+    if stats is not None:
+        _dev(stats, "stats", (torch.int64,))
+    if scale is None:
+        scale = dk ** -0.5
+    cfg = _inv_cfg(mode, N, mask, compute)
+    st = _lib.gdn_chunk_fwd_noalloc(_ptr(Q), _ptr(K), _ptr(V), GDN_BF16, _ptr(beta), _ptr(g), _ptr(S0),
+                                    _ptr(O), _TORCH_DTYPE[O.dtype], _ptr(S_out), B, H, T, dk, dv, C,
+                                    float(scale), ctypes.byref(cfg), _ptr(stats), _stream(stream))
+    _check(st, "gdn_chunk_fwd_noalloc")
     return O, S_out
 
 

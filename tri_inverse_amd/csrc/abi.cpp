@@ -284,6 +284,55 @@ gdn_status gdn_chunk_fwd(const void* Q, const void* K, const void* V, int32_t qk
                          int32_t d_k, int32_t d_v, int32_t C, float scale,
                          const gdn_inverse_cfg* inv, void* workspace, size_t workspace_bytes,
                          gdn_fp8_stats* stats, void* stream) {
+  return gdn::chunk_fwd_impl(Q, K, V, qkv_dtype, beta, g, S0, O, o_dtype, S_out, B, H, T, d_k, d_v, C,
+                             scale, inv, workspace, workspace_bytes, nullptr, stats, stream);
+}
+
+gdn_status gdn_decode(const void* Q, const void* K, const void* V, int32_t qkv_dtype,
+                      const float* beta, const float* g, const float* S_in, float* S_out,
+                      void* O, int32_t o_dtype, int32_t B, int32_t H, int32_t n,
+                      int32_t d_k, int32_t d_v, float scale, void* stream) {
+  if (B < 0 || H < 0 || n < 0 || d_k <= 0 || d_v <= 0) return GDN_ERR_BAD_SHAPE;
+  if (qkv_dtype != GDN_BF16 && qkv_dtype != GDN_F32) return GDN_ERR_BAD_DTYPE;
+  if (o_dtype != GDN_F32 && o_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
+  if (!(d_k == 64 || d_k == 128)) return GDN_ERR_UNSUPPORTED;
+  if (d_v % 32 != 0 || d_v > 256) return GDN_ERR_UNSUPPORTED;
+  if ((int64_t)B * H == 0) return GDN_OK;
+  if (!S_out) return GDN_ERR_NULL_POINTER;
+  if (n > 0 && (!Q || !K || !V || !beta || !g || !O)) return GDN_ERR_NULL_POINTER;
+  for (const void* p : {Q, K, V, (const void*)beta, (const void*)g, (const void*)S_in,
+                        (const void*)S_out, (const void*)O})
+    if (p && !aligned16(p)) return GDN_ERR_BAD_ALIGNMENT;
+  gdn::DecodeLaunch p;
+  p.Q = Q;
+  p.K = K;
+  p.V = V;
+  p.beta = beta;
+  p.g = g;
+  p.S_in = S_in;
+  p.S_out = S_out;
+  p.O = O;
+  p.B = B;
+  p.H = H;
+  p.n = n;
+  p.d_k = d_k;
+  p.d_v = d_v;
+  p.in_bf16 = qkv_dtype == GDN_BF16;
+  p.o_bf16 = o_dtype == GDN_BF16;
+  p.scale = scale;
+  return launch_result(gdn::launch_decode(p, as_stream(stream)));
+}
+
+}  // extern "C"
+
+namespace gdn {
+
+gdn_status chunk_fwd_impl(const void* Q, const void* K, const void* V, int32_t qkv_dtype,
+                          const float* beta, const float* g, const float* S0, void* O,
+                          int32_t o_dtype, float* S_out, int32_t B, int32_t H, int64_t T,
+                          int32_t d_k, int32_t d_v, int32_t C, float scale,
+                          const gdn_inverse_cfg* inv, void* workspace, size_t workspace_bytes,
+                          void* (*workspace_of_device)(size_t need), gdn_fp8_stats* stats, void* stream) {
   gdn_status st = check_chunk_args(qkv_dtype, o_dtype, B, H, T, d_k, d_v, C, inv);
   if (st != GDN_OK) return st;
   if (stats && !aligned16(stats)) return GDN_ERR_BAD_ALIGNMENT;
@@ -297,7 +346,15 @@ gdn_status gdn_chunk_fwd(const void* Q, const void* K, const void* V, int32_t qk
         !aligned16(O) || !aligned16(S_out) || (S0 && !aligned16(S0)))
       return GDN_ERR_BAD_ALIGNMENT;
     if (need > 0) {
-      if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
+      if (workspace_of_device) {
+        // no workspace argument: the caller's resolver supplies it (NULL if need exceeds
+        // what it holds, or if the HIP runtime failed; it reports which)
+        if (need > workspace_bytes) return GDN_ERR_WORKSPACE;
+        workspace = workspace_of_device(need);
+        if (!workspace) return GDN_ERR_HIP;
+      } else if (!workspace || workspace_bytes < need) {
+        return GDN_ERR_WORKSPACE;
+      }
       if (!aligned16(workspace)) return GDN_ERR_BAD_ALIGNMENT;
     }
   }
@@ -345,39 +402,4 @@ gdn_status gdn_chunk_fwd(const void* Q, const void* K, const void* V, int32_t qk
   return launch_result(gdn::launch_chunk_fwd(p, s));
 }
 
-gdn_status gdn_decode(const void* Q, const void* K, const void* V, int32_t qkv_dtype,
-                      const float* beta, const float* g, const float* S_in, float* S_out,
-                      void* O, int32_t o_dtype, int32_t B, int32_t H, int32_t n,
-                      int32_t d_k, int32_t d_v, float scale, void* stream) {
-  if (B < 0 || H < 0 || n < 0 || d_k <= 0 || d_v <= 0) return GDN_ERR_BAD_SHAPE;
-  if (qkv_dtype != GDN_BF16 && qkv_dtype != GDN_F32) return GDN_ERR_BAD_DTYPE;
-  if (o_dtype != GDN_F32 && o_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
-  if (!(d_k == 64 || d_k == 128)) return GDN_ERR_UNSUPPORTED;
-  if (d_v % 32 != 0 || d_v > 256) return GDN_ERR_UNSUPPORTED;
-  if ((int64_t)B * H == 0) return GDN_OK;
-  if (!S_out) return GDN_ERR_NULL_POINTER;
-  if (n > 0 && (!Q || !K || !V || !beta || !g || !O)) return GDN_ERR_NULL_POINTER;
-  for (const void* p : {Q, K, V, (const void*)beta, (const void*)g, (const void*)S_in,
-                        (const void*)S_out, (const void*)O})
-    if (p && !aligned16(p)) return GDN_ERR_BAD_ALIGNMENT;
-  gdn::DecodeLaunch p;
-  p.Q = Q;
-  p.K = K;
-  p.V = V;
-  p.beta = beta;
-  p.g = g;
-  p.S_in = S_in;
-  p.S_out = S_out;
-  p.O = O;
-  p.B = B;
-  p.H = H;
-  p.n = n;
-  p.d_k = d_k;
-  p.d_v = d_v;
-  p.in_bf16 = qkv_dtype == GDN_BF16;
-  p.o_bf16 = o_dtype == GDN_BF16;
-  p.scale = scale;
-  return launch_result(gdn::launch_decode(p, as_stream(stream)));
-}
-
-}  // extern "C"
+}  // namespace gdn

@@ -81,6 +81,20 @@ struct ChunkLaunch {
 // packs the pre-pass wrote (p.packs).
 bool chunk_fwd_band_path(int mode, int N, int mask, int cmp);
 int launch_chunk_fwd(const ChunkLaunch& p, hipStream_t s);
+}  // namespace gdn
+
+#include "gdn.h"
+namespace gdn {
+// gdn_chunk_fwd's validation and launches.  With workspace_of_device == NULL the
+// workspace arguments are the caller's; otherwise workspace_bytes is the most the
+// resolver can supply and the resolver returns device memory of at least `need` bytes
+// for the current device (NULL if the HIP runtime failed).
+gdn_status chunk_fwd_impl(const void* Q, const void* K, const void* V, int32_t qkv_dtype,
+                          const float* beta, const float* g, const float* S0, void* O,
+                          int32_t o_dtype, float* S_out, int32_t B, int32_t H, int64_t T,
+                          int32_t d_k, int32_t d_v, int32_t C, float scale,
+                          const gdn_inverse_cfg* inv, void* workspace, size_t workspace_bytes,
+                          void* (*workspace_of_device)(size_t need), gdn_fp8_stats* stats, void* stream);
 
 struct DecodeLaunch {
   const void* Q;
