@@ -94,7 +94,10 @@ __global__ __launch_bounds__(256) void inverse_kernel(BlocksArgs a, int N, int m
   in.load(a, blk);
   Mat<NT> AD, AT, TT;
   in.template to_A<MAXD, BANDED>(a, BANDED ? band : -1, AD, AT);
-  if constexpr (MODE == MODE_EXACT)
+  if constexpr (MODE == MODE_EXACT && NT == 4 && CMP == CMP_BF16) {
+    __shared__ __bf16 xt[4][64][XT_LD];  // per wave: X^T for the transpose read
+    doubling_T_lds(AD, AT, TT, xt[threadIdx.x / WAVE]);
+  } else if constexpr (MODE == MODE_EXACT)
     doubling_T<NT, CMP>(AD, AT, TT);
   else if constexpr (MODE == MODE_RESIDUAL)
     residual_T<NT>(AD, AT, N, mask != 0, S, TT);

@@ -877,6 +877,103 @@ __device__ __forceinline__ void doubling_T(const Mat<NT>& AD, const Mat<NT>& AT,
   }
 }
 
+// Exact doubling at C = 64 on bf16 products, the method's m - 1 squarings and m - 1
+// products and no more: P = I + A; for q = 1..m-1: X <- X X (D-form); P <- P + P X.
+// A product needs its left factor in T-form and its right factor in D-form, so the
+// square is formed once (D-form) and its T-form row packs are read back from a bf16 copy
+// of X^T in LDS (xt: this wave's 64 x XT_LD scratch) with the transpose read.  Tiles
+// that Lemma 3.1 makes zero are skipped: X = A^d vanishes below sub-diagonal d, so
+// tile (I, J) of X is zero when 16 (I - J) + 15 < d, and a product's tile (I, J) only
+// sums over the tiles K where both factors can be non-zero.  P + P X accumulates onto
+// P's own tile inside the MFMA.
+constexpr int XT_LD = 72;  // bf16 row stride of the X^T scratch (64 + 8: bank spread)
+
+// first and last tile index K of a product's tile (I, J) given the smallest non-zero tile
+// distance of the left (kl) and right (kr) factor
+__device__ __forceinline__ constexpr int tile_kmin(int J, int kr) { return J + kr; }
+__device__ __forceinline__ constexpr int tile_kmax(int I, int kl) { return I - kl; }
+// smallest tile distance I - J at which A^d can be non-zero (entries only at i - j >= d)
+__device__ __forceinline__ constexpr int tile_dist(int d) { return d <= 15 ? 0 : (d - 15 + 15) / 16; }
+
+__device__ __forceinline__ void doubling_T_lds(const Mat<4>& AD, const Mat<4>& AT, Mat<4>& PT,
+                                               __bf16 (*xt)[XT_LD]) {
+  constexpr int NT = 4, NP = 2;
+  const int l = lane_id(), g = l >> 4, c = l & 15;
+  bf16x8 xr[NT][NP], xc[NP][NT];  // row packs (T-form) and column packs (D-form) of X
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int p = 0; p < NP; ++p) xr[I][p] = pack8(tile_or_zero(AT, I, 2 * p), tile_or_zero(AT, I, 2 * p + 1));
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int J = 0; J < NT; ++J) xc[p][J] = pack8(tile_or_zero(AD, 2 * p, J), tile_or_zero(AD, 2 * p + 1, J));
+  PT = AT;
+  add_eye(PT);
+#pragma unroll
+  for (int q = 1; q < 6; ++q) {
+    const int d = 1 << (q - 1);  // X = A^d
+    const int kx = tile_dist(d), kx2 = tile_dist(2 * d);
+    // X <- X X (D-form)
+    Mat<NT> XD;
+#pragma unroll
+    for (int I = 0; I < NT; ++I)
+#pragma unroll
+      for (int J = 0; J <= I; ++J) {
+        f32x4 acc = zero4();
+        if (I - J >= kx2) {
+          const int k0 = tile_kmin(J, kx), k1 = tile_kmax(I, kx);
+#pragma unroll
+          for (int p = 0; p < NP; ++p)
+            if (2 * p + 1 >= k0 && 2 * p <= k1) acc = mma_bf16(xr[I][p], xc[p][J], acc);
+        }
+        XD.t[I][J] = acc;
+      }
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int J = 0; J < NT; ++J) xc[p][J] = pack8(tile_or_zero(XD, 2 * p, J), tile_or_zero(XD, 2 * p + 1, J));
+    // P <- P + P X (T-form: operands swapped), accumulated onto P's tile
+    bf16x8 pr[NT][NP];
+#pragma unroll
+    for (int I = 0; I < NT; ++I)
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+        if (2 * p <= I) pr[I][p] = pack8(tile_or_zero(PT, I, 2 * p), tile_or_zero(PT, I, 2 * p + 1));
+#pragma unroll
+    for (int I = 0; I < NT; ++I)
+#pragma unroll
+      for (int J = 0; J <= I; ++J) {
+        if (I - J < kx2) continue;  // (P X)(I, J) needs K - J >= kx2 with K <= I
+        const int k0 = tile_kmin(J, kx2), k1 = I;
+        f32x4 acc = PT.t[I][J];
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+          if (2 * p + 1 >= k0 && 2 * p <= k1) acc = mma_bf16(xc[p][J], pr[I][p], acc);
+        PT.t[I][J] = acc;
+      }
+    if (q < 5) {
+      // the new X's row packs: its column packs hold X^T's rows 16J + c, columns
+      // 32p + 16h + 4g .. +3; write them and read the T-form back transposed
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int J = 0; J < NT; ++J) {
+          const u32x4 w = __builtin_bit_cast(u32x4, xc[p][J]);
+          *reinterpret_cast<u32x2*>(&xt[16 * J + c][32 * p + 4 * g]) = u32x2{w[0], w[1]};
+          *reinterpret_cast<u32x2*>(&xt[16 * J + c][32 * p + 16 + 4 * g]) = u32x2{w[2], w[3]};
+        }
+#pragma unroll
+      for (int I = 0; I < NT; ++I)
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          const __bf16* b0 = &xt[32 * p + 4 * g + (c >> 2)][16 * I + 4 * (c & 3)];
+          xr[I][p] = join8(lds_read_tr4(b0), lds_read_tr4(b0 + 16 * XT_LD));
+        }
+    }
+  }
+}
+
 // ---- stores ------------------------------------------------------------------
 // T-form tile (I,J): lane (g,c) holds row 16I + c, columns 16J + 4g .. +3.
 
