@@ -151,6 +151,8 @@ def bench_c1(torch, tri, synth, steps, warmup):
                 ("neumann", 3, False, torch.float32), ("neumann", 4, False, torch.float32),
                 ("exact", 0, False, torch.float32), ("exact", 0, False, torch.bfloat16),
                 ("neumann", 3, True, torch.bfloat16), ("residual", 3, True, torch.float32, 8),
+                ("residual", 3, True, torch.float32, 0), ("residual", 3, True, torch.float32, 1),
+                ("residual", 3, True, torch.float32, 2), ("residual", 3, True, torch.float32, 4),
                 ("int8", 3, True, torch.float32), ("int8", 3, False, torch.float32)]
     for v in variants:
         name = ("exact" if v[0] == "exact" else "N%d_%s" % (v[1], "masked" if v[2] else "unmasked"))
@@ -258,7 +260,8 @@ def bench_chunk(torch, tri, synth, cfg, variants, steps, warmup, n_sets=2, stats
                               S_out=outs[i][1], stats=st, workspace=ws)
         ms, _ = time_launches(torch, launch, n_sets, steps, warmup)
         tok, by, fl = chunk_bytes_flops(cfg, v)
-        name = ("exact" if mode == "exact" else "N%d_%s" % (N, "masked" if mask else "unmasked")) + "_" + compute
+        name = ("exact" if mode == "exact" else "N%d_%s" % (N, "masked" if mask else "unmasked"))
+        name += ("_products" if mode == "neumann_products" else "") + "_" + compute
         res[name] = {"ms_per_step": ms, "tokens_per_s": tok / (ms * 1e-3),
                      "hbm_frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "mfma_frac": fl / (ms * 1e-3) / 1e12 / (FP8_PEAK_TFLOPS if compute == "fp8" else BF16_PEAK_TFLOPS),
@@ -425,9 +428,49 @@ def profile_decode(torch, tri, synth, n):
     torch.cuda.synchronize()
 
 
-def cpu_baseline_c1():
+def _err_summary(X, R, is_T=True):
+    """Error of X against R (stacks of blocks, fp64): relative Frobenius over the stack and
+    over X - I (is_T: inverses only), SNR in dB, and per-block relative Frobenius quantiles."""
+    import numpy as np
+    d = X - R
+    nr = float(np.linalg.norm(R))
+    nd = float(np.linalg.norm(d))
+    per = np.linalg.norm(d.reshape(d.shape[0], -1), axis=1) / np.maximum(
+        np.linalg.norm(R.reshape(R.shape[0], -1), axis=1), 1e-300)
+    out = {"relF": nd / nr if nr > 0 else 0.0,
+           "snr_db": (10 * np.log10(nr ** 2 / nd ** 2)) if nd > 0 else None,
+           "block_relF_p50": float(np.percentile(per, 50)), "block_relF_p90": float(np.percentile(per, 90)),
+           "block_relF_p99": float(np.percentile(per, 99)), "block_relF_max": float(per.max())}
+    if is_T:
+        eye = np.eye(X.shape[-1])
+        den = float(np.linalg.norm(R - eye))
+        out["relF_T_minus_I"] = float(np.linalg.norm(d) / den) if den > 0 else 0.0
+    return out
+
+
+def cpu_baseline_and_accuracy(torch, tri, synth):
+    """The oracle (fp64, plain loops, OpenMP over blocks or heads) on the host cores.
+
+    cpu_baseline: timed on the full headline workload (A build + N=3 masked Neumann),
+    plus one thread on 256 of its blocks, plus the chunk forward on 4 prefill heads.
+
+    accuracy, on bounded samples of the same workloads (same generators and shapes):
+      c1: the first 256 blocks of the headline input.  approx_vs_exact: the method's own
+          error, each truncated variant (and the residual correction's S sweep) against
+          the exact inverse, all in fp64 (oracle only); gpu_vs_oracle: the GPU's T against
+          the oracle running the same algorithm on the same blocks.
+      fp8: 256 chunks shaped like the seq-32768 prefill (4 heads x 64 chunks of the
+          prefill generator): the e4m3 chain's T against the unquantised fp64 sum and
+          against the exact inverse (error distribution), against the oracle's e4m3
+          emulation, and the counters of both.
+      c3: 4 prefill heads of 8192 tokens: O and S of the masked N=3 forward against the
+          exact-inverse forward (oracle), and the GPU's against the oracle's."""
+    import numpy as np
     import oracle
-    import synth
+
+    def f64(t):
+        return t.detach().cpu().double().numpy()
+
     n_blocks = C1["B"] * C1["H"] * C1["T"] // C1["C"]
     inp = synth.blocks(1, n_blocks, C1["C"], C1["d_k"], k_dtype="bf16")
     K = inp["K"].double().numpy()
@@ -443,27 +486,97 @@ def cpu_baseline_c1():
             break
     dt = time.perf_counter() - t0
     cores = oracle.max_threads()
-    # one thread, on the first 256 blocks of the same workload (about 2 s)
     sub = slice(0, 256)
     oracle.set_threads(1)
     try:
         reps1 = 0
         t1 = time.perf_counter()
         while True:
-            A = oracle.build_A(K[sub], beta[sub], g[sub])
-            oracle.neumann(A, 3, True)
+            A1 = oracle.build_A(K[sub], beta[sub], g[sub])
+            oracle.neumann(A1, 3, True)
             reps1 += 1
             if time.perf_counter() - t1 > 2.0 or reps1 >= 100:
                 break
         dt1 = time.perf_counter() - t1
     finally:
         oracle.set_threads(cores)
-    return {"value": reps * n_blocks / dt, "unit": "blocks/s", "cores": cores,
-            "kind": "oracle",
-            "sample": "the full 2048-block workload (A build + N=3 masked Neumann, fp64), "
-                      "%d pass(es), %.1f s" % (reps, dt),
-            "single_thread": {"value": reps1 * 256 / dt1, "unit": "blocks/s",
-                              "sample": "256 of the 2048 blocks, %d pass(es), %.1f s" % (reps1, dt1)}}
+    # chunk forward: 4 heads of the prefill workload
+    xc = synth.prefill(3, 1, 4, C3["T"], C3["d_k"], C3["d_v"])
+    x64 = [xc[k].double().numpy() for k in ("Q", "K", "V", "beta", "g")]
+    scale = C3["d_k"] ** -0.5
+    tc = time.perf_counter()
+    Or, Sr = oracle.chunk_fwd(*x64, C=64, scale=scale, inv_mode=oracle.INV_NEUMANN, N=3, mask=True)
+    dtc = time.perf_counter() - tc
+    cpu = {"value": reps * n_blocks / dt, "unit": "blocks/s", "cores": cores, "kind": "oracle",
+           "sample": "the full 2048-block workload (A build + N=3 masked Neumann, fp64), "
+                     "%d pass(es), %.1f s" % (reps, dt),
+           "single_thread": {"value": reps1 * 256 / dt1, "unit": "blocks/s",
+                             "sample": "256 of the 2048 blocks, %d pass(es), %.1f s" % (reps1, dt1)},
+           "chunk_fwd": {"value": (4 / C3["H"]) * C3["T"] / dtc, "unit": "tokens/s",
+                         "sample": "4 heads of the B=4 H=16 seq-8192 prefill (N=3 masked, fp64), one "
+                                   "pass of %.2f s; tokens counted as in the GPU figure (B x seq, "
+                                   "all 16 heads), so 4 heads are a quarter of a token row" % dtc}}
+
+    acc = {}
+    # ---- c1 sample: approximation against exact, GPU against oracle
+    A64 = A[sub]
+    T_ex = oracle.fs_inverse(A64)
+    Kd, bd, gd = inp["K"][sub].cuda(), inp["beta"][sub].cuda(), inp["g"][sub].cuda()
+    c1acc = {}
+    for N in (2, 3, 4):
+        for mask in (True, False):
+            Tm = oracle.neumann(A64, N, mask)
+            Tg = tri.gdn_tri_inverse_neumann(K=Kd, beta=bd, g=gd, C=64, N=N, mask=mask, compute="bf16")
+            torch.cuda.synchronize()
+            c1acc["N%d_%s" % (N, "masked" if mask else "unmasked")] = {
+                "approx_vs_exact": _err_summary(Tm, T_ex), "gpu_vs_oracle": _err_summary(f64(Tg), Tm)}
+    Tg = tri.gdn_tri_inverse_exact(K=Kd, beta=bd, g=gd, C=64, compute="bf16")
+    torch.cuda.synchronize()
+    c1acc["exact"] = {"approx_vs_exact": _err_summary(oracle.doubling(A64), T_ex),
+                      "gpu_vs_oracle": _err_summary(f64(Tg), oracle.doubling(A64))}
+    for S in (0, 1, 2, 4, 8):
+        Tm = oracle.residual(A64, 3, True, S)
+        Tg = tri.gdn_tri_inverse_residual(K=Kd, beta=bd, g=gd, C=64, N=3, mask=True, S=S, compute="f32")
+        torch.cuda.synchronize()
+        c1acc["N3_masked_residual_S%d" % S] = {"approx_vs_exact": _err_summary(Tm, T_ex),
+                                               "gpu_vs_oracle": _err_summary(f64(Tg), Tm)}
+    acc["c1_sample_256_blocks"] = c1acc
+    # ---- fp8: prefill-shaped chunks
+    xf = synth.prefill(4, 1, 4, 4096, 128, 128)
+    nbf = 4 * 4096 // 64
+    Kf = xf["K"].reshape(nbf, 64, 128)
+    bf = xf["beta"].reshape(nbf, 64)
+    gf = xf["g"].reshape(nbf, 64)
+    Af = oracle.build_A(Kf.double().numpy(), bf.double().numpy(), gf.double().numpy())
+    Tf_ex = oracle.fs_inverse(Af)
+    f8 = {}
+    st = torch.zeros(4, dtype=torch.int64, device="cuda")
+    for mask in (True, False):
+        Tg = tri.gdn_tri_inverse_neumann(K=Kf.cuda(), beta=bf.cuda(), g=gf.cuda(), C=64, N=3, mask=mask,
+                                         compute="fp8", stats=st)
+        torch.cuda.synchronize()
+        Tg = f64(Tg)
+        Te, cnt, amax = oracle.neumann_fp8(Af.astype(np.float32).astype(np.float64), 3, mask)
+        f8["N3_%s" % ("masked" if mask else "unmasked")] = {
+            "vs_fp64_same_algorithm": _err_summary(Tg, oracle.neumann(Af, 3, mask)),
+            "vs_exact": _err_summary(Tg, Tf_ex),
+            "vs_e4m3_emulation": _err_summary(Tg, Te),
+            "counters_gpu": dict(zip(tri.FP8_STATS_FIELDS, st.cpu().tolist())),
+            "counters_emulation": dict(zip(tri.FP8_STATS_FIELDS, [int(v) for v in cnt.sum(axis=0)])),
+            "absmax_mean": {"A": float(amax[:, 0].mean()), "X_2": float(amax[:, 2].mean()),
+                            "X_3": float(amax[:, 3].mean())}}
+    acc["fp8_sample_256_prefill_chunks"] = f8
+    # ---- c3 sample: O and S
+    Oe, Se = oracle.chunk_fwd(*x64, C=64, scale=scale, inv_mode=oracle.INV_EXACT)
+    Og, Sg = tri.gdn_chunk_fwd(*(xc[k].cuda() for k in ("Q", "K", "V", "beta", "g")), C=64, scale=scale,
+                               N=3, mask=True)
+    torch.cuda.synchronize()
+    acc["c3_sample_4_heads"] = {
+        "approx_vs_exact_O": _err_summary(Or[0], Oe[0], False),
+        "approx_vs_exact_S": _err_summary(Sr[0], Se[0], False),
+        "gpu_vs_oracle_O": _err_summary(f64(Og)[0], Or[0], False),
+        "gpu_vs_oracle_S": _err_summary(f64(Sg)[0], Sr[0], False)}
+    return cpu, acc
 
 
 def main():
@@ -526,9 +639,20 @@ def main():
     }
     if args.only in ("all", "c3"):
         c3 = bench_chunk(torch, tri, synth, C3,
-                         [("neumann", 3, True, "bf16"), ("neumann", 3, False, "bf16"),
-                          ("exact", 0, False, "bf16")], max(5, args.steps // 5), 2)
+                         [("neumann", 3, True, "bf16"), ("neumann_products", 3, True, "bf16"),
+                          ("neumann", 3, False, "bf16"), ("exact", 0, False, "bf16")],
+                         max(5, args.steps // 5), 2)
         h3 = c3["N3_masked_bf16"]
+        # MFMAs the band path issues per (workgroup, chunk): state waves 2 x (16 for K S, 5 for
+        # (T - I) Y, 32 for the hi/lo state update), T wave 28 (Gram band tiles), output waves
+        # 108 (Q S, Q K^T, hi/lo P U'); 16x16x32 bf16 each; the same count SQ_INSTS_MFMA
+        # gives per chunk and CU.  It includes the d_v slices' repeated T and P and the hi/lo
+        # splits, and none of the Horner products the method's count assumes.
+        band_mfma = 242 * (C3["B"] * C3["H"] * C3["d_v"] // 32) * (C3["T"] // C3["C"])
+        h3["mfma_frac_executed"] = band_mfma * 16 * 16 * 32 * 2 / (h3["ms_per_step"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS
+        h3["mfma_note"] = ("mfma_frac counts the method's dense products (Horner included); the band "
+                           "path forms the masked N=3 band element by element and executes "
+                           "mfma_frac_executed; the Horner products are timed as N3_masked_products_bf16")
         out["chunk_fwd"] = {
             "workload": "chunk-wise GDN prefill forward, B=4 H=16 seq=8192 d_k=d_v=128 C=64, "
                         "N=3 band-masked inverse, bf16 Q/K/V/O, fp32 state",
@@ -557,7 +681,7 @@ def main():
                                            [("neumann", 3, True, "fp8"), ("neumann", 3, False, "fp8")],
                                            3, 1, n_sets=1, stats=True)
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline_c1()
+        out["cpu_baseline"], out["accuracy"] = cpu_baseline_and_accuracy(torch, tri, synth)
     print(json.dumps(out))
 
 

@@ -69,8 +69,13 @@ typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1, GDN_FP8_E4M3 = 2, GDN_INT8 =
 typedef enum gdn_inv_mode {
   GDN_INV_NEUMANN = 0, /* truncated sum_{n<=N} A^n ([GEO] Methodologie SS1), optional
                           band mask i - j <= N ([GEO] Methodologie SS2)                */
-  GDN_INV_EXACT = 1    /* prod_{i<m} (I + A^(2^i)), m = ceil(log2 C): exact because
+  GDN_INV_EXACT = 1,   /* prod_{i<m} (I + A^(2^i)), m = ceil(log2 C): exact because
                           A^C = 0 (Lemma 3.1 of [GEO])                                */
+  GDN_INV_NEUMANN_PRODUCTS = 2 /* gdn_chunk_fwd only: the GDN_INV_NEUMANN sum, always
+                          formed by its Horner products on MFMA (in the pre-pass), also
+                          where the masked band with N <= 3 would otherwise be formed
+                          element by element from A's sub-diagonals (identical in exact
+                          arithmetic; the products round their operands to bf16)      */
 } gdn_inv_mode;
 
 /* How T is formed.  `compute` is the MFMA operand type of the power chain:

@@ -206,6 +206,9 @@ def test_chunk_fwd_workspace_query():
     assert q(_inv(mask=0)) == chunks * 6144
     assert q(_inv(mode=tri.GDN_INV_EXACT)) == chunks * 6144
     assert q(_inv(compute=tri.GDN_FP8_E4M3)) == chunks * 6144
+    assert q(_inv(mode=tri.GDN_INV_NEUMANN_PRODUCTS)) == chunks * 6144   # Horner products asked for
+    assert q(_inv(mode=tri.GDN_INV_NEUMANN_PRODUCTS, compute=tri.GDN_FP8_E4M3)) == chunks * 6144
+    assert q(_inv(mode=3)) == 0
     assert q(None) == 0
     assert q(_inv(), T=100) == 0                     # T % C != 0
     assert q(_inv(), C=32) == 0                      # unsupported chunk size

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 tri = pytest.importorskip("tri_inverse_amd")
 
 TOL = {"bf16": 2e-3, "fp8": 5e-2}
-INV = {"neumann": oracle.INV_NEUMANN, "exact": oracle.INV_EXACT}
+INV = {"neumann": oracle.INV_NEUMANN, "exact": oracle.INV_EXACT, "neumann_products": oracle.INV_NEUMANN}
 
 
 # ------------------------------------------------------------------ WY products
@@ -94,7 +94,8 @@ def _run_chunk(x, **kw):
 
 
 @pytest.mark.parametrize("variant", [("neumann", 3, True), ("neumann", 3, False), ("neumann", 2, True),
-                                     ("neumann", 1, True), ("neumann", 5, True), ("exact", 0, False)])
+                                     ("neumann", 1, True), ("neumann", 5, True), ("exact", 0, False),
+                                     ("neumann_products", 3, True), ("neumann_products", 2, True)])
 def test_chunk_fwd_small(variant):
     mode, N, mask = variant
     B, H, T, dk, dv = 1, 3, 320, 128, 128   # 3 heads: the non-multiple-of-8 grid path

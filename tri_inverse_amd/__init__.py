@@ -26,7 +26,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 # dtype and mode codes (gdn.h)
 GDN_F32, GDN_BF16, GDN_FP8_E4M3, GDN_INT8 = 0, 1, 2, 3
-GDN_INV_NEUMANN, GDN_INV_EXACT = 0, 1
+GDN_INV_NEUMANN, GDN_INV_EXACT, GDN_INV_NEUMANN_PRODUCTS = 0, 1, 2
 GDN_OK = 0
 GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = 5, 6, 7
 FP8_STATS_FIELDS = ("nonfinite", "sat_dynamic", "sat_static", "underflow")
@@ -240,7 +240,12 @@ def gdn_tri_inverse_fs(A=None, K=None, beta=None, g=None, C: int = 64, t_dtype=t
 
 def _inv_cfg(mode, N, mask, compute):
     c = gdn_inverse_cfg()
-    c.mode = GDN_INV_EXACT if mode in ("exact", GDN_INV_EXACT) else GDN_INV_NEUMANN
+    if mode in ("exact", GDN_INV_EXACT):
+        c.mode = GDN_INV_EXACT
+    elif mode in ("neumann_products", GDN_INV_NEUMANN_PRODUCTS):
+        c.mode = GDN_INV_NEUMANN_PRODUCTS
+    else:
+        c.mode = GDN_INV_NEUMANN
     c.N, c.mask, c.compute = int(N), int(bool(mask)), _compute_code(compute)
     return c
 

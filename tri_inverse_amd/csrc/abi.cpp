@@ -253,14 +253,15 @@ static gdn_status check_chunk_args(int32_t qkv_dtype, int32_t o_dtype, int32_t B
   if (o_dtype != GDN_F32 && o_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
   if (!chunk_ok(C)) return GDN_ERR_UNSUPPORTED;
   if (T % C != 0) return GDN_ERR_BAD_SHAPE;
-  if (inv->mode != GDN_INV_NEUMANN && inv->mode != GDN_INV_EXACT) return GDN_ERR_BAD_SHAPE;
-  if (inv->mode == GDN_INV_NEUMANN && (inv->N < 1 || inv->N >= C)) return GDN_ERR_BAD_SHAPE;
+  if (inv->mode != GDN_INV_NEUMANN && inv->mode != GDN_INV_EXACT && inv->mode != GDN_INV_NEUMANN_PRODUCTS)
+    return GDN_ERR_BAD_SHAPE;
+  if (inv->mode != GDN_INV_EXACT && (inv->N < 1 || inv->N >= C)) return GDN_ERR_BAD_SHAPE;
   if (inv->mask != 0 && inv->mask != 1) return GDN_ERR_BAD_SHAPE;
   if (inv->compute != GDN_BF16 && inv->compute != GDN_FP8_E4M3 && inv->compute != GDN_F32 &&
       inv->compute != GDN_INT8)
     return GDN_ERR_BAD_DTYPE;
   if (inv->compute == GDN_F32 || inv->compute == GDN_INT8) return GDN_ERR_UNSUPPORTED;
-  if (inv->compute == GDN_FP8_E4M3 && inv->mode != GDN_INV_NEUMANN) return GDN_ERR_UNSUPPORTED;
+  if (inv->compute == GDN_FP8_E4M3 && inv->mode == GDN_INV_EXACT) return GDN_ERR_UNSUPPORTED;
   if (C != 64) return GDN_ERR_UNSUPPORTED;
   if (!(d_k == 64 || d_k == 128)) return GDN_ERR_UNSUPPORTED;
   if (d_v % 32 != 0 || d_v > 256) return GDN_ERR_UNSUPPORTED;
@@ -268,7 +269,8 @@ static gdn_status check_chunk_args(int32_t qkv_dtype, int32_t o_dtype, int32_t B
 }
 
 static size_t chunk_workspace(int32_t B, int32_t H, int64_t T, int32_t C, const gdn_inverse_cfg* inv) {
-  if (gdn::chunk_fwd_band_path(inv->mode, inv->N, inv->mask, inv->compute)) return 0;
+  if (inv->mode == GDN_INV_NEUMANN && gdn::chunk_fwd_band_path(inv->mode, inv->N, inv->mask, inv->compute))
+    return 0;
   return (size_t)B * (size_t)H * (size_t)(T / C) * gdn::T_PACK_BYTES;
 }
 
@@ -374,8 +376,9 @@ gdn_status chunk_fwd_impl(const void* Q, const void* K, const void* V, int32_t q
     ba.C = C;
     ba.d_k = d_k;
     ba.g_cumulative = 0;
+    const int mode = inv->mode == GDN_INV_EXACT ? 1 : 0;  // the products of either Neumann mode
     const gdn_status pre =
-        launch_result(gdn::launch_T_packs(ba, inv->mode, inv->N, inv->mask, inv->compute, workspace, st64, s));
+        launch_result(gdn::launch_T_packs(ba, mode, inv->N, inv->mask, inv->compute, workspace, st64, s));
     if (pre != GDN_OK) return pre;
   }
   gdn::ChunkLaunch p;
@@ -394,7 +397,7 @@ gdn_status chunk_fwd_impl(const void* Q, const void* K, const void* V, int32_t q
   p.d_k = d_k;
   p.d_v = d_v;
   p.o_bf16 = o_dtype == GDN_BF16;
-  p.mode = inv->mode;
+  p.mode = inv->mode == GDN_INV_EXACT ? 1 : 0;
   p.N = inv->N;
   p.mask = inv->mask;
   p.cmp = inv->compute;

@@ -751,10 +751,12 @@ int launch_chunk_fwd(const ChunkLaunch& p, hipStream_t s) {
   a.scale = p.scale;
   const dim3 grid((unsigned)(a.BH * (p.d_v / DVS)));
   const dim3 block(NWAVES * WAVE);
-  const bool band = chunk_fwd_band_path(p.mode, p.N, p.mask, p.cmp);
+  // the pre-pass's packs, when given, are used (every variant but the band path, and the
+  // band-masked sum when its Horner products were asked for)
+  const bool band = p.packs == nullptr;
+  if (band && !chunk_fwd_band_path(p.mode, p.N, p.mask, p.cmp)) return -1;
   // with the band mask and N <= 16 the packs below the first sub-tile-diagonal are zero
   const bool narrow = p.mode == MODE_NEUMANN && p.mask && p.N <= 16;
-  if (!band && !p.packs) return -1;
   auto go = [&](auto dk, auto mode, auto maxd) {
     if (p.o_bf16)
       hipLaunchKernelGGL((chunk_fwd_kernel<dk.value, mode.value, CMP_BF16, maxd.value, true>), grid, block,
