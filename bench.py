@@ -366,61 +366,89 @@ def replay_launches(torch, launch, n_sets, n):
     del graph
 
 
-def profile_c1(torch, tri, synth, n):
-    """Headline launch n times on rotating buffer sets (graph-replayed), then a plain
-    256 MiB copy n times: the copy's FETCH_SIZE / WRITE_SIZE per dispatch calibrate the
-    counters."""
-    C = C1["C"]
-    n_blocks = C1["B"] * C1["H"] * C1["T"] // C
-    sets = [{k: v.cuda() for k, v in synth.blocks(1 if s == 0 else 1000 + s, n_blocks, C, C1["d_k"],
-                                                  k_dtype="bf16").items()} for s in range(N_SETS)]
-    outs = [torch.empty((n_blocks, C, C), device="cuda") for _ in range(N_SETS)]
-
-    def launch(i):
-        x = sets[i]
-        tri.gdn_tri_inverse_neumann(K=x["K"], beta=x["beta"], g=x["g"], C=C, N=3, mask=True,
-                                    compute="bf16", out=outs[i])
-    replay_launches(torch, launch, N_SETS, n)
-    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(n):
-        dst.copy_(src)
-    torch.cuda.synchronize()
+PROFILE_LEGS = ("c1", "c1_exact", "c1_fs", "c3", "c3_products", "c4", "c2_C64", "c2_C128", "c2_C256",
+                "c2_C256_exact", "decode")
 
 
-def profile_c3(torch, tri, synth, n):
-    """Prefill forward (B=4 H=16 seq 8192, N=3 masked) n times (graph-replayed), then the
-    256 MiB copy."""
-    cfg = C3
-    x = {k: v.cuda() for k, v in synth.prefill(3, cfg["B"], cfg["H"], cfg["T"], cfg["d_k"],
-                                                cfg["d_v"]).items()}
-    O = torch.empty((cfg["B"], cfg["H"], cfg["T"], cfg["d_v"]), device="cuda", dtype=torch.bfloat16)
-    S = torch.empty((cfg["B"], cfg["H"], cfg["d_k"], cfg["d_v"]), device="cuda")
-    def launch(i):
-        tri.gdn_chunk_fwd(x["Q"], x["K"], x["V"], x["beta"], x["g"], C=64, scale=cfg["d_k"] ** -0.5,
-                          N=3, mask=True, O=O, S_out=S)
-    replay_launches(torch, launch, 1, n)
-    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(n):
-        dst.copy_(src)
-    torch.cuda.synchronize()
+def profile_leg(torch, tri, synth, key, n):
+    """Profiling mode: the launch that `key` names, n times on rotating buffer sets
+    (graph-replayed, as in the timed region), then a plain 256 MiB device copy n times,
+    whose FETCH_SIZE / WRITE_SIZE per dispatch calibrate the HBM counters.
+      c1, c1_exact, c1_fs  batched 64x64 inverse of the headline workload (2048 blocks):
+                           N=3 masked (T fp32), exact doubling (T bf16), forward substitution
+      c3, c3_products      prefill forward B=4 H=16 seq 8192: the band path; the Horner
+                           products (pre-pass + scan)
+      c4                   the same at seq 32768 with the fp8 inverse (N=3 masked)
+      c2_C64 .. c2_C256    WY products (A build + N=3 masked inverse + W, U) at B=2 H=16
+                           seq 16384; c2_C256_exact: exact doubling at C=256
+      decode               one decode step for 64 sequences (B=64 H=32)"""
+    if key.startswith("c1"):
+        C = C1["C"]
+        nb = C1["B"] * C1["H"] * C1["T"] // C
+        sets = [{k: v.cuda() for k, v in synth.blocks(1 if s == 0 else 1000 + s, nb, C, C1["d_k"],
+                                                      k_dtype="bf16").items()} for s in range(N_SETS)]
+        tdt = torch.bfloat16 if key == "c1_exact" else torch.float32
+        outs = [torch.empty((nb, C, C), device="cuda", dtype=tdt) for _ in range(N_SETS)]
 
+        def launch(i):
+            x = sets[i]
+            if key == "c1_exact":
+                tri.gdn_tri_inverse_exact(K=x["K"], beta=x["beta"], g=x["g"], C=C, compute="bf16", out=outs[i])
+            elif key == "c1_fs":
+                tri.gdn_tri_inverse_fs(K=x["K"], beta=x["beta"], g=x["g"], C=C, out=outs[i])
+            else:
+                tri.gdn_tri_inverse_neumann(K=x["K"], beta=x["beta"], g=x["g"], C=C, N=3, mask=True,
+                                            compute="bf16", out=outs[i])
+        n_sets = N_SETS
+    elif key in ("c3", "c3_products", "c4"):
+        cfg = C4 if key == "c4" else C3
+        x = {k: v.cuda() for k, v in synth.prefill(3, cfg["B"], cfg["H"], cfg["T"], cfg["d_k"],
+                                                    cfg["d_v"]).items()}
+        O = torch.empty((cfg["B"], cfg["H"], cfg["T"], cfg["d_v"]), device="cuda", dtype=torch.bfloat16)
+        S = torch.empty((cfg["B"], cfg["H"], cfg["d_k"], cfg["d_v"]), device="cuda")
+        mode = "neumann_products" if key == "c3_products" else "neumann"
+        compute = "fp8" if key == "c4" else "bf16"
+        need = tri.gdn_chunk_fwd_workspace_bytes(cfg["B"], cfg["H"], cfg["T"], cfg["d_k"], cfg["d_v"], 64,
+                                                 mode, 3, True, compute)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+        st = torch.zeros(4, dtype=torch.int64, device="cuda") if compute == "fp8" else None
 
-def profile_decode(torch, tri, synth, n):
-    """Decode step for 64 sequences (B=64 H=32 d=128, four rotating 128 MiB state sets)
-    n times (graph-replayed), then the 256 MiB copy."""
-    B, H, dk, dv = 64, DEC["H"], DEC["d_k"], DEC["d_v"]
-    sets = []
-    for i in range(4):
-        x = {k: v.cuda() for k, v in synth.prefill(60 + i, B, H, 1, dk, dv).items()}
-        x["S"] = torch.zeros((B, H, dk, dv), device="cuda")
-        x["O"] = torch.empty((B, H, 1, dv), device="cuda", dtype=torch.bfloat16)
-        sets.append(x)
-    def launch(i):
-        x = sets[i]
-        tri.gdn_decode(x["Q"], x["K"], x["V"], x["beta"], x["g"], S=x["S"], S_out=x["S"], O=x["O"])
-    replay_launches(torch, launch, 4, n)
+        def launch(i):
+            tri.gdn_chunk_fwd(x["Q"], x["K"], x["V"], x["beta"], x["g"], C=64, scale=cfg["d_k"] ** -0.5,
+                              mode=mode, N=3, mask=True, compute=compute, O=O, S_out=S, stats=st,
+                              workspace=ws)
+        n_sets = 1
+    elif key.startswith("c2"):
+        C = int(key.split("_")[1][1:])
+        mode = "exact" if key.endswith("exact") else "neumann"
+        B, H, T, dk, dv = 2, 16, 16384, 128, 128
+        nb = B * H * T // C
+        sets = [{k: v.cuda() for k, v in synth.blocks(2 if s == 0 else 200 + s, nb, C, dk, k_dtype="bf16",
+                                                      d_v=dv).items()} for s in range(2)]
+        outs = [(torch.empty((nb, C, dk), device="cuda", dtype=torch.bfloat16),
+                 torch.empty((nb, C, dv), device="cuda", dtype=torch.bfloat16)) for _ in range(2)]
+
+        def launch(i):
+            x = sets[i]
+            tri.gdn_wy(x["K"], x["beta"], x["g"], x["V"], C=C, mode=mode, N=3, mask=True,
+                       W_out=outs[i][0], U_out=outs[i][1])
+        n_sets = 2
+    elif key == "decode":
+        B, H, dk, dv = 64, DEC["H"], DEC["d_k"], DEC["d_v"]
+        sets = []
+        for i in range(4):
+            x = {k: v.cuda() for k, v in synth.prefill(60 + i, B, H, 1, dk, dv).items()}
+            x["S"] = torch.zeros((B, H, dk, dv), device="cuda")
+            x["O"] = torch.empty((B, H, 1, dv), device="cuda", dtype=torch.bfloat16)
+            sets.append(x)
+
+        def launch(i):
+            x = sets[i]
+            tri.gdn_decode(x["Q"], x["K"], x["V"], x["beta"], x["g"], S=x["S"], S_out=x["S"], O=x["O"])
+        n_sets = 4
+    else:
+        raise SystemExit("unknown profiling leg %r (one of %s)" % (key, ", ".join(PROFILE_LEGS)))
+    replay_launches(torch, launch, n_sets, n)
     src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(n):
@@ -587,8 +615,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="all")
     ap.add_argument("--profile-launches", type=int, default=0,
-                    help="profiling mode: run the headline launch this many times plus a "
-                         "256 MiB device copy (counter calibration), print nothing else")
+                    help="profiling mode: run the launch --only names (default the headline) "
+                         "this many times plus a 256 MiB device copy (counter calibration), "
+                         "print nothing else")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -601,16 +630,11 @@ def main():
 
     torch.cuda.set_device(0)
     if args.profile_launches:
-        if args.only == "c3":
-            profile_c3(torch, tri, synth, args.profile_launches)
-        elif args.only == "decode":
-            profile_decode(torch, tri, synth, args.profile_launches)
-        else:
-            profile_c1(torch, tri, synth, args.profile_launches)
+        profile_leg(torch, tri, synth, args.only if args.only != "all" else "c1", args.profile_launches)
         return
     c1 = bench_c1(torch, tri, synth, args.steps, args.warmup)
     head = c1["N3_masked_Tf32"]
-    traffic = load_traffic("inverse_kernel<4,1,128,1,0,1>")
+    traffic = load_traffic("inverse_kernel<4,1,128,1,0,1,false>")
     roofline = {
         "bound": "hbm",
         "achieved": head["bytes"] / (head["ms_kernel"] * 1e-3) / 1e9,
