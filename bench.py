@@ -134,9 +134,9 @@ def bench_c1(torch, tri, synth, steps, warmup):
             if variant[0] == "exact":
                 tri.gdn_tri_inverse_exact(K=x["K"], beta=x["beta"], g=x["g"], C=C, compute="bf16",
                                           out=outs[i])
-            elif variant[0] == "int8":
+            elif variant[0] in ("int8", "int16"):
                 tri.gdn_tri_inverse_neumann(K=x["K"], beta=x["beta"], g=x["g"], C=C, N=variant[1],
-                                            mask=variant[2], compute="int8", out=outs[i])
+                                            mask=variant[2], compute=variant[0], out=outs[i])
             elif variant[0] == "residual":
                 tri.gdn_tri_inverse_residual(K=x["K"], beta=x["beta"], g=x["g"], C=C, N=variant[1],
                                              mask=variant[2], S=variant[4], compute="f32", out=outs[i])
@@ -153,19 +153,21 @@ def bench_c1(torch, tri, synth, steps, warmup):
                 ("neumann", 3, True, torch.bfloat16), ("residual", 3, True, torch.float32, 8),
                 ("residual", 3, True, torch.float32, 0), ("residual", 3, True, torch.float32, 1),
                 ("residual", 3, True, torch.float32, 2), ("residual", 3, True, torch.float32, 4),
-                ("int8", 3, True, torch.float32), ("int8", 3, False, torch.float32)]
+                ("int8", 3, True, torch.float32), ("int8", 3, False, torch.float32),
+                ("int16", 3, True, torch.float32), ("int16", 3, False, torch.float32)]
     for v in variants:
         name = ("exact" if v[0] == "exact" else "N%d_%s" % (v[1], "masked" if v[2] else "unmasked"))
         if v[0] == "residual":
             name = "N%d_masked_residual_S%d_f32" % (v[1], v[4])
-        elif v[0] == "int8":
-            name = "N%d_%s_int8" % (v[1], "masked" if v[2] else "unmasked")
+        elif v[0] in ("int8", "int16"):
+            name = "N%d_%s_%s" % (v[1], "masked" if v[2] else "unmasked", v[0])
         name += "_T" + ("f32" if v[3] == torch.float32 else "bf16")
         st = steps if v == variants[0] else max(10, steps // 2)
         ms_step, reps = time_launches(torch, mk(v, v[3]), N_SETS, st, warmup)
         ms_kernel = ms_step
         nb, by, fl = c1_bytes_flops(v, 4 if v[3] == torch.float32 else 2)
-        if v[0] == "int8":  # bf16 Gram, int8 products: MFMA time at each one's peak
+        if v[0] in ("int8", "int16"):  # bf16 Gram, int8 products (int16: the method's count, not
+            # the four 8-bit digit products issued): MFMA time at each one's peak
             gram = nb * 2 * C * C * C1["d_k"]
             t_mfma = gram / (BF16_PEAK_TFLOPS * 1e12) + (fl - gram) / (INT8_PEAK_TOPS * 1e12)
         else:

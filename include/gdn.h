@@ -63,7 +63,7 @@ typedef enum gdn_status {
 } gdn_status;
 
 /* element types (int32 codes in every signature) */
-typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1, GDN_FP8_E4M3 = 2, GDN_INT8 = 3 } gdn_dtype;
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1, GDN_FP8_E4M3 = 2, GDN_INT8 = 3, GDN_INT16 = 4 } gdn_dtype;
 
 /* inverse variants */
 typedef enum gdn_inv_mode {
@@ -87,6 +87,11 @@ typedef enum gdn_inv_mode {
  *            smallest 2^e with max|x| <= 127 2^e), int32 accumulation (16x16x64 i8
  *            MFMA), Horner on X = H - I ([GEO] "Adaptation a la Quantification");
  *            gdn_tri_inverse_neumann only, C <= 64.
+ *   GDN_INT16 the same chain on 16-bit codes, |code| <= 32639 = 127 * 257, the range
+ *            whose balanced base-256 digits (code = 256 hi + lo, lo in [-128, 127]) both
+ *            fit int8: each product is four 16x16x64 i8 MFMAs (hi hi, hi lo, lo hi, lo
+ *            lo) recombined exactly in fp64, and each sum A' + P 2^e is formed in fp64
+ *            and rounded to fp32; gdn_tri_inverse_neumann only, C <= 64.
  * N is ignored for GDN_INV_EXACT. */
 typedef struct gdn_inverse_cfg {
   int32_t mode;    /* gdn_inv_mode                  */
@@ -142,8 +147,8 @@ gdn_status gdn_build_A(const gdn_blocks* in, float* A_out, void* stream);
 
 /* T = M^(N) .* sum_{n=0}^{N} A^n (mask != 0) or the plain truncated sum (mask == 0),
  * evaluated as N-1 Horner products H <- I + A H ([GEO] Methodologie SS1-2).
- * compute: GDN_F32, GDN_BF16, GDN_FP8_E4M3 or GDN_INT8 (C <= 64).  With GDN_INT8 and a
- * given fp32 A the result is exactly determined: every scaling is by a power of two,
+ * compute: GDN_F32, GDN_BF16, GDN_FP8_E4M3, GDN_INT8 or GDN_INT16 (C <= 64).  With
+ * GDN_INT8 or GDN_INT16 and a given fp32 A the result is exactly determined: every scaling is by a power of two,
  * integer products are exact and each intermediate sum is rounded once to fp32.
  * T_out [n_blocks][C][C], t_dtype GDN_F32
  * or GDN_BF16.  stats: device gdn_fp8_stats (see above) or NULL; when given it is

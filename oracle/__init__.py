@@ -61,6 +61,7 @@ def _load():
     lib.oracle_neumann.argtypes = [i64, i32, P, i32, i32, P]
     lib.oracle_doubling.argtypes = [i64, i32, P, P]
     lib.oracle_neumann_int8.argtypes = [i64, i32, P, i32, i32, P]
+    lib.oracle_neumann_int16.argtypes = [i64, i32, P, i32, i32, P]
     U64P = ctypes.POINTER(ctypes.c_uint64)
     lib.oracle_neumann_fp8.argtypes = [i64, i32, P, i32, i32, P, U64P, P]
     lib.oracle_e4m3_round.argtypes = [i64, P, P]
@@ -70,6 +71,7 @@ def _load():
                                      i32, i32, i32, P, P]
     lib.oracle_recurrence.argtypes = [i32, i32, i64, i32, i32, P, P, P, P, P, P, f64, P, P]
     for fn in ("oracle_build_A", "oracle_fs_inverse", "oracle_neumann", "oracle_neumann_int8",
+               "oracle_neumann_int16",
                "oracle_neumann_fp8", "oracle_e4m3_round",
                "oracle_doubling",
                "oracle_residual", "oracle_wy", "oracle_chunk_fwd", "oracle_recurrence",
@@ -133,6 +135,17 @@ def neumann_int8(A, N: int, mask: bool) -> np.ndarray:
     nb, C, _ = A.shape
     T = np.empty_like(A)
     _load().oracle_neumann_int8(nb, C, _ptr(A), int(N), int(bool(mask)), _ptr(T))
+    return T
+
+
+def neumann_int16(A, N: int, mask: bool) -> np.ndarray:
+    """The same chain on 16-bit codes (|code| <= 32639 = 127 * 257, two signed 8-bit digits),
+    each sum formed in fp64 and rounded to fp32 ([GEO] "Adaptation a la Quantification";
+    reading in gdn_oracle.c).  A holds fp32 values."""
+    A = _f64(A)
+    nb, C, _ = A.shape
+    T = np.empty_like(A)
+    _load().oracle_neumann_int16(nb, C, _ptr(A), int(N), int(bool(mask)), _ptr(T))
     return T
 
 

@@ -184,27 +184,32 @@ void oracle_neumann(int64_t nb, int C, const double* A, int N, int mask, double*
  *     quantised, so out-of-band magnitudes never set a scale.
  * Every output value is an fp32 value, returned in fp64. */
 
-/* smallest integer e with amax <= 127 * 2^e (0 for an all-zero block), found by
+/* smallest integer e with amax <= code_max * 2^e (0 for an all-zero block), found by
  * stepping e directly from that definition */
-static int int8_scale_exponent(double amax) {
+static int int_scale_exponent(double amax, double code_max) {
   if (!(amax > 0.0)) return 0;
   int e = 0;
-  while (amax > 127.0 * ldexp(1.0, e)) ++e;
-  while (amax <= 127.0 * ldexp(1.0, e - 1)) --e;
+  while (amax > code_max * ldexp(1.0, e)) ++e;
+  while (amax <= code_max * ldexp(1.0, e - 1)) --e;
   return e;
 }
 
 /* codes q[i] = round_half_even(x[i] / 2^e) of one C x C operand; returns e */
-static int int8_quantise(int C, const double* X, long* q) {
+static int int_quantise(int C, const double* X, double code_max, long* q) {
   double amax = 0.0;
   for (size_t i = 0; i < (size_t)C * C; ++i)
     if (fabs(X[i]) > amax) amax = fabs(X[i]);
-  const int e = int8_scale_exponent(amax);
+  const int e = int_scale_exponent(amax, code_max);
   for (size_t i = 0; i < (size_t)C * C; ++i) q[i] = (long)nearbyint(ldexp(X[i], -e));
   return e;
 }
 
-void oracle_neumann_int8(int64_t nb, int C, const double* A, int N, int mask, double* T) {
+/* the chain with integer codes of magnitude <= code_max; see the reading above.  The
+ * sum A' + P 2^(eA + eX) is formed in fp64 and rounded to fp32: for 8-bit codes P stays
+ * below 2^20 and the fp64 sum is exact, so this is one rounding of the exact sum; for
+ * 16-bit codes P reaches 2^36 and the fp64 step can round too. */
+static void neumann_int_chain(int64_t nb, int C, const double* A, int N, int mask, double code_max,
+                              double* T) {
 #pragma omp parallel for schedule(static)
   for (int64_t b = 0; b < nb; ++b) {
     const size_t CC = (size_t)C * C;
@@ -215,17 +220,17 @@ void oracle_neumann_int8(int64_t nb, int C, const double* A, int N, int mask, do
     long* qx = (long*)malloc(sizeof(long) * CC);
     memcpy(Am, A + (size_t)b * CC, sizeof(double) * CC);
     if (mask) apply_band_mask(C, N, Am);
-    const int eA = int8_quantise(C, Am, qa);
+    const int eA = int_quantise(C, Am, code_max, qa);
     for (size_t i = 0; i < CC; ++i) Ad[i] = ldexp((double)qa[i], eA);
     memcpy(X, Ad, sizeof(double) * CC); /* X_1 = A' */
     for (int k = 1; k < N; ++k) {
-      const int eX = int8_quantise(C, X, qx);
+      const int eX = int_quantise(C, X, code_max, qx);
       for (int i = 0; i < C; ++i)
         for (int j = 0; j < C; ++j) {
           long p = 0;
           for (int m = 0; m < C; ++m) p += qa[(size_t)i * C + m] * qx[(size_t)m * C + j];
-          const double exact = Ad[(size_t)i * C + j] + ldexp((double)p, eA + eX);
-          X[(size_t)i * C + j] = (double)(float)exact;
+          const double sum = Ad[(size_t)i * C + j] + ldexp((double)p, eA + eX);
+          X[(size_t)i * C + j] = (double)(float)sum;
         }
       if (mask) apply_band_mask(C, N, X);
     }
@@ -238,6 +243,18 @@ void oracle_neumann_int8(int64_t nb, int C, const double* A, int N, int mask, do
     free(qa);
     free(qx);
   }
+}
+
+void oracle_neumann_int8(int64_t nb, int C, const double* A, int N, int mask, double* T) {
+  neumann_int_chain(nb, C, A, N, mask, 127.0, T);
+}
+
+/* The same chain on 16-bit codes ([GEO] "Adaptation a la Quantification" names INT16
+ * beside INT8).  Reading: codes of magnitude <= 32639 = 127 * 257, the largest range
+ * whose balanced base-256 digits (q = 256 hi + lo, lo in [-128, 127]) both fit a signed
+ * 8-bit integer -- the form in which 8-bit integer matrix units multiply them. */
+void oracle_neumann_int16(int64_t nb, int C, const double* A, int N, int mask, double* T) {
+  neumann_int_chain(nb, C, A, N, mask, 32639.0, T);
 }
 
 /* ---- a8: the power chain on fp8 (OCP e4m3) operands --------------------------

@@ -175,10 +175,14 @@ def test_decode_validation():
 
 
 def test_int8_compute_routing():
-    """int8 compute is accepted by the Neumann entry point at C <= 64 only."""
+    """int8 and int16 compute are accepted by the Neumann entry point at C <= 64 only."""
     neu = lambda d, c: lib.gdn_tri_inverse_neumann(ctypes.byref(d), 3, 1, c, FAKE, tri.GDN_F32,
                                                    None, None)
     assert neu(blocks(n_blocks=0), tri.GDN_INT8) == 0
+    assert neu(blocks(n_blocks=0), tri.GDN_INT16) == 0
+    assert neu(blocks(C=128, n_blocks=0), tri.GDN_INT16) == 5
+    assert lib.gdn_tri_inverse_exact(ctypes.byref(blocks(n_blocks=0)), tri.GDN_INT16, FAKE,
+                                      tri.GDN_F32, None) == 5
     assert neu(blocks(n_blocks=0), 9) == 3
     assert neu(blocks(C=128, n_blocks=0), tri.GDN_INT8) == 5
     assert lib.gdn_tri_inverse_exact(ctypes.byref(blocks(n_blocks=0)), tri.GDN_INT8, FAKE,

@@ -460,6 +460,65 @@ def test_int8_chain_close_to_fp64_on_c1_inputs():
     assert np.all(np.triu(T8, 1) == 0.0)
 
 
+# ---------------------------------------------------------------- int16 chain
+# The same Horner chain on 16-bit codes (|code| <= 32639 = 127 * 257, each sum formed in
+# fp64 then rounded to fp32); reading in oracle/gdn_oracle.c.
+
+@pytest.mark.parametrize("rho", [0.125, 0.25, 0.5])
+@pytest.mark.parametrize("N", [1, 2, 3, 4])
+@pytest.mark.parametrize("mask", [False, True])
+def test_int16_chain_exact_on_closed_form(rho, N, mask):
+    """A = -rho L, rho a power of two: every operand through N = 4 is a multiple of its
+    power-of-two scale with codes <= 32639 (the unmasked third power reaches 221.375 at
+    rho = 1/2, still 3 fractional bits below a 2^-7 step), so the 16-bit chain
+    reproduces the closed-form truncated sum exactly, where the int8 chain does not."""
+    C = 64
+    A = (-rho * np.tril(np.ones((C, C)), -1))[None]
+    np.testing.assert_array_equal(oracle.neumann_int16(A, N, mask)[0], _closed_form_truncated(C, rho, N, mask))
+    if rho == 0.5 and N == 4 and not mask:
+        assert np.max(np.abs(oracle.neumann_int8(A, N, mask)[0] - _closed_form_truncated(C, rho, N, mask))) > 1.0
+
+
+def test_int16_quantiser_properties():
+    """N = 1 returns I + A': codes in [-32639, 32639] under one power-of-two scale 2^e per
+    block, round to nearest (|A' - A| <= 2^(e-1)), and the finest scale that does not
+    exceed the code range."""
+    A = _rand_A(14, 16, 64).astype(np.float32).astype(np.float64)
+    Ad = oracle.neumann_int16(A, 1, False) - np.eye(64)
+    for b in range(A.shape[0]):
+        amax = np.max(np.abs(A[b]))
+        e = math.frexp(amax / 32639.0)[1]
+        if amax <= 32639.0 * 2.0 ** (e - 1):
+            e -= 1
+        q = Ad[b] * 2.0 ** -e
+        np.testing.assert_array_equal(q, np.round(q))
+        assert np.max(np.abs(q)) <= 32639
+        assert np.max(np.abs(Ad[b] - A[b])) <= 2.0 ** (e - 1)
+        assert 32639.0 * 2.0 ** (e - 1) < amax <= 32639.0 * 2.0 ** e
+
+
+def test_int16_code_range_splits_into_two_int8_digits():
+    """The reading's code bound: every q with |q| <= 32639 is 256 hi + lo with both balanced
+    digits in [-128, 127] (the form in which 8-bit matrix units take it), and 32640 is
+    not (its hi digit would be 128)."""
+    q = np.arange(-32639, 32640)
+    lo = ((q + 128) & 255) - 128
+    hi = (q - lo) >> 8
+    np.testing.assert_array_equal(256 * hi + lo, q)
+    assert lo.min() >= -128 and lo.max() <= 127 and hi.min() >= -128 and hi.max() <= 127
+    assert ((32640 - (((32640 + 128) & 255) - 128)) >> 8) == 128
+
+
+def test_int16_chain_close_to_fp64_on_c1_inputs():
+    """16-bit codes keep T - I within 1e-4 of the fp64 masked sum (int8: 2e-2)."""
+    A = _rand_A(13, 24, 64).astype(np.float32).astype(np.float64)
+    T16 = oracle.neumann_int16(A, 3, True)
+    Tf = oracle.neumann(A, 3, True)
+    I = np.eye(64)
+    assert _relF(T16 - I, Tf - I) < 1e-4
+    assert _relF(T16 - I, Tf - I) < 0.01 * _relF(oracle.neumann_int8(A, 3, True) - I, Tf - I)
+
+
 # ---------------------------------------------------------------- fp8 (e4m3) chain
 # [GEO] "Adaptation a la Quantification" runs the power chain on low-bit operands; the
 # e4m3 reading (format, rounding, scales, counters) is stated in oracle/gdn_oracle.c.

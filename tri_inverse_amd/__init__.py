@@ -25,14 +25,14 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 # dtype and mode codes (gdn.h)
-GDN_F32, GDN_BF16, GDN_FP8_E4M3, GDN_INT8 = 0, 1, 2, 3
+GDN_F32, GDN_BF16, GDN_FP8_E4M3, GDN_INT8, GDN_INT16 = 0, 1, 2, 3, 4
 GDN_INV_NEUMANN, GDN_INV_EXACT, GDN_INV_NEUMANN_PRODUCTS = 0, 1, 2
 GDN_OK = 0
 GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = 5, 6, 7
 FP8_STATS_FIELDS = ("nonfinite", "sat_dynamic", "sat_static", "underflow")
 
 _COMPUTE = {"f32": GDN_F32, "fp32": GDN_F32, "bf16": GDN_BF16, "fp8": GDN_FP8_E4M3,
-            "e4m3": GDN_FP8_E4M3, "int8": GDN_INT8}
+            "e4m3": GDN_FP8_E4M3, "int8": GDN_INT8, "int16": GDN_INT16}
 _TORCH_DTYPE = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
 
 

@@ -111,7 +111,8 @@ gdn_status gdn_tri_inverse_neumann(const gdn_blocks* in, int32_t N, int32_t mask
   if (st != GDN_OK) return st;
   if (N < 1 || N >= in->C) return GDN_ERR_BAD_SHAPE;
   if (mask != 0 && mask != 1) return GDN_ERR_BAD_SHAPE;
-  if (compute != GDN_F32 && compute != GDN_BF16 && compute != GDN_FP8_E4M3 && compute != GDN_INT8)
+  if (compute != GDN_F32 && compute != GDN_BF16 && compute != GDN_FP8_E4M3 && compute != GDN_INT8 &&
+      compute != GDN_INT16)
     return GDN_ERR_BAD_DTYPE;
   if (t_dtype != GDN_F32 && t_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
   // C >= 128 (bf16 keys and products): the band kernel for the masked sum with N <= 16,
@@ -146,7 +147,7 @@ gdn_status gdn_tri_inverse_exact(const gdn_blocks* in, int32_t compute, void* T_
   int src = 0;
   gdn_status st = check_blocks(in, true, false, &src);
   if (st != GDN_OK) return st;
-  if (compute == GDN_FP8_E4M3 || compute == GDN_INT8) return GDN_ERR_UNSUPPORTED;
+  if (compute == GDN_FP8_E4M3 || compute == GDN_INT8 || compute == GDN_INT16) return GDN_ERR_UNSUPPORTED;
   if (compute != GDN_F32 && compute != GDN_BF16) return GDN_ERR_BAD_DTYPE;
   if (t_dtype != GDN_F32 && t_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
   const bool large = !chunk_small(in->C);
@@ -169,7 +170,8 @@ gdn_status gdn_tri_inverse_residual(const gdn_blocks* in, int32_t N, int32_t mas
   if (N < 1 || N >= in->C) return GDN_ERR_BAD_SHAPE;
   if (mask != 0 && mask != 1) return GDN_ERR_BAD_SHAPE;
   if (S < 0 || S > 64) return GDN_ERR_BAD_SHAPE;
-  if (compute != GDN_F32 && compute != GDN_BF16 && compute != GDN_FP8_E4M3 && compute != GDN_INT8)
+  if (compute != GDN_F32 && compute != GDN_BF16 && compute != GDN_FP8_E4M3 && compute != GDN_INT8 &&
+      compute != GDN_INT16)
     return GDN_ERR_BAD_DTYPE;
   if (t_dtype != GDN_F32 && t_dtype != GDN_BF16) return GDN_ERR_BAD_DTYPE;
   if (compute != GDN_F32) return GDN_ERR_UNSUPPORTED;
@@ -213,7 +215,8 @@ gdn_status gdn_wy(const gdn_blocks* in, const void* T, int32_t t_dtype, const gd
     if (inv->mode == GDN_INV_NEUMANN && (inv->N < 1 || inv->N >= in->C)) return GDN_ERR_BAD_SHAPE;
     if (inv->mask != 0 && inv->mask != 1) return GDN_ERR_BAD_SHAPE;
     if (inv->compute != GDN_BF16) {
-      if (inv->compute == GDN_F32 || inv->compute == GDN_FP8_E4M3 || inv->compute == GDN_INT8)
+      if (inv->compute == GDN_F32 || inv->compute == GDN_FP8_E4M3 || inv->compute == GDN_INT8 ||
+          inv->compute == GDN_INT16)
         return GDN_ERR_UNSUPPORTED;
       return GDN_ERR_BAD_DTYPE;
     }
@@ -258,9 +261,9 @@ static gdn_status check_chunk_args(int32_t qkv_dtype, int32_t o_dtype, int32_t B
   if (inv->mode != GDN_INV_EXACT && (inv->N < 1 || inv->N >= C)) return GDN_ERR_BAD_SHAPE;
   if (inv->mask != 0 && inv->mask != 1) return GDN_ERR_BAD_SHAPE;
   if (inv->compute != GDN_BF16 && inv->compute != GDN_FP8_E4M3 && inv->compute != GDN_F32 &&
-      inv->compute != GDN_INT8)
+      inv->compute != GDN_INT8 && inv->compute != GDN_INT16)
     return GDN_ERR_BAD_DTYPE;
-  if (inv->compute == GDN_F32 || inv->compute == GDN_INT8) return GDN_ERR_UNSUPPORTED;
+  if (inv->compute == GDN_F32 || inv->compute == GDN_INT8 || inv->compute == GDN_INT16) return GDN_ERR_UNSUPPORTED;
   if (inv->compute == GDN_FP8_E4M3 && inv->mode == GDN_INV_EXACT) return GDN_ERR_UNSUPPORTED;
   if (C != 64) return GDN_ERR_UNSUPPORTED;
   if (!(d_k == 64 || d_k == 128)) return GDN_ERR_UNSUPPORTED;

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void inverse_kernel(BlocksArgs a, int N, int m
   // fp8 and int8 mask A and every intermediate (the band sets the quantisation
   // scales); bf16 / fp32 mask only the final sum (identical result, see neumann_T)
   const int band = (MODE == MODE_NEUMANN && mask) ? N : -1;
-  constexpr bool BANDED = (MODE == MODE_NEUMANN && (CMP == CMP_FP8 || CMP == CMP_INT8));
+  constexpr bool BANDED = (MODE == MODE_NEUMANN && (CMP == CMP_FP8 || CMP == CMP_INT8 || CMP == CMP_INT16));
   Fp8Counts cnt{0, 0, 0, 0};
   const bool count = (CMP == CMP_FP8) && stats != nullptr;
   BlockIn<NT, SRC, DK> in;
@@ -103,6 +103,8 @@ __global__ __launch_bounds__(256) void inverse_kernel(BlocksArgs a, int N, int m
     residual_T<NT>(AD, AT, N, mask != 0, S, TT);
   else if constexpr (CMP == CMP_INT8)
     neumann_T_i8<NT, MAXD>(AD, AT, N, mask != 0, TT);
+  else if constexpr (CMP == CMP_INT16)
+    neumann_T_i16<NT, MAXD>(AD, AT, N, mask != 0, TT);
   else
     neumann_T<NT, CMP, MAXD>(AD, AT, N, mask != 0, TT, cnt, count);
   if constexpr (PK) {
@@ -259,6 +261,7 @@ int launch_neumann(const BlocksArgs& a, int src, int N, int mask, int cmp, void*
       case CMP_BF16: return go(std::integral_constant<int, CMP_BF16>{});
       case CMP_FP8: return go(std::integral_constant<int, CMP_FP8>{});
       case CMP_INT8: return go(std::integral_constant<int, CMP_INT8>{});
+      case CMP_INT16: return go(std::integral_constant<int, CMP_INT16>{});
       default: return -1;
     }
   });

@@ -21,7 +21,7 @@
 
 namespace gdn {
 
-enum : int { CMP_F32 = 0, CMP_BF16 = 1, CMP_FP8 = 2, CMP_INT8 = 3 };
+enum : int { CMP_F32 = 0, CMP_BF16 = 1, CMP_FP8 = 2, CMP_INT8 = 3, CMP_INT16 = 4 };
 enum : int { MODE_NEUMANN = 0, MODE_EXACT = 1, MODE_RESIDUAL = 2, MODE_FS = 3 };
 
 template <int NT>
@@ -679,6 +679,120 @@ __device__ __forceinline__ void neumann_T_i8(Mat<NT>& AD, Mat<NT>& AT, int N, bo
 #pragma unroll
           for (int r = 0; r < 4; ++r) X.t[I][J][r] = AD.t[I][J][r] + ldexpf((float)p[r], es);
         }
+      }
+    if (mask) {
+      if (last)
+        mask_T(TT, band);
+      else
+        mask_D(X, band);
+    }
+  }
+  add_eye(TT);
+}
+
+// ---- int16 variant: 16-bit codes as two signed 8-bit digits ------------------------
+// [GEO] "Adaptation a la Quantification" names INT16 beside INT8; gfx950's integer matrix
+// cores multiply 8-bit operands, so a 16-bit code q is carried as its balanced base-256
+// digits q = 256 hi + lo, lo in [-128, 127].  Codes are limited to |q| <= 32639 = 127 * 257
+// so that hi fits int8 as well; one power-of-two scale per block and operand, as for
+// int8.  A product of codes is four 16x16x64 i8 MFMAs (hi hi, hi lo, lo hi, lo lo), each
+// exact in int32, recombined exactly in fp64; A' + P 2^(eA + eX) is formed in fp64 and
+// rounded to fp32 (two roundings, in that order, which fixes the result).
+
+// smallest e with amax <= 32639 2^e: amax = m 2^E, m in [0.5, 1); 32639 2^(E-15) =
+// (32639 / 32768) 2^E covers amax iff m <= 32639 / 32768, else 32639 2^(E-14) does
+__device__ __forceinline__ int i16_exponent(float amax) {
+  if (!(amax > 0.f) || !__builtin_isfinite(amax)) return 0;
+  int E;
+  const float m = frexpf(amax, &E);
+  return (m <= 32639.f / 32768.f) ? E - 15 : E - 14;
+}
+
+// digits of one tile's 4 registers, packed in register order (byte r = register r)
+__device__ __forceinline__ void q16x4(const f32x4& v, int neg_e, int& hw, int& lw) {
+  uint32_t h = 0, lo = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int q = (int)__builtin_rintf(ldexpf(v[r], neg_e));
+    const int ld = ((q + 128) & 255) - 128;
+    const int hd = (q - ld) >> 8;
+    h |= ((uint32_t)hd & 0xffu) << (8 * r);
+    lo |= ((uint32_t)ld & 0xffu) << (8 * r);
+  }
+  hw = (int)h;
+  lw = (int)lo;
+}
+
+template <int NT>
+__device__ __forceinline__ void i16_rowfrag(const Mat<NT>& XT, int I, int neg_e, i32x4& hi, i32x4& lo) {
+#pragma unroll
+  for (int K = 0; K < 4; ++K) {
+    int h, l;
+    q16x4(tile_or_zero(XT, I, K), neg_e, h, l);
+    hi[K] = h;
+    lo[K] = l;
+  }
+}
+template <int NT>
+__device__ __forceinline__ void i16_colfrag(const Mat<NT>& YD, int J, int neg_e, i32x4& hi, i32x4& lo) {
+#pragma unroll
+  for (int K = 0; K < 4; ++K) {
+    int h, l;
+    q16x4(tile_or_zero(YD, K, J), neg_e, h, l);
+    hi[K] = h;
+    lo[K] = l;
+  }
+}
+
+// out = fl32(fl64(base + P 2^es)) with P the product of the two digit fragments
+__device__ __forceinline__ f32x4 i16_product(const i32x4& ah, const i32x4& al, const i32x4& bh, const i32x4& bl,
+                                             const f32x4& base, int es) {
+  const i32x4 hh = mma_i8(ah, bh), hl = mma_i8(ah, bl), lh = mma_i8(al, bh), ll = mma_i8(al, bl);
+  f32x4 out;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const double p = (double)hh[r] * 65536.0 + (double)(hl[r] + lh[r]) * 256.0 + (double)ll[r];
+    out[r] = (float)((double)base[r] + ldexp(p, es));
+  }
+  return out;
+}
+
+// Horner on X = H - I as neumann_T_i8, with 16-bit codes.  C <= 64.
+template <int NT, int MAXD = NT - 1>
+__device__ __forceinline__ void neumann_T_i16(Mat<NT>& AD, Mat<NT>& AT, int N, bool mask, Mat<NT>& TT) {
+  static_assert(NT <= 4, "one 64-wide MFMA contraction per tile");
+  const int band = mask ? N : (1 << 30);
+  const int eA = i16_exponent(absmax(AT));
+  i8_roundtrip(AD, eA);  // x -> round(x / 2^e) 2^e: the dequantised operand, any code width
+  i8_roundtrip(AT, eA);
+  if (N <= 1) {
+    TT = AT;
+    add_eye(TT);
+    return;
+  }
+  i32x4 rh[NT], rl[NT];
+#pragma unroll
+  for (int I = 0; I < NT; ++I) i16_rowfrag(AT, I, -eA, rh[I], rl[I]);
+  Mat<NT> X = AD;
+  for (int k = 1; k < N; ++k) {
+    const int eX = i16_exponent(absmax(X));
+    i32x4 ch[NT], cl[NT];
+#pragma unroll
+    for (int J = 0; J < NT; ++J) i16_colfrag(X, J, -eX, ch[J], cl[J]);
+    const int es = eA + eX;
+    const bool last = (k == N - 1);
+#pragma unroll
+    for (int I = 0; I < NT; ++I)
+#pragma unroll
+      for (int J = 0; J <= I; ++J) {
+        if (I - J > MAXD) {
+          (last ? TT : X).t[I][J] = zero4();
+          continue;
+        }
+        if (last)  // T-form: operands swapped
+          TT.t[I][J] = i16_product(ch[J], cl[J], rh[I], rl[I], AT.t[I][J], es);
+        else
+          X.t[I][J] = i16_product(rh[I], rl[I], ch[J], cl[J], AD.t[I][J], es);
       }
     if (mask) {
       if (last)
