@@ -227,6 +227,21 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   return a + b;
 }
 
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u<0x128>(v));
+  v = min(v, dpp_u<0x124>(v));
+  v = min(v, dpp_u<0x122>(v));
+  v = min(v, dpp_u<0x121>(v));
+  uint32_t a, b;
+  self_swap<16>(v, a, b);
+  v = min(a, b);
+  self_swap<32>(v, a, b);
+  return min(a, b);
+}
+
+// true in every lane iff pred holds in every active lane
+__device__ __forceinline__ bool wave_all(bool pred) { return __builtin_amdgcn_ballot_w64(!pred) == 0; }
+
 __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }

@@ -510,43 +510,43 @@ __device__ __forceinline__ long quant8(const f32x4& lo, const f32x4& hi, float i
   return (long)(((uint64_t)w1 << 32) | (uint64_t)w0);
 }
 
-// count diagnostics of quantising the lower tiles of M with scale s (dynamic) and
-// s_static (the static scale), per lane
-template <int NT>
-__device__ __forceinline__ void fp8_count(const Mat<NT>& M, float s, float s_static,
-                                          Fp8Counts& cnt) {
-  const float inv_s = 1.f / s, inv_st = 1.f / s_static;
+// count diagnostics of quantising the lower tiles of M (those within MAXD tile-diagonals
+// of the main one; the rest are zero and count nothing) under the reciprocal scales
+// inv_s (dynamic) and inv_st (static), per lane, element by element
+template <int NT, int MAXD>
+__device__ __forceinline__ void fp8_count(const Mat<NT>& M, float inv_s, float inv_st, Fp8Counts& cnt) {
   constexpr float UNDER = 0.0009765625f;  // 2^-10: half the smallest e4m3 subnormal
 #pragma unroll
   for (int I = 0; I < NT; ++I)
 #pragma unroll
-    for (int J = 0; J <= I; ++J)
+    for (int J = 0; J <= I; ++J) {
+      if (I - J > MAXD) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float x = M.t[I][J][r];
-        if (!__builtin_isfinite(x)) {
-          cnt.nonfinite++;
-          continue;
-        }
-        float a = fabsf(x);
-        cnt.sat_dyn += (a * inv_s >= FP8_SAT) ? 1u : 0u;
-        cnt.sat_static += (a * inv_st >= FP8_SAT) ? 1u : 0u;
-        cnt.underflow += (x != 0.f && a * inv_s <= UNDER) ? 1u : 0u;
+        const float x = M.t[I][J][r];
+        const float a = fabsf(x);
+        const bool fin = __builtin_isfinite(x);
+        cnt.nonfinite += fin ? 0u : 1u;
+        cnt.sat_dyn += (fin && a * inv_s >= FP8_SAT) ? 1u : 0u;
+        cnt.sat_static += (fin && a * inv_st >= FP8_SAT) ? 1u : 0u;
+        cnt.underflow += (fin && x != 0.f && a * inv_s <= UNDER) ? 1u : 0u;
       }
+    }
 }
 
-template <int NT>
+// block absmax of the lower tiles within MAXD tile-diagonals (a NaN never becomes the
+// maximum: fmaxf returns the other operand)
+template <int NT, int MAXD = NT - 1>
 __device__ __forceinline__ float absmax(const Mat<NT>& M) {
   float m = 0.f;
 #pragma unroll
   for (int I = 0; I < NT; ++I)
 #pragma unroll
-    for (int J = 0; J <= I; ++J)
+    for (int J = 0; J <= I; ++J) {
+      if (I - J > MAXD) continue;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float a = fabsf(M.t[I][J][r]);
-        m = (a > m) ? a : m;  // NaN does not propagate into the scale
-      }
+      for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(M.t[I][J][r]));
+    }
   return wave_max(m);
 }
 
@@ -554,14 +554,57 @@ __device__ __forceinline__ float fp8_scale(float amax) {
   return (amax > 0.f && __builtin_isfinite(amax)) ? amax / FP8_MAX : 1.f;
 }
 
-// fake-quantise the lower tiles of M (x -> s * q(x / s)); returns nothing, M updated
-template <int NT>
+// The scale absmax/448 of M and, when count is set, the four counters of quantising M
+// under it and under the static scale s_static (s_static <= 0: M's own scale).
+// Counting element by element is skipped when block-wide aggregates show that every
+// counter is zero; this is exact, because a correctly rounded product a * c (c > 0) does
+// not decrease as a grows:
+//   - every element finite (x * 0 + acc stays 0 unless some x is infinite or NaN);
+//   - absmax * inv < 464 for both scales: no finite |x| <= absmax reaches 464;
+//   - the smallest non-zero |x| times inv_s exceeds 2^-10: no non-zero |x| underflows.
+// The smallest non-zero magnitude comes from an unsigned minimum over
+// (bits(x) << 1) - 1, which drops the sign and sends both zeros to the largest value.
+template <int NT, int MAXD>
+__device__ __forceinline__ float fp8_scale_count(const Mat<NT>& M, float s_static, Fp8Counts& cnt, bool count) {
+  constexpr float UNDER = 0.0009765625f;
+  float m = 0.f, nf = 0.f;
+  uint32_t mn = 0xffffffffu;
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int J = 0; J <= I; ++J) {
+      if (I - J > MAXD) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = M.t[I][J][r];
+        m = fmaxf(m, fabsf(x));
+        if (count) {
+          nf = __builtin_fmaf(x, 0.f, nf);
+          mn = min(mn, (__builtin_bit_cast(uint32_t, x) << 1) - 1u);
+        }
+      }
+    }
+  const float amax = wave_max(m);
+  const float s = fp8_scale(amax);
+  if (count) {
+    const float inv_s = 1.f / s, inv_st = 1.f / (s_static > 0.f ? s_static : s);
+    const uint32_t mnw = wave_min_u32(mn);
+    bool quiet = wave_all(nf == 0.f) && amax * inv_s < FP8_SAT && amax * inv_st < FP8_SAT;
+    if (mnw != 0xffffffffu) quiet = quiet && __builtin_bit_cast(float, (mnw + 1u) >> 1) * inv_s > UNDER;
+    if (!quiet) fp8_count<NT, MAXD>(M, inv_s, inv_st, cnt);
+  }
+  return s;
+}
+
+// fake-quantise the lower tiles of M within MAXD tile-diagonals (x -> s * q(x / s))
+template <int NT, int MAXD = NT - 1>
 __device__ __forceinline__ void fp8_roundtrip(Mat<NT>& M, float s) {
   const float inv_s = 1.f / s;
 #pragma unroll
   for (int I = 0; I < NT; ++I)
 #pragma unroll
     for (int J = 0; J <= I; ++J) {
+      if (I - J > MAXD) continue;
       long q = quant8(M.t[I][J], zero4(), inv_s);
       uint32_t w = (uint32_t)(uint64_t)q;
       M.t[I][J][0] = fp8_to_f32<0>(w) * s;
@@ -826,11 +869,10 @@ __device__ __forceinline__ void neumann_T_fp8(const Mat<NT>& AD, const Mat<NT>& 
                                               Mat<NT>& TT, Fp8Counts& cnt, bool count) {
   constexpr int NP = (NT + 1) / 2;
   const int band = mask ? N : (1 << 30);
-  const float sA = fp8_scale(absmax(AT));
-  if (count) fp8_count(AT, sA, sA, cnt);
+  const float sA = fp8_scale_count<NT, MAXD>(AT, 0.f, cnt, count);
   if (N <= 1) {
     TT = AT;
-    fp8_roundtrip(TT, sA);
+    fp8_roundtrip<NT, MAXD>(TT, sA);
     add_eye(TT);
     return;
   }
@@ -842,13 +884,27 @@ __device__ __forceinline__ void neumann_T_fp8(const Mat<NT>& AD, const Mat<NT>& 
     for (int p = 0; p < NP; ++p)
       if (2 * p <= I && I - (2 * p + 1) <= MAXD)
         ra[I][p] = quant8(tile_or_zero(AT, I, 2 * p), tile_or_zero(AT, I, 2 * p + 1), iA);
-  Mat<NT> AqD = AD, AqT = AT;  // A' in both forms
-  fp8_roundtrip(AqD, sA);
-  fp8_roundtrip(AqT, sA);
+  // A' in both forms; the T-form decodes A's row codes (the same quantisation)
+  Mat<NT> AqD = AD, AqT;
+  fp8_roundtrip<NT, MAXD>(AqD, sA);
+#pragma unroll
+  for (int I = 0; I < NT; ++I)
+#pragma unroll
+    for (int J = 0; J <= I; ++J) {
+      if (I - J > MAXD) {
+        AqT.t[I][J] = zero4();
+        continue;
+      }
+      const uint64_t q = (uint64_t)ra[I][J / 2];
+      const uint32_t w = (J & 1) ? (uint32_t)(q >> 32) : (uint32_t)q;
+      AqT.t[I][J][0] = fp8_to_f32<0>(w) * sA;
+      AqT.t[I][J][1] = fp8_to_f32<1>(w) * sA;
+      AqT.t[I][J][2] = fp8_to_f32<2>(w) * sA;
+      AqT.t[I][J][3] = fp8_to_f32<3>(w) * sA;
+    }
   Mat<NT> X = AqD;  // X_1 (D-form)
   for (int k = 1; k < N; ++k) {
-    const float sX = fp8_scale(absmax(X));
-    if (count) fp8_count(X, sX, sA, cnt);
+    const float sX = fp8_scale_count<NT, MAXD>(X, sA, cnt, count);
     const float iX = 1.f / sX, sxy = sA * sX;
     long cx[NP][NT];
 #pragma unroll
@@ -886,9 +942,8 @@ __device__ __forceinline__ void neumann_T_fp8(const Mat<NT>& AD, const Mat<NT>& 
         mask_D(X, band);
     }
   }
-  const float sT = fp8_scale(absmax(TT));
-  if (count) fp8_count(TT, sT, sA, cnt);
-  fp8_roundtrip(TT, sT);
+  const float sT = fp8_scale_count<NT, MAXD>(TT, sA, cnt, count);
+  fp8_roundtrip<NT, MAXD>(TT, sT);
   add_eye(TT);
 }
 
