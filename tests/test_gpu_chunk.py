@@ -312,6 +312,7 @@ def test_chunk_fwd_fp8_full_size_sampled_heads():
     say("chunk fwd fp8 full size")
     x = synth.prefill(3, B, H, T, dk, dv)
     stats = torch.zeros(4, dtype=torch.int64, device="cuda")
+    stats_inv = torch.zeros(4, dtype=torch.int64, device="cuda")
     heads = [(0, 0), (1, 7), (2, 12), (3, 15)]
     sel = {k: np.concatenate([f64(v[b:b + 1, h:h + 1]) for b, h in heads], axis=1) for k, v in x.items()}
     args = (sel["Q"], sel["K"], sel["V"], sel["beta"], sel["g"], 64, dk ** -0.5)
@@ -320,6 +321,13 @@ def test_chunk_fwd_fp8_full_size_sampled_heads():
                           o_dtype=torch.bfloat16)
         s = stats.cpu().tolist()
         assert s[0] == 0 and s[1] == 0
+        # the chunk forward's pre-pass (waves walking many chunks each) counts exactly what
+        # the batched inverse (one wave per chunk) counts over the same 32768 chunks
+        Kc, bc, gc = (cuda(x[k]) for k in ("K", "beta", "g"))
+        tri.gdn_tri_inverse_neumann(K=Kc, beta=bc, g=gc, C=64, N=3, mask=mask, compute="fp8", stats=stats_inv)
+        torch.cuda.synchronize()
+        assert stats_inv.cpu().tolist() == s, (stats_inv.cpu().tolist(), s)
+        del Kc, bc, gc
         Og = np.concatenate([O[b:b + 1, h:h + 1] for b, h in heads], axis=1)
         Sg = np.concatenate([S[b:b + 1, h:h + 1] for b, h in heads], axis=1)
         Or, Sr = oracle.chunk_fwd(*args, N=3, mask=mask)

@@ -75,28 +75,23 @@ __global__ __launch_bounds__(256) void build_A_kernel(BlocksArgs a, float* __res
   store_T_f32<NT>(A_out + (size_t)blk * C * C, AT);
 }
 
-// The inverse: one wave per block.  MAXD is the largest tile distance I - J kept
-// (NT - 1 in general, 1 for the band-masked sum with N <= 16).
+// The inverse of one block by the current wave.  MAXD is the largest tile distance
+// I - J kept (NT - 1 in general, 1 for the band-masked sum with N <= 16).
 // PK: write T - I as the chunk forward's row packs (store_T_packs) instead of T.
-template <int NT, int SRC, int DK, int CMP, int MODE, int MAXD, bool PK = false>
-__global__ __launch_bounds__(256) void inverse_kernel(BlocksArgs a, int N, int mask, void* T_out,
-                                                      int t_bf16, unsigned long long* stats, int S) {
+template <int NT, int SRC, int DK, int CMP, int MODE, int MAXD, bool PK>
+__device__ __forceinline__ void inverse_block(const BlocksArgs& a, int64_t blk, const BlockIn<NT, SRC, DK>& in,
+                                              int N, int mask, void* T_out, int t_bf16, Fp8Counts& cnt,
+                                              bool count, int S, int wave) {
   constexpr int C = 16 * NT;
-  const int64_t blk = (int64_t)blockIdx.x * (blockDim.x / WAVE) + (threadIdx.x / WAVE);
-  if (blk >= a.n_blocks) return;
   // fp8 and int8 mask A and every intermediate (the band sets the quantisation
   // scales); bf16 / fp32 mask only the final sum (identical result, see neumann_T)
   const int band = (MODE == MODE_NEUMANN && mask) ? N : -1;
   constexpr bool BANDED = (MODE == MODE_NEUMANN && (CMP == CMP_FP8 || CMP == CMP_INT8 || CMP == CMP_INT16));
-  Fp8Counts cnt{0, 0, 0, 0};
-  const bool count = (CMP == CMP_FP8) && stats != nullptr;
-  BlockIn<NT, SRC, DK> in;
-  in.load(a, blk);
   Mat<NT> AD, AT, TT;
   in.template to_A<MAXD, BANDED>(a, BANDED ? band : -1, AD, AT);
   if constexpr (MODE == MODE_EXACT && NT == 4 && CMP == CMP_BF16) {
     __shared__ __bf16 xt[4][64][XT_LD];  // per wave: X^T for the transpose read
-    doubling_T_lds(AD, AT, TT, xt[threadIdx.x / WAVE]);
+    doubling_T_lds(AD, AT, TT, xt[wave]);
   } else if constexpr (MODE == MODE_EXACT)
     doubling_T<NT, CMP>(AD, AT, TT);
   else if constexpr (MODE == MODE_RESIDUAL)
@@ -114,6 +109,41 @@ __global__ __launch_bounds__(256) void inverse_kernel(BlocksArgs a, int N, int m
     store_T_bf16<NT, MAXD>(reinterpret_cast<__bf16*>(T_out) + (size_t)blk * C * C, TT);
   } else {
     store_T_f32<NT, MAXD>(reinterpret_cast<float*>(T_out) + (size_t)blk * C * C, TT);
+  }
+}
+
+// The batched inverse.  PF = false: one wave per block.  PF = true: fewer waves than
+// blocks, each walking the blocks with the grid's stride; while it forms and stores T
+// of one block, the next block's raw inputs are already on their way into registers
+// (the index is clamped, so the load is unconditional and the wait before the next
+// block covers only those loads).  That overlap pays where the per-block work is long
+// next to its loads (the fp8 chain over many blocks); with few blocks, or light work,
+// two independent waves per SIMD hide the loads better, so PF stays off there.
+template <int NT, int SRC, int DK, int CMP, int MODE, int MAXD, bool PK = false, bool PF = false>
+__global__ __launch_bounds__(256) void inverse_kernel(BlocksArgs a, int N, int mask, void* T_out,
+                                                      int t_bf16, unsigned long long* stats, int S) {
+  Fp8Counts cnt{0, 0, 0, 0};
+  const bool count = (CMP == CMP_FP8) && stats != nullptr;
+  if constexpr (!PF) {
+    const int64_t blk = (int64_t)blockIdx.x * (blockDim.x / WAVE) + (threadIdx.x / WAVE);
+    if (blk >= a.n_blocks) return;
+    BlockIn<NT, SRC, DK> in;
+    in.load(a, blk);
+    inverse_block<NT, SRC, DK, CMP, MODE, MAXD, PK>(a, blk, in, N, mask, T_out, t_bf16, cnt, count, S,
+                                                    threadIdx.x / WAVE);
+  } else {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+    const int64_t first = (int64_t)blockIdx.x * (blockDim.x / WAVE) + wave;
+    if (first >= a.n_blocks) return;
+    const int64_t stride = (int64_t)gridDim.x * (blockDim.x / WAVE);
+    BlockIn<NT, SRC, DK> in;
+    in.load(a, first);
+    for (int64_t blk = first; blk < a.n_blocks; blk += stride) {
+      BlockIn<NT, SRC, DK> nxt;
+      nxt.load(a, blk + stride < a.n_blocks ? blk + stride : a.n_blocks - 1);
+      inverse_block<NT, SRC, DK, CMP, MODE, MAXD, PK>(a, blk, in, N, mask, T_out, t_bf16, cnt, count, S, wave);
+      in = nxt;
+    }
   }
   if constexpr (CMP == CMP_FP8) {
     if (count) flush_counts(cnt, stats);
@@ -174,6 +204,10 @@ static constexpr int WAVES_PER_WG = 4;
 static dim3 grid_for(int64_t n_blocks) {
   return dim3((unsigned)((n_blocks + WAVES_PER_WG - 1) / WAVES_PER_WG));
 }
+
+// Waves of the persistent fp8 pre-pass: two per SIMD of the 256 CUs.  It is used from
+// four blocks per wave on (below that, one wave per block measured as fast).
+static constexpr int64_t PF_WAVES = 2048;
 
 // dispatch helpers over (NT, SRC, DK); `F` is a generic lambda taking the three
 // integral constants and launching the right instantiation.
@@ -290,9 +324,13 @@ int launch_T_packs(const BlocksArgs& a, int mode, int N, int mask, int cmp, void
                    unsigned long long* stats, hipStream_t s) {
   if (a.C != 64) return -1;
   auto go = [&](auto dk, auto cm, auto md, auto maxd) {
-    hipLaunchKernelGGL((inverse_kernel<4, SRC_K_BF16, dk.value, cm.value, md.value, maxd.value, true>),
-                       grid_for(a.n_blocks), dim3(WAVE * WAVES_PER_WG), 0, s, a, N, mask, packs, 0,
-                       stats, 0);
+    if (cm.value == CMP_FP8 && a.n_blocks >= 4 * PF_WAVES)
+      hipLaunchKernelGGL((inverse_kernel<4, SRC_K_BF16, dk.value, cm.value, md.value, maxd.value, true, true>),
+                         grid_for(PF_WAVES), dim3(WAVE * WAVES_PER_WG), 0, s, a, N, mask, packs, 0, stats, 0);
+    else
+      hipLaunchKernelGGL((inverse_kernel<4, SRC_K_BF16, dk.value, cm.value, md.value, maxd.value, true>),
+                         grid_for(a.n_blocks), dim3(WAVE * WAVES_PER_WG), 0, s, a, N, mask, packs, 0,
+                         stats, 0);
     return 0;
   };
   using M1 = std::integral_constant<int, 1>;
