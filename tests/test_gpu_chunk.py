@@ -304,6 +304,31 @@ def test_chunk_fwd_full_size_all_heads():
             assert relF(S[b, h], Sr[b, h]) <= TOL["bf16"], (b, h, relF(S[b, h], Sr[b, h]))
 
 
+@pytest.mark.parametrize("mask", [False, True])
+def test_chunk_fwd_fp8_ragged_chunk_count(mask):
+    """8256 chunks (129 heads of 64).  Unmasked, the fp8 pre-pass then has waves walking 4
+    or 5 chunks each, the last round only partly filled.  Its counters must equal the
+    batched inverse's over the same chunks, and the last head, whose chunks are the
+    pre-pass's tail, is checked against the oracle's e4m3 emulation."""
+    B, H, T, dk, dv = 3, 43, 64 * 64, 128, 128
+    say(f"chunk fwd fp8 ragged chunk count mask={mask}")
+    x = synth.prefill(23, B, H, T, dk, dv)
+    stats = torch.zeros(4, dtype=torch.int64, device="cuda")
+    stats_inv = torch.zeros(4, dtype=torch.int64, device="cuda")
+    O, S = _run_chunk(x, C=64, scale=dk ** -0.5, N=3, mask=mask, compute="fp8", stats=stats,
+                      o_dtype=torch.float32)
+    tri.gdn_tri_inverse_neumann(K=cuda(x["K"]), beta=cuda(x["beta"]), g=cuda(x["g"]), C=64, N=3, mask=mask,
+                                compute="fp8", stats=stats_inv)
+    torch.cuda.synchronize()
+    assert stats.cpu().tolist() == stats_inv.cpu().tolist(), (stats.cpu().tolist(), stats_inv.cpu().tolist())
+    b, h = 2, 42
+    sel = {k: f64(v[b:b + 1, h:h + 1]) for k, v in x.items()}
+    Oe, Se = oracle.chunk_fwd(sel["Q"], sel["K"], sel["V"], sel["beta"], sel["g"], 64, dk ** -0.5,
+                              inv_mode=oracle.INV_FP8, N=3, mask=mask)
+    assert relF(O[b:b + 1, h:h + 1], Oe) <= TOL_FP8_EMU, relF(O[b:b + 1, h:h + 1], Oe)
+    assert relF(S[b:b + 1, h:h + 1], Se) <= TOL_FP8_EMU, relF(S[b:b + 1, h:h + 1], Se)
+
+
 def test_chunk_fwd_fp8_full_size_sampled_heads():
     """B=4, H=16, seq 32768 with the fp8 inverse (the launch the fp8 measurement times),
     masked and unmasked: four heads against the oracle (fp64 and the e4m3 emulation),

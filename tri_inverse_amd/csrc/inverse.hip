@@ -117,8 +117,8 @@ __device__ __forceinline__ void inverse_block(const BlocksArgs& a, int64_t blk, 
 // of one block, the next block's raw inputs are already on their way into registers
 // (the index is clamped, so the load is unconditional and the wait before the next
 // block covers only those loads).  That overlap pays where the per-block work is long
-// next to its loads (the fp8 chain over many blocks); with few blocks, or light work,
-// two independent waves per SIMD hide the loads better, so PF stays off there.
+// next to its loads (the unmasked fp8 chain over many blocks); with fewer blocks or
+// lighter work, independent waves hide the loads better, so PF stays off there.
 template <int NT, int SRC, int DK, int CMP, int MODE, int MAXD, bool PK = false, bool PF = false>
 __global__ __launch_bounds__(256) void inverse_kernel(BlocksArgs a, int N, int mask, void* T_out,
                                                       int t_bf16, unsigned long long* stats, int S) {
@@ -205,8 +205,10 @@ static dim3 grid_for(int64_t n_blocks) {
   return dim3((unsigned)((n_blocks + WAVES_PER_WG - 1) / WAVES_PER_WG));
 }
 
-// Waves of the persistent fp8 pre-pass: two per SIMD of the 256 CUs.  It is used from
-// four blocks per wave on (below that, one wave per block measured as fast).
+// Waves of the persistent fp8 pre-pass: two per SIMD of the 256 CUs.  It is used for the
+// unmasked chain (all ten lower tiles per power) from four blocks per wave on: measured
+// on one box at 32768 chunks, 633 -> 453 us.  The band-masked chain has a third of the
+// tiles and is faster with one wave per chunk (228 against 271 us), as are fewer blocks.
 static constexpr int64_t PF_WAVES = 2048;
 
 // dispatch helpers over (NT, SRC, DK); `F` is a generic lambda taking the three
@@ -324,7 +326,7 @@ int launch_T_packs(const BlocksArgs& a, int mode, int N, int mask, int cmp, void
                    unsigned long long* stats, hipStream_t s) {
   if (a.C != 64) return -1;
   auto go = [&](auto dk, auto cm, auto md, auto maxd) {
-    if (cm.value == CMP_FP8 && a.n_blocks >= 4 * PF_WAVES)
+    if (cm.value == CMP_FP8 && maxd.value == 3 && a.n_blocks >= 4 * PF_WAVES)
       hipLaunchKernelGGL((inverse_kernel<4, SRC_K_BF16, dk.value, cm.value, md.value, maxd.value, true, true>),
                          grid_for(PF_WAVES), dim3(WAVE * WAVES_PER_WG), 0, s, a, N, mask, packs, 0, stats, 0);
     else
