@@ -184,8 +184,8 @@ __device__ __forceinline__ void write_gates(float gl, float bl, ChunkGates& GT) 
 // scan and stays zero.
 constexpr int MODE_BAND = 16;  // chunk-only codes next to the MODE_* values
 // Every other variant (the truncated sum on bf16 or fp8 operands, masked or not, and the
-// exact product) has its T - I formed by the batched pre-pass, one wave per block, as
-// the row packs the state step reads; the T wave only streams them into LDS.
+// exact product) has its T - I formed by the batched pre-pass as the row packs the
+// state step reads; the T wave only streams them into LDS.
 constexpr int MODE_LOAD = 17;
 
 // row-pack slot (bf16 index into trp) of T - I at row i, column j

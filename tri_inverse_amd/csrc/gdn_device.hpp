@@ -148,6 +148,85 @@ __device__ __forceinline__ void store_pair_bf16(__bf16* __restrict__ row, int e,
   *reinterpret_cast<u32x4*>(row + 16 * (e + (g & 1)) + 8 * (g >> 1)) = out;
 }
 
+// ---- whole 128-byte row pieces from output tiles -----------------------------------
+// An output tile in T-form gives lane (g, c) row c and columns 4g .. 4g + 3, so one store
+// of a tile writes 16 rows of 64 bytes (fp32) or 32 bytes (bf16), and each 128-byte line
+// reaches memory in parts.  Below, lanes c and c ^ 8 of each 16-lane row trade values
+// (DPP row_ror:8) so that each store instruction covers 8 rows of 128 contiguous bytes.
+
+// lanes c < 8 keep lo and take the partner's hi as their second value; lanes c >= 8 take
+// the partner's lo as their first value and keep hi
+__device__ __forceinline__ void trade8(uint32_t lo, uint32_t hi, uint32_t& v0, uint32_t& v1) {
+  const bool up = (lane_id() & 15) >= 8;
+  const uint32_t got = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(up ? lo : hi), 0x128, 0xf, 0xf, false);
+  v0 = up ? got : lo;
+  v1 = up ? hi : got;
+}
+
+template <bool NTS, class V>
+__device__ __forceinline__ void store16(V* p, const V& v) {
+  if constexpr (NTS)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
+}
+
+// fp32 tiles a (columns 0 .. 15) and b (16 .. 31) of a 16-row band at base (row stride
+// ld elements): store k writes rows 8k + (c & 7), columns 4(g + 4(c >> 3)) .. + 3
+template <bool NTS>
+__device__ __forceinline__ void store_rows_f32x2(float* __restrict__ base, size_t ld, const f32x4& a,
+                                                 const f32x4& b) {
+  const int l = lane_id(), g = l >> 4, c = l & 15;
+  f32x4 v0, v1;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float ar = a[r], br = b[r];  // vector elements to scalars before any bit cast
+    uint32_t w0, w1;
+    trade8(__builtin_bit_cast(uint32_t, ar), __builtin_bit_cast(uint32_t, br), w0, w1);
+    v0[r] = __builtin_bit_cast(float, w0);
+    v1[r] = __builtin_bit_cast(float, w1);
+  }
+  const size_t o = (size_t)(c & 7) * ld + 4 * (g + 4 * (c >> 3));
+  store16<NTS>(reinterpret_cast<f32x4*>(base + o), v0);
+  store16<NTS>(reinterpret_cast<f32x4*>(base + o + 8 * ld), v1);
+}
+
+// four bf16 tiles t[0..3] (columns 0 .. 63) of a 16-row band at base: the tile pairs
+// (0, 1) and (2, 3) first become 16 contiguous bytes per lane (v_permlane16_swap: group g
+// then holds columns 16(e + g % 2) + 8(g / 2) .. + 7 of pair e), then lanes c and c ^ 8
+// trade, so that store k writes rows 8k + (c & 7), columns 32(c >> 3) + 16(g % 2) +
+// 8(g / 2) .. + 7
+template <bool NTS>
+__device__ __forceinline__ void store_rows_bf16x4(__bf16* __restrict__ base, size_t ld, const f32x4 (&t)[4]) {
+  const int l = lane_id(), g = l >> 4, c = l & 15;
+  u32x4 pr[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const bf16x4 h0 = pack4(t[2 * e]), h1 = pack4(t[2 * e + 1]);
+    const u32x2 w0 = __builtin_bit_cast(u32x2, h0), w1 = __builtin_bit_cast(u32x2, h1);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const unsigned x0 = w0[k], x1 = w1[k];
+      const auto sw = __builtin_amdgcn_permlane16_swap(x0, x1, false, false);
+      const unsigned y0 = sw[0], y1 = sw[1];
+      pr[e][k] = y0;
+      pr[e][2 + k] = y1;
+    }
+  }
+  u32x4 v0, v1;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t lo = pr[0][k], hi = pr[1][k];
+    uint32_t a0, a1;
+    trade8(lo, hi, a0, a1);
+    v0[k] = a0;
+    v1[k] = a1;
+  }
+  const size_t o = (size_t)(c & 7) * ld + 32 * (c >> 3) + 16 * (g & 1) + 8 * (g >> 1);
+  store16<NTS>(reinterpret_cast<u32x4*>(base + o), v0);
+  store16<NTS>(reinterpret_cast<u32x4*>(base + o + 8 * ld), v1);
+}
+
 // ---- wave-wide reductions and scans (wave64) ------------------------------------
 // All in the VALU (no LDS round trip): DPP within each 16-lane row, then
 // v_permlane16_swap / v_permlane32_swap (or readlane) across the four rows.  Each swap

@@ -1,5 +1,9 @@
-// inverse.hip -- batched per-block kernels: A build and the two multiplication-only
-// inverses of I - A, one wave (64 lanes) per C x C block, everything in registers.
+// inverse.hip -- batched per-block kernels: A build, the multiplication-only inverses of
+// I - A (truncated / masked Neumann sum in fp32, bf16, fp8, int8 or int16 operands, exact
+// doubling, residual correction) and forward substitution.  A wave (64 lanes) works on
+// one C x C block at a time with the matrices in registers (the exact 64 x 64 doubling
+// also passes each square through a per-wave LDS slice); the unmasked fp8 chain over
+// many blocks walks several blocks per wave.
 //
 // [GEO] "When Good Enough Is Optimal: Multiplication-Only Matrix Inversion
 // Approximation for Quantized Gated DeltaNet": problem statement (T = (I - A)^-1 per
@@ -72,7 +76,10 @@ __global__ __launch_bounds__(256) void build_A_kernel(BlocksArgs a, float* __res
   else
     gram_f32<NT, DK>(reinterpret_cast<const float*>(a.K) + (size_t)blk * C * DK, S);
   gram_to_A<NT>(S, gt, -1, AD, AT);
-  store_T_f32<NT>(A_out + (size_t)blk * C * C, AT);
+  if constexpr (NT == 4)
+    store_T_rows_f32<3>(A_out + (size_t)blk * C * C, AT);
+  else
+    store_T_f32<NT>(A_out + (size_t)blk * C * C, AT);
 }
 
 // The inverse of one block by the current wave.  MAXD is the largest tile distance
@@ -106,9 +113,15 @@ __device__ __forceinline__ void inverse_block(const BlocksArgs& a, int64_t blk, 
     static_assert(NT == 4, "row packs of 64 x 64 blocks");
     store_T_packs(reinterpret_cast<bf16x8*>(T_out) + (size_t)blk * T_PACKS * WAVE, TT);
   } else if (t_bf16) {
-    store_T_bf16<NT, MAXD>(reinterpret_cast<__bf16*>(T_out) + (size_t)blk * C * C, TT);
+    if constexpr (NT == 4)
+      store_T_rows_bf16<MAXD>(reinterpret_cast<__bf16*>(T_out) + (size_t)blk * C * C, TT);
+    else
+      store_T_bf16<NT, MAXD>(reinterpret_cast<__bf16*>(T_out) + (size_t)blk * C * C, TT);
   } else {
-    store_T_f32<NT, MAXD>(reinterpret_cast<float*>(T_out) + (size_t)blk * C * C, TT);
+    if constexpr (NT == 4)
+      store_T_rows_f32<MAXD>(reinterpret_cast<float*>(T_out) + (size_t)blk * C * C, TT);
+    else
+      store_T_f32<NT, MAXD>(reinterpret_cast<float*>(T_out) + (size_t)blk * C * C, TT);
   }
 }
 

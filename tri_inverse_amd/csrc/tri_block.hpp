@@ -1174,6 +1174,33 @@ __device__ __forceinline__ void store_T_bf16(__bf16* __restrict__ out, const Mat
     }
 }
 
+// ---- T of a 64 x 64 block as whole 128-byte row pieces (store_rows_*) ----------------
+// Tiles beyond MAXD tile-diagonals and above the diagonal are zero.
+template <int MAXD>
+__device__ __forceinline__ f32x4 tile_kept(const Mat<4>& M, int I, int J) {
+  return (J <= I && I - J <= MAXD) ? M.t[I][J] : zero4();
+}
+
+template <int MAXD>
+__device__ __forceinline__ void store_T_rows_f32(float* __restrict__ out, const Mat<4>& M) {
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int J = 0; J < 4; J += 2)
+      store_rows_f32x2<true>(out + (size_t)16 * I * 64 + 16 * J, 64, tile_kept<MAXD>(M, I, J),
+                             tile_kept<MAXD>(M, I, J + 1));
+}
+
+template <int MAXD>
+__device__ __forceinline__ void store_T_rows_bf16(__bf16* __restrict__ out, const Mat<4>& M) {
+#pragma unroll
+  for (int I = 0; I < 4; ++I) {
+    const f32x4 t[4] = {tile_kept<MAXD>(M, I, 0), tile_kept<MAXD>(M, I, 1), tile_kept<MAXD>(M, I, 2),
+                        tile_kept<MAXD>(M, I, 3)};
+    store_rows_bf16x4<true>(out + (size_t)16 * I * 64, 64, t);
+  }
+}
+
 // T - I of a 64 x 64 block as the six left-operand row packs of the chunk forward's
 // product (T - I) Y: pack k <-> (I, p) in the order (0,0) (1,0) (2,0) (2,1) (3,0) (3,1),
 // tiles (I, 2p) and (I, 2p + 1) in T-form, 16 bytes per lane at out[64 k + lane].  The

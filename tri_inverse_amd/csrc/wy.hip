@@ -44,24 +44,25 @@ __device__ __forceinline__ void stage_rows(const __bf16* __restrict__ X, WyLds<N
 // row-major LDS copy with the transpose read: lane (g, j) addressing
 // xr[r0 + 4g + j/4][c0 + 4(j%4)] receives xr[r0 + 4g + k][c0 + j], k = 0..3, which is
 // the token pair p column fragment (slot t <-> token 32p + 16(t/4) + 4g + t%4) of
-// column c0 + j.  Stored row-major [C][D]: fp32 as 4 consecutive columns per lane,
-// bf16 as 8 (two column tiles at a time, store_pair_bf16).
+// column c0 + j.  Four column tiles at a time, stored row-major [C][D] as whole 128-byte
+// row pieces (store_rows_bf16x4, store_rows_f32x2), so that no line is written in parts
+// at different times.
 template <int NT, int D>
 __device__ __forceinline__ void apply_rows(const bf16x8 (&rp)[NT][(NT + 1) / 2],
                                            const bf16x8 (&rl)[NT][(NT + 1) / 2],
                                            const WyLds<NT, D>& L, void* __restrict__ out,
                                            bool out_bf16) {
   constexpr int C = 16 * NT, NP = (NT + 1) / 2;
-  static_assert(D % 32 == 0, "column tiles are stored in pairs");
+  static_assert(D % 64 == 0, "column tiles are stored four at a time");
   const int l = lane_id(), g = l >> 4, c = l & 15;
 #pragma unroll
-  for (int e2 = 0; e2 < D / 32; ++e2) {
-    bf16x8 cp[2][NP];
+  for (int e4 = 0; e4 < D / 64; ++e4) {
+    bf16x8 cp[4][NP];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 4; ++h)
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const int e = 2 * e2 + h;
+        const int e = 4 * e4 + h;
         const bf16x4 lo = lds_read_tr4(&L.xr[32 * p + 4 * g + (c >> 2)][16 * e + 4 * (c & 3)]);
         bf16x4 hi = bf16x4{};
         if (32 * p + 16 < C) hi = lds_read_tr4(&L.xr[32 * p + 16 + 4 * g + (c >> 2)][16 * e + 4 * (c & 3)]);
@@ -69,9 +70,9 @@ __device__ __forceinline__ void apply_rows(const bf16x8 (&rp)[NT][(NT + 1) / 2],
       }
 #pragma unroll
     for (int I = 0; I < NT; ++I) {
-      f32x4 acc[2];
+      f32x4 acc[4];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < 4; ++h) {
         acc[h] = zero4();
 #pragma unroll
         for (int p = 0; p <= I / 2; ++p) {
@@ -79,13 +80,12 @@ __device__ __forceinline__ void apply_rows(const bf16x8 (&rp)[NT][(NT + 1) / 2],
           acc[h] = mma_bf16(cp[h][p], rl[I][p], acc[h]);
         }
       }
-      const size_t rowo = (size_t)(16 * I + c) * D;
+      const size_t o = (size_t)16 * I * D + 64 * e4;
       if (out_bf16) {
-        store_pair_bf16(reinterpret_cast<__bf16*>(out) + rowo, 2 * e2, acc[0], acc[1]);
+        store_rows_bf16x4<false>(reinterpret_cast<__bf16*>(out) + o, D, acc);
       } else {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + rowo + 16 * (2 * e2 + h) + 4 * g) = acc[h];
+        store_rows_f32x2<false>(reinterpret_cast<float*>(out) + o, D, acc[0], acc[1]);
+        store_rows_f32x2<false>(reinterpret_cast<float*>(out) + o + 32, D, acc[2], acc[3]);
       }
     }
   }
