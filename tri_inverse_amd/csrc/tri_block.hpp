@@ -156,12 +156,18 @@ struct KBlock {
   float gl, bl;
 };
 
-template <int NT, int DK, bool NT_LOAD = false>
+// GATES_FIRST: the gate inputs are loaded before the key rows (loads complete in order),
+// so the gate factors can be formed while the keys are still arriving
+template <int NT, int DK, bool NT_LOAD = false, bool GATES_FIRST = false>
 __device__ __forceinline__ void load_kblock(const __bf16* __restrict__ K,
                                             const float* __restrict__ beta,
                                             const float* __restrict__ g, KBlock<NT, DK>& kb) {
   constexpr int C = 16 * NT;
   const int l = lane_id(), grp = l >> 4, c = l & 15;
+  if constexpr (GATES_FIRST) {
+    kb.gl = (l < C) ? g[l] : 0.f;
+    kb.bl = (l < C) ? beta[l] : 0.f;
+  }
 #pragma unroll
   for (int I = 0; I < NT; ++I)
 #pragma unroll
@@ -171,8 +177,10 @@ __device__ __forceinline__ void load_kblock(const __bf16* __restrict__ K,
         // streaming (non-temporal) when nothing reads these rows again
         kb.kf[I][s] = NT_LOAD ? __builtin_nontemporal_load(src) : *src;
       }
-  kb.gl = (l < C) ? g[l] : 0.f;
-  kb.bl = (l < C) ? beta[l] : 0.f;
+  if constexpr (!GATES_FIRST) {
+    kb.gl = (l < C) ? g[l] : 0.f;
+    kb.bl = (l < C) ? beta[l] : 0.f;
+  }
 }
 
 // gate cumsum and gather to the two index families from the raw lane values
