@@ -27,8 +27,8 @@ struct BlockIn<NT, SRC_K_BF16, DK> {
   // GF: load the gate inputs first and form the gate factors (they need only those two
   // loads) while the key rows arrive, before any Gram product waits for the keys.
   // Measured faster where the block's work after A is long (exact doubling, quantised
-  // chains: 8-9 %) and slower for the light bf16 / fp32 truncated sums (3-4 %), which
-  // keep the compiler's own order.
+  // chains: 8-10 %; residual correction: 2-3 %) and slower for the light bf16 / fp32
+  // truncated sums (3-4 %), which keep the compiler's own order.
   template <bool GF = false>
   __device__ __forceinline__ void load(const BlocksArgs& a, int64_t blk) {
     constexpr int C = 16 * NT;
@@ -93,7 +93,8 @@ __global__ __launch_bounds__(256) void build_A_kernel(BlocksArgs a, float* __res
 // long work after A: the gate factors are formed first, while the keys arrive (BlockIn)
 template <int CMP, int MODE>
 constexpr bool gates_first() {
-  return MODE == MODE_EXACT || (MODE == MODE_NEUMANN && (CMP == CMP_FP8 || CMP == CMP_INT8 || CMP == CMP_INT16));
+  return MODE == MODE_EXACT || MODE == MODE_RESIDUAL ||
+         (MODE == MODE_NEUMANN && (CMP == CMP_FP8 || CMP == CMP_INT8 || CMP == CMP_INT16));
 }
 
 // The inverse of one block by the current wave.  MAXD is the largest tile distance
