@@ -163,17 +163,14 @@ __global__ __launch_bounds__(256) void wy_kernel(BlocksArgs a, const void* __res
 #pragma unroll
         for (int s = 0; s < DK / 32; ++s)
           kb.kf[I][s] = *reinterpret_cast<const bf16x8*>(&LK.xr[16 * I + c][32 * s + 8 * g]);
-      kb.gl = (l < C) ? a.g[(size_t)b * C + l] : 0.f;
-      kb.bl = (l < C) ? a.beta[(size_t)b * C + l] : 0.f;
     } else {
       load_kblock<NT, DK>(reinterpret_cast<const __bf16*>(a.K) + (size_t)b * C * DK, a.beta + (size_t)b * C,
                           a.g + (size_t)b * C, kb);
     }
-    Gates<NT> g2;
-    gates_from_lanes<NT>(kb.gl, kb.bl, a.g_cumulative != 0, g2);
+    // A from the Gram tiles and the gate factors formed at the top (gt)
     Mat<NT> S, AD, AT;
     gram_from_frags<NT, DK, MAXD>(kb, S);
-    gram_to_A<NT, MAXD, false>(S, g2, -1, AD, AT);
+    gram_to_A<NT, MAXD, false>(S, gt, -1, AD, AT);
     if constexpr (MODE == MODE_EXACT) {
       doubling_T<NT, CMP_BF16>(AD, AT, TT);
     } else {
