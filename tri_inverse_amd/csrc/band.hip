@@ -11,9 +11,10 @@
 // work linear in the chunk size and independent across tiles.
 //
 // A workgroup of eight waves covers 128 rows of one block; it stages those rows plus the
-// 16 rows above them (K, V columns, log-gates, beta) in LDS with coalesced 16-byte
-// loads (eight waves rather than four: an eighth of the rows staged twice instead of a
-// quarter, and 16 waves per CU instead of 12; 13-14 % faster at C = 128 and 256), then each wave builds its window's A (gate differences need only the
+// 16 rows above them (K, log-gates, beta; later the V columns into the same buffer) in
+// LDS with coalesced 16-byte loads (eight waves rather than four: an eighth of the rows
+// staged twice instead of a quarter, 13-14 % faster at C = 128 and 256; one buffer for
+// K and then V: half the LDS, 5-8 % faster again), then each wave builds its window's A (gate differences need only the
 // window's own log-gates), forms the masked sum with the 2 x 2 tile products, and
 // writes its tile row of T, or of W = T diag(s) K and U = T diag(beta) V.  The key
 // gate s = beta exp(G) needs G itself, the block prefix sum, which the workgroup
@@ -27,10 +28,11 @@ constexpr int BAND_WAVES = 8;        // row tiles per workgroup
 constexpr int BAND_ROWS = 16 * (BAND_WAVES + 1);
 constexpr int BAND_PAD = 8;
 
+// one row buffer: the staged K rows, then (after the W product) the V rows
 template <int DK, int DV>
 struct alignas(16) BandLds {
-  __bf16 k[BAND_ROWS][DK + BAND_PAD];
-  __bf16 v[DV ? BAND_ROWS : 1][(DV ? DV : 8) + BAND_PAD];
+  static constexpr int LD = (DK > DV ? DK : DV) + BAND_PAD;
+  __bf16 x[BAND_ROWS][LD];
   float gam[BAND_ROWS];
   float bet[BAND_ROWS];
   float gpre;  // sum of the log-gates of the block's rows above the staged ones
@@ -51,20 +53,20 @@ struct BandArgs {
 
 // K^T (or V^T) operand fragment over the 32 window rows starting at local row r0,
 // columns 16e .. 16e + 15: lane (g, c) slot t <-> X[r0 + 16(t/4) + 4g + t%4][16e + c]
-template <int D, int ROWS>
-__device__ __forceinline__ bf16x8 window_colpack(const __bf16 (&X)[ROWS][D + BAND_PAD], int r0, int e) {
+template <int LD>
+__device__ __forceinline__ bf16x8 window_colpack(const __bf16* X, int r0, int e) {
   const int l = lane_id(), g = l >> 4, j = l & 15;
-  const __bf16* p0 = &X[r0 + 4 * g + (j >> 2)][16 * e + 4 * (j & 3)];
-  const __bf16* p1 = &X[r0 + 16 + 4 * g + (j >> 2)][16 * e + 4 * (j & 3)];
+  const __bf16* p0 = X + (r0 + 4 * g + (j >> 2)) * LD + 16 * e + 4 * (j & 3);
+  const __bf16* p1 = X + (r0 + 16 + 4 * g + (j >> 2)) * LD + 16 * e + 4 * (j & 3);
   return join8(lds_read_tr4(p0), lds_read_tr4(p1));
 }
 
 // Z (T-form row tile) = R X over the window, R as a hi/lo pair of row packs; stored
 // row-major at row `row` of out: fp32 as columns 16e + 4g .. +3, bf16 two column tiles
 // at a time with 16 contiguous bytes per lane (store_pair_bf16)
-template <int D, int ROWS>
+template <int D, int LD>
 __device__ __forceinline__ void window_apply(const bf16x8& rh, const bf16x8& rl,
-                                             const __bf16 (&X)[ROWS][D + BAND_PAD], int r0,
+                                             const __bf16* X, int r0,
                                              void* __restrict__ out, int64_t row, bool obf16) {
   static_assert(D % 32 == 0, "column tiles are stored in pairs");
   const int g = lane_id() >> 4;
@@ -73,7 +75,7 @@ __device__ __forceinline__ void window_apply(const bf16x8& rh, const bf16x8& rl,
     f32x4 acc[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const bf16x8 cp = window_colpack<D, ROWS>(X, r0, 2 * e2 + h);
+      const bf16x8 cp = window_colpack<LD>(X, r0, 2 * e2 + h);
       acc[h] = mma_bf16(cp, rh, zero4());
       acc[h] = mma_bf16(cp, rl, acc[h]);
     }
@@ -118,22 +120,7 @@ __global__ __launch_bounds__(BAND_WAVES * WAVE) void band_kernel(BandArgs p) {
       const int gr = row0 + r;
       if (e < NSEG) {
         const bf16x8 v = *reinterpret_cast<const bf16x8*>(Kb + (int64_t)(gr < 0 ? 0 : gr) * DK + 8 * s);
-        *reinterpret_cast<bf16x8*>(&L.k[r][8 * s]) = gr < 0 ? bf16x8{} : v;
-      }
-    }
-    if constexpr (DV > 0) {
-      constexpr int SV = DV / 8;
-      constexpr int NSV = BAND_ROWS * SV;
-      constexpr int NV = (NSV + BAND_WAVES * WAVE - 1) / (BAND_WAVES * WAVE);
-      const __bf16* Vb = p.V + b * C * DV;
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int e = i * BAND_WAVES * WAVE + tid, r = e / SV, s = e % SV;
-        const int gr = row0 + r;
-        if (e < NSV) {
-          const bf16x8 v = *reinterpret_cast<const bf16x8*>(Vb + (int64_t)(gr < 0 ? 0 : gr) * DV + 8 * s);
-          *reinterpret_cast<bf16x8*>(&L.v[r][8 * s]) = gr < 0 ? bf16x8{} : v;
-        }
+        *reinterpret_cast<bf16x8*>(&L.x[r][8 * s]) = gr < 0 ? bf16x8{} : v;
       }
     }
     if (tid < BAND_ROWS) {
@@ -163,7 +150,7 @@ __global__ __launch_bounds__(BAND_WAVES * WAVE) void band_kernel(BandArgs p) {
 #pragma unroll
   for (int J = 0; J < 2; ++J)
 #pragma unroll
-    for (int s = 0; s < DK / 32; ++s) kb.kf[J][s] = *reinterpret_cast<const bf16x8*>(&L.k[r0 + 16 * J + c][32 * s + 8 * g]);
+    for (int s = 0; s < DK / 32; ++s) kb.kf[J][s] = *reinterpret_cast<const bf16x8*>(&L.x[r0 + 16 * J + c][32 * s + 8 * g]);
   kb.gl = gl;
   kb.bl = bl;
   Gates<2> gt;
@@ -215,9 +202,31 @@ __global__ __launch_bounds__(BAND_WAVES * WAVE) void band_kernel(BandArgs p) {
     bf16x8 wh, wl, uh, ul;
     hilo(tw[0], tw[1], wh, wl);
     hilo(tu[0], tu[1], uh, ul);
+    // the V rows go into registers now, so that their loads overlap the W product, and
+    // into the row buffer once every wave is done with K
+    constexpr int SV = DV / 8;
+    constexpr int NSV = BAND_ROWS * SV;
+    constexpr int NV = (NSV + BAND_WAVES * WAVE - 1) / (BAND_WAVES * WAVE);
+    const __bf16* Vb = p.V + b * C * DV;
+    bf16x8 vr[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = i * BAND_WAVES * WAVE + tid, r = e / SV, s = e % SV;
+      const int gr = row0 + r;
+      vr[i] = bf16x8{};
+      if (e < NSV && gr >= 0) vr[i] = *reinterpret_cast<const bf16x8*>(Vb + (int64_t)gr * DV + 8 * s);
+    }
     const int64_t row = b * C + 16 * I + c;
-    window_apply<DK, BAND_ROWS>(wh, wl, L.k, r0, p.W_out, row, p.out_bf16 != 0);
-    window_apply<DV, BAND_ROWS>(uh, ul, L.v, r0, p.U_out, row, p.out_bf16 != 0);
+    constexpr int LD = BandLds<DK, DV>::LD;
+    window_apply<DK, LD>(wh, wl, &L.x[0][0], r0, p.W_out, row, p.out_bf16 != 0);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = i * BAND_WAVES * WAVE + tid, r = e / SV, s = e % SV;
+      if (e < NSV) *reinterpret_cast<bf16x8*>(&L.x[r][8 * s]) = vr[i];
+    }
+    __syncthreads();
+    window_apply<DV, LD>(uh, ul, &L.x[0][0], r0, p.U_out, row, p.out_bf16 != 0);
   }
 }
 
