@@ -162,15 +162,19 @@ __global__ __launch_bounds__(BAND_WAVES * WAVE) void band_kernel(BandArgs p) {
   neumann_T<2, CMP_BF16, 1>(AD, AT, p.N, true, TT, cnt, false);
 
   if constexpr (TOUT) {
-    // row tile I of T: tiles (I, I-1) and (I, I) from the window, zero elsewhere
+    // row tile I of T: tiles (I, I-1) and (I, I) from the window, zero elsewhere, as
+    // whole 128-byte row pieces (store_rows_*)
     const int NTB = C / 16;
-    for (int J = 0; J < NTB; ++J) {
-      const f32x4 t = (J == I) ? TT.t[1][1] : (J == I - 1) ? TT.t[1][0] : zero4();
-      const int64_t o = b * C * C + (int64_t)(16 * I + c) * C + 16 * J + 4 * g;
-      if (p.t_bf16)
-        *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(p.T_out) + o) = pack4(t);
-      else
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.T_out) + o) = t;
+    auto tile = [&](int J) -> f32x4 { return (J == I) ? TT.t[1][1] : (J == I - 1) ? TT.t[1][0] : zero4(); };
+    const int64_t rowbase = b * C * C + (int64_t)(16 * I) * C;
+    if (p.t_bf16) {
+      for (int J = 0; J < NTB; J += 4) {
+        const f32x4 t[4] = {tile(J), tile(J + 1), tile(J + 2), tile(J + 3)};
+        store_rows_bf16x4<true>(reinterpret_cast<__bf16*>(p.T_out) + rowbase + 16 * J, C, t);
+      }
+    } else {
+      for (int J = 0; J < NTB; J += 2)
+        store_rows_f32x2<true>(reinterpret_cast<float*>(p.T_out) + rowbase + 16 * J, C, tile(J), tile(J + 1));
     }
   }
   if constexpr (DV > 0) {

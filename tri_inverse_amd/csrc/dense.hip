@@ -304,21 +304,32 @@ __global__ __launch_bounds__(NT * WAVE / 2, 1) void dense_kernel(DenseArgs p) {
   }
 
   if constexpr (DV == 0) {
-    // ---- T out: the owned rows, zero above the diagonal ---------------------------
+    // ---- T out: the owned rows, zero above the diagonal, as whole 128-byte row pieces
     auto store_row = [&](int I, auto& row, auto nj) {
       constexpr int NJ = decltype(nj)::value;
-      static_for<NT>([&](auto Jc) {
+      auto tile = [&](auto Jc) -> f32x4 {
         constexpr int J = decltype(Jc)::value;
         f32x4 t = zero4();
         if constexpr (J < NJ) {
           if (J <= I) t = row[J];
         }
-        const int64_t o = b * C * C + (int64_t)(16 * I + c) * C + 16 * J + 4 * g;
-        if (p.t_bf16)
-          *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(p.T_out) + o) = pack4(t);
-        else
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.T_out) + o) = t;
-      });
+        return t;
+      };
+      const int64_t rowbase = b * C * C + (int64_t)(16 * I) * C;
+      if (p.t_bf16) {
+        static_for<NT / 4>([&](auto qc) {
+          constexpr int J = 4 * decltype(qc)::value;
+          const f32x4 t[4] = {tile(std::integral_constant<int, J>{}), tile(std::integral_constant<int, J + 1>{}),
+                              tile(std::integral_constant<int, J + 2>{}), tile(std::integral_constant<int, J + 3>{})};
+          store_rows_bf16x4<true>(reinterpret_cast<__bf16*>(p.T_out) + rowbase + 16 * J, C, t);
+        });
+      } else {
+        static_for<NT / 2>([&](auto pc) {
+          constexpr int J = 2 * decltype(pc)::value;
+          store_rows_f32x2<true>(reinterpret_cast<float*>(p.T_out) + rowbase + 16 * J, C,
+                                 tile(std::integral_constant<int, J>{}), tile(std::integral_constant<int, J + 1>{}));
+        });
+      }
     };
     store_row(I0, T.a, std::integral_constant<int, NT / 2>{});
     store_row(I1, T.b, std::integral_constant<int, NT>{});
