@@ -131,6 +131,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 // v_permlane16_swap of (tile e, tile e+1) exchanges the odd groups' tile-e values with
 // the even groups' tile-(e+1) values, after which group g holds the 8 consecutive
 // columns 16 (e + g % 2) + 8 (g / 2) .. +7 of the pair.
+template <bool NTS = false>
 __device__ __forceinline__ void store_pair_bf16(__bf16* __restrict__ row, int e, const f32x4& a0,
                                                 const f32x4& a1) {
   const int g = lane_id() >> 4;
@@ -145,7 +146,11 @@ __device__ __forceinline__ void store_pair_bf16(__bf16* __restrict__ row, int e,
     out[k] = y0;
     out[2 + k] = y1;
   }
-  *reinterpret_cast<u32x4*>(row + 16 * (e + (g & 1)) + 8 * (g >> 1)) = out;
+  u32x4* p = reinterpret_cast<u32x4*>(row + 16 * (e + (g & 1)) + 8 * (g >> 1));
+  if constexpr (NTS)
+    __builtin_nontemporal_store(out, p);
+  else
+    *p = out;
 }
 
 // ---- whole 128-byte row pieces from output tiles -----------------------------------

@@ -84,8 +84,8 @@ __global__ __launch_bounds__(256) void build_A_kernel(BlocksArgs a, float* __res
   else
     gram_f32<NT, DK>(reinterpret_cast<const float*>(a.K) + (size_t)blk * C * DK, S);
   gram_to_A<NT>(S, gt, -1, AD, AT);
-  if constexpr (NT == 4)
-    store_T_rows_f32<3>(A_out + (size_t)blk * C * C, AT);
+  if constexpr (NT >= 2)
+    store_T_rows_f32<NT, NT - 1>(A_out + (size_t)blk * C * C, AT);
   else
     store_T_f32<NT>(A_out + (size_t)blk * C * C, AT);
 }
@@ -128,13 +128,13 @@ __device__ __forceinline__ void inverse_block(const BlocksArgs& a, int64_t blk, 
     static_assert(NT == 4, "row packs of 64 x 64 blocks");
     store_T_packs(reinterpret_cast<bf16x8*>(T_out) + (size_t)blk * T_PACKS * WAVE, TT);
   } else if (t_bf16) {
-    if constexpr (NT == 4)
-      store_T_rows_bf16<MAXD>(reinterpret_cast<__bf16*>(T_out) + (size_t)blk * C * C, TT);
+    if constexpr (NT >= 2)
+      store_T_rows_bf16<NT, MAXD>(reinterpret_cast<__bf16*>(T_out) + (size_t)blk * C * C, TT);
     else
       store_T_bf16<NT, MAXD>(reinterpret_cast<__bf16*>(T_out) + (size_t)blk * C * C, TT);
   } else {
-    if constexpr (NT == 4)
-      store_T_rows_f32<MAXD>(reinterpret_cast<float*>(T_out) + (size_t)blk * C * C, TT);
+    if constexpr (NT >= 2)
+      store_T_rows_f32<NT, MAXD>(reinterpret_cast<float*>(T_out) + (size_t)blk * C * C, TT);
     else
       store_T_f32<NT, MAXD>(reinterpret_cast<float*>(T_out) + (size_t)blk * C * C, TT);
   }

@@ -1182,30 +1182,43 @@ __device__ __forceinline__ void store_T_bf16(__bf16* __restrict__ out, const Mat
     }
 }
 
-// ---- T of a 64 x 64 block as whole 128-byte row pieces (store_rows_*) ----------------
+// ---- T of a 32 x 32 or 64 x 64 block as whole 128-byte row pieces ------------------
 // Tiles beyond MAXD tile-diagonals and above the diagonal are zero.
-template <int MAXD>
-__device__ __forceinline__ f32x4 tile_kept(const Mat<4>& M, int I, int J) {
+template <int NT, int MAXD>
+__device__ __forceinline__ f32x4 tile_kept(const Mat<NT>& M, int I, int J) {
   return (J <= I && I - J <= MAXD) ? M.t[I][J] : zero4();
 }
 
-template <int MAXD>
-__device__ __forceinline__ void store_T_rows_f32(float* __restrict__ out, const Mat<4>& M) {
+// fp32: tile pairs through store_rows_f32x2 (a pair is 128 bytes of a row)
+template <int NT, int MAXD>
+__device__ __forceinline__ void store_T_rows_f32(float* __restrict__ out, const Mat<NT>& M) {
+  static_assert(NT == 2 || NT == 4, "32 x 32 or 64 x 64 blocks");
+  constexpr int C = 16 * NT;
 #pragma unroll
-  for (int I = 0; I < 4; ++I)
+  for (int I = 0; I < NT; ++I)
 #pragma unroll
-    for (int J = 0; J < 4; J += 2)
-      store_rows_f32x2<true>(out + (size_t)16 * I * 64 + 16 * J, 64, tile_kept<MAXD>(M, I, J),
-                             tile_kept<MAXD>(M, I, J + 1));
+    for (int J = 0; J < NT; J += 2)
+      store_rows_f32x2<true>(out + (size_t)16 * I * C + 16 * J, C, tile_kept<NT, MAXD>(M, I, J),
+                             tile_kept<NT, MAXD>(M, I, J + 1));
 }
 
-template <int MAXD>
-__device__ __forceinline__ void store_T_rows_bf16(__bf16* __restrict__ out, const Mat<4>& M) {
+// bf16: at C = 64 four tiles through store_rows_bf16x4; at C = 32 a row is 64 bytes and
+// one tile pair through store_pair_bf16 writes 16 contiguous rows
+template <int NT, int MAXD>
+__device__ __forceinline__ void store_T_rows_bf16(__bf16* __restrict__ out, const Mat<NT>& M) {
+  static_assert(NT == 2 || NT == 4, "32 x 32 or 64 x 64 blocks");
+  constexpr int C = 16 * NT;
+  const int c = lane_id() & 15;
 #pragma unroll
-  for (int I = 0; I < 4; ++I) {
-    const f32x4 t[4] = {tile_kept<MAXD>(M, I, 0), tile_kept<MAXD>(M, I, 1), tile_kept<MAXD>(M, I, 2),
-                        tile_kept<MAXD>(M, I, 3)};
-    store_rows_bf16x4<true>(out + (size_t)16 * I * 64, 64, t);
+  for (int I = 0; I < NT; ++I) {
+    if constexpr (NT == 4) {
+      const f32x4 t[4] = {tile_kept<NT, MAXD>(M, I, 0), tile_kept<NT, MAXD>(M, I, 1),
+                          tile_kept<NT, MAXD>(M, I, 2), tile_kept<NT, MAXD>(M, I, 3)};
+      store_rows_bf16x4<true>(out + (size_t)16 * I * C, C, t);
+    } else {
+      store_pair_bf16<true>(out + (size_t)(16 * I + c) * C, 0, tile_kept<NT, MAXD>(M, I, 0),
+                            tile_kept<NT, MAXD>(M, I, 1));
+    }
   }
 }
 
