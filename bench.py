@@ -368,8 +368,8 @@ def replay_launches(torch, launch, n_sets, n):
     del graph
 
 
-PROFILE_LEGS = ("c1", "c1_exact", "c1_fs", "c3", "c3_products", "c4", "c2_C64", "c2_C128", "c2_C256",
-                "c2_C256_exact", "decode")
+PROFILE_LEGS = ("c1", "c1_exact", "c1_fs", "c3", "c3_products", "c4", "c4_products", "c2_C64", "c2_C128",
+                "c2_C256", "c2_C256_exact", "decode")
 
 
 def profile_leg(torch, tri, synth, key, n):
@@ -380,7 +380,8 @@ def profile_leg(torch, tri, synth, key, n):
                            N=3 masked (T fp32), exact doubling (T bf16), forward substitution
       c3, c3_products      prefill forward B=4 H=16 seq 8192: the band path; the Horner
                            products (pre-pass + scan)
-      c4                   the same at seq 32768 with the fp8 inverse (N=3 masked)
+      c4, c4_products      the same at seq 32768 with the fp8 inverse (N=3 masked): the
+                           band pre-pass + scan; the Horner products (pre-pass + scan)
       c2_C64 .. c2_C256    WY products (A build + N=3 masked inverse + W, U) at B=2 H=16
                            seq 16384; c2_C256_exact: exact doubling at C=256
       decode               one decode step for 64 sequences (B=64 H=32)"""
@@ -402,14 +403,14 @@ def profile_leg(torch, tri, synth, key, n):
                 tri.gdn_tri_inverse_neumann(K=x["K"], beta=x["beta"], g=x["g"], C=C, N=3, mask=True,
                                             compute="bf16", out=outs[i])
         n_sets = N_SETS
-    elif key in ("c3", "c3_products", "c4"):
-        cfg = C4 if key == "c4" else C3
+    elif key in ("c3", "c3_products", "c4", "c4_products"):
+        cfg = C4 if key.startswith("c4") else C3
         x = {k: v.cuda() for k, v in synth.prefill(3, cfg["B"], cfg["H"], cfg["T"], cfg["d_k"],
                                                     cfg["d_v"]).items()}
         O = torch.empty((cfg["B"], cfg["H"], cfg["T"], cfg["d_v"]), device="cuda", dtype=torch.bfloat16)
         S = torch.empty((cfg["B"], cfg["H"], cfg["d_k"], cfg["d_v"]), device="cuda")
-        mode = "neumann_products" if key == "c3_products" else "neumann"
-        compute = "fp8" if key == "c4" else "bf16"
+        mode = "neumann_products" if key.endswith("_products") else "neumann"
+        compute = "fp8" if key.startswith("c4") else "bf16"
         need = tri.gdn_chunk_fwd_workspace_bytes(cfg["B"], cfg["H"], cfg["T"], cfg["d_k"], cfg["d_v"], 64,
                                                  mode, 3, True, compute)
         ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
@@ -704,7 +705,8 @@ def main():
         out["wy"] = bench_wy(torch, tri, synth, max(5, args.steps // 5), 2)
     if args.only in ("all", "c4"):
         out["chunk_fwd_fp8"] = bench_chunk(torch, tri, synth, C4,
-                                           [("neumann", 3, True, "fp8"), ("neumann", 3, False, "fp8")],
+                                           [("neumann", 3, True, "fp8"), ("neumann_products", 3, True, "fp8"),
+                                            ("neumann", 3, False, "fp8")],
                                            3, 1, n_sets=1, stats=True)
     if not args.no_cpu:
         out["cpu_baseline"], out["accuracy"] = cpu_baseline_and_accuracy(torch, tri, synth)

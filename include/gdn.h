@@ -192,10 +192,11 @@ gdn_status gdn_wy(const gdn_blocks* in, const void* T, int32_t t_dtype,
 
 /* Device workspace, in bytes, that gdn_chunk_fwd needs for these arguments.  The
  * band-masked truncated sum with N <= 3 on bf16 operands forms T inside the scan and
- * needs none (0).  Every other inverse variant forms T - I of all B*H*T/C chunks in a
- * batched pre-pass and hands it to the scan through the workspace: 6144 bytes per
- * chunk at C = 64.  Returns 0 as well for arguments gdn_chunk_fwd rejects (it then
- * reports why).  No HIP call is made. */
+ * needs none (0).  The same sum on fp8 operands (GDN_INV_NEUMANN) forms the band of
+ * T - I of all B*H*T/C chunks in a pre-pass: 512 bytes per chunk at C = 64.  Every other
+ * inverse variant (GDN_INV_NEUMANN_PRODUCTS included) forms T - I of all chunks in a
+ * batched pre-pass of MFMA products: 6144 bytes per chunk at C = 64.  Returns 0 as well
+ * for arguments gdn_chunk_fwd rejects (it then reports why).  No HIP call is made. */
 size_t gdn_chunk_fwd_workspace_bytes(int32_t B, int32_t H, int64_t T, int32_t d_k, int32_t d_v,
                                      int32_t C, const gdn_inverse_cfg* inv);
 
@@ -226,8 +227,9 @@ gdn_status gdn_chunk_fwd(const void* Q, const void* K, const void* V, int32_t qk
  * allocation.  The workspace the variant needs (gdn_chunk_fwd_workspace_bytes) comes
  * from a fixed device array inside the library, GDN_NOALLOC_SCRATCH_BYTES per GPU,
  * held from library load until the process ends; a call needing more returns
- * GDN_ERR_WORKSPACE before enqueuing anything (64 MiB covers 10922 chunks of 64, e.g.
- * B*H = 64 heads of 8192 tokens).  The call allocates nothing.  Every call on one GPU
+ * GDN_ERR_WORKSPACE before enqueuing anything (64 MiB covers 10922 chunks of 64 for
+ * the MFMA pre-pass, e.g. B*H = 64 heads of 8192 tokens, and 131072 chunks for the fp8
+ * band pre-pass).  The call allocates nothing.  Every call on one GPU
  * shares that GPU's array: calls that overlap on one GPU (concurrent streams or
  * threads) race on it and must be serialised by the caller.  Arguments, results and
  * errors otherwise as gdn_chunk_fwd (GDN_ERR_HIP if the array's device address

@@ -198,9 +198,10 @@ def _inv(mode=tri.GDN_INV_NEUMANN, N=3, mask=1, compute=tri.GDN_BF16):
 
 
 def test_chunk_fwd_workspace_query():
-    """The band path (N <= 3, masked, bf16 products) needs no workspace; every other
-    variant needs 6144 bytes per chunk for the pre-pass's T - I packs; arguments the
-    call would reject query as 0."""
+    """The band path (N <= 3, masked, bf16) needs no workspace; the masked fp8 chain with
+    N <= 3 needs 512 bytes per chunk for its band pre-pass's rows; every other variant
+    needs 6144 bytes per chunk for the pre-pass's T - I packs; arguments the call would
+    reject query as 0."""
     q = lambda inv, B=4, H=16, T=8192, dk=128, dv=128, C=64: lib.gdn_chunk_fwd_workspace_bytes(
         B, H, T, dk, dv, C, ctypes.byref(inv) if inv is not None else None)
     chunks = 4 * 16 * 8192 // 64
@@ -209,7 +210,10 @@ def test_chunk_fwd_workspace_query():
     assert q(_inv(N=4)) == chunks * 6144
     assert q(_inv(mask=0)) == chunks * 6144
     assert q(_inv(mode=tri.GDN_INV_EXACT)) == chunks * 6144
-    assert q(_inv(compute=tri.GDN_FP8_E4M3)) == chunks * 6144
+    assert q(_inv(compute=tri.GDN_FP8_E4M3)) == chunks * 512       # the e4m3 chain in band form
+    assert q(_inv(N=2, compute=tri.GDN_FP8_E4M3)) == chunks * 512
+    assert q(_inv(N=4, compute=tri.GDN_FP8_E4M3)) == chunks * 6144
+    assert q(_inv(mask=0, compute=tri.GDN_FP8_E4M3)) == chunks * 6144
     assert q(_inv(mode=tri.GDN_INV_NEUMANN_PRODUCTS)) == chunks * 6144   # Horner products asked for
     assert q(_inv(mode=tri.GDN_INV_NEUMANN_PRODUCTS, compute=tri.GDN_FP8_E4M3)) == chunks * 6144
     assert q(_inv(mode=3)) == 0
@@ -241,6 +245,7 @@ def test_chunk_fwd_validation():
     assert cf(unmasked) == 6
     assert cf(unmasked, ws=FAKE, ws_bytes=need - 1) == 6
     assert cf(unmasked, ws=FAKE + 8, ws_bytes=need) == 4
+    assert cf(_inv(mask=0, compute=tri.GDN_FP8_E4M3)) == 6
     assert cf(_inv(compute=tri.GDN_FP8_E4M3)) == 6
     # empty problems enqueue nothing and need no workspace
     assert cf(unmasked, B=0) == 0

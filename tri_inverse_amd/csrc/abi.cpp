@@ -274,7 +274,10 @@ static gdn_status check_chunk_args(int32_t qkv_dtype, int32_t o_dtype, int32_t B
 static size_t chunk_workspace(int32_t B, int32_t H, int64_t T, int32_t C, const gdn_inverse_cfg* inv) {
   if (inv->mode == GDN_INV_NEUMANN && gdn::chunk_fwd_band_path(inv->mode, inv->N, inv->mask, inv->compute))
     return 0;
-  return (size_t)B * (size_t)H * (size_t)(T / C) * gdn::T_PACK_BYTES;
+  const size_t chunks = (size_t)B * (size_t)H * (size_t)(T / C);
+  if (inv->mode == GDN_INV_NEUMANN && gdn::chunk_fwd_fp8_band(inv->mode, inv->N, inv->mask, inv->compute))
+    return chunks * gdn::BAND_ROW_BYTES;
+  return chunks * gdn::T_PACK_BYTES;
 }
 
 size_t gdn_chunk_fwd_workspace_bytes(int32_t B, int32_t H, int64_t T, int32_t d_k, int32_t d_v,
@@ -345,6 +348,9 @@ gdn_status chunk_fwd_impl(const void* Q, const void* K, const void* V, int32_t q
   auto* st64 = reinterpret_cast<unsigned long long*>(stats);
   const bool empty = (int64_t)B * H == 0 || T == 0;
   const size_t need = empty ? 0 : chunk_workspace(B, H, T, C, inv);
+  // the masked fp8 chain with N <= 3: its band pre-pass instead of the row packs
+  const bool fp8_band =
+      inv->mode == GDN_INV_NEUMANN && gdn::chunk_fwd_fp8_band(inv->mode, inv->N, inv->mask, inv->compute);
   if (!empty) {
     if (!Q || !K || !V || !beta || !g || !O || !S_out) return GDN_ERR_NULL_POINTER;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(beta) || !aligned16(g) ||
@@ -381,7 +387,8 @@ gdn_status chunk_fwd_impl(const void* Q, const void* K, const void* V, int32_t q
     ba.g_cumulative = 0;
     const int mode = inv->mode == GDN_INV_EXACT ? 1 : 0;  // the products of either Neumann mode
     const gdn_status pre =
-        launch_result(gdn::launch_T_packs(ba, mode, inv->N, inv->mask, inv->compute, workspace, st64, s));
+        launch_result(fp8_band ? gdn::launch_band_fp8(ba, inv->N, workspace, st64, s)
+                               : gdn::launch_T_packs(ba, mode, inv->N, inv->mask, inv->compute, workspace, st64, s));
     if (pre != GDN_OK) return pre;
   }
   gdn::ChunkLaunch p;
@@ -394,6 +401,7 @@ gdn_status chunk_fwd_impl(const void* Q, const void* K, const void* V, int32_t q
   p.O = O;
   p.S_out = S_out;
   p.packs = need > 0 ? workspace : nullptr;
+  p.band_rows = fp8_band ? 1 : 0;
   p.T = T;
   p.B = B;
   p.H = H;

@@ -66,6 +66,7 @@ struct ChunkArgs {
   void* O;
   float* S_out;
   const bf16x8* packs;  // T - I row packs of every chunk (pre-pass), MODE_LOAD only
+  const bf16x4* band;   // band rows of T - I of every chunk (fp8 band pre-pass), MODE_LOADBAND only
   int64_t T;
   int BH;
   int dv;
@@ -177,16 +178,21 @@ __device__ __forceinline__ void write_gates(float gl, float bl, ChunkGates& GT) 
 }
 
 // ---- T wave -----------------------------------------------------------------------------
-// Band-masked sum with N <= 3: the band of T - I by band3_from_subdiag (lane i = row
-// i).  The Gram entries come from the MFMA diagonal tiles and the last four columns of
-// the tile left of each (T-form, through LDS to the row lanes).  Only the band slots of
-// the row packs are written: the rest of both pack buffers is cleared once before the
-// scan and stays zero.
+// Band-masked sum with N <= 3: the band of T - I by band3_from_subdiag (bf16 operands:
+// the exact band of the masked sum in fp32) or by band3_fp8 (the e4m3 chain), lane i =
+// row i.  The Gram entries come from the MFMA diagonal tiles and the last four columns of
+// the tile left of each (T-form, through LDS to the row lanes); the gate factor is
+// applied as gram_to_A applies it, so A's band is bit for bit the A of the batched
+// inverse (gdn_build_A).  Only the band slots of the row packs are written: the rest of
+// both pack buffers is cleared once before the scan and stays zero.
 constexpr int MODE_BAND = 16;  // chunk-only codes next to the MODE_* values
 // Every other variant (the truncated sum on bf16 or fp8 operands, masked or not, and the
 // exact product) has its T - I formed by the batched pre-pass as the row packs the
 // state step reads; the T wave only streams them into LDS.
 constexpr int MODE_LOAD = 17;
+// The masked fp8 chain with N <= 3: the band pre-pass (band_fp8_kernel) wrote the band of
+// T - I per row; the T wave puts it into the band slots of the row packs.
+constexpr int MODE_LOADBAND = 18;
 
 // row-pack slot (bf16 index into trp) of T - I at row i, column j
 __device__ __forceinline__ int trp_slot(int i, int j) {
@@ -194,35 +200,111 @@ __device__ __forceinline__ int trp_slot(int i, int j) {
   return ((I * 2 + p) * WAVE + 16 * gg + c) * 8 + (j & 3) + 4 * h;
 }
 
+// a_d(l) = A[l][l - d] for d = 1..3 from the Gram band sv[d] = k_l . k_{l-d} and this
+// lane's beta, G, exp(G), exp(-G): (-beta_l exp(G_l)) S exp(-G_{l-d}) when every exp(-G)
+// of the chunk is finite, else -beta_l exp(G_l - G_{l-d}) S (gram_to_A's two forms, in its
+// operation order); zero outside the chunk (l < d) or the band (d > N)
+__device__ __forceinline__ void band_A(const float (&sv)[4], float bl, float Gl, float eg, float eng, bool split,
+                                       int N, float (&ad)[4]) {
+  const int l = lane_id();
+  const float rl = -bl * eg;
+  float Gm = Gl, nm = eng;
+  ad[0] = 0.f;
+#pragma unroll
+  for (int d = 1; d <= 3; ++d) {
+    Gm = lane_shr1(Gm);
+    nm = lane_shr1(nm);
+    const float v = split ? rl * sv[d] * nm : -bl * __expf(Gl - Gm) * sv[d];
+    ad[d] = (l >= d && d <= N) ? v : 0.f;
+  }
+}
+
+// band values t[1..3] of row l into their row-pack slots
+__device__ __forceinline__ void scatter_band(const float (&t)[4], bf16x8 (&trp)[CNT][2][WAVE]) {
+  const int l = lane_id();
+  __bf16* tb = reinterpret_cast<__bf16*>(&trp[0][0][0]);
+#pragma unroll
+  for (int d = 1; d <= 3; ++d)
+    if (l - d >= 0) tb[trp_slot(l, l - d)] = (__bf16)t[d];
+}
+
 template <int DK>
 __device__ __forceinline__ void produce_T_band(const ChunkArgs& a, const ChunkIn<DK>& R,
                                                bf16x8 (&trp)[CNT][2][WAVE], const ChunkGates& GT,
                                                float (&xr)[CH][XR_LD]) {
   const int l = lane_id(), c = l & 15;
-  const float bl = R.beta[l];
   bf16x8 kf[CNT][DK / 32];
 #pragma unroll
   for (int I = 0; I < CNT; ++I)
 #pragma unroll
     for (int p = 0; p < DK / 32; ++p) kf[I][p] = rowfrag_nat<DK>(R, 16 * I + c, p);
-  const float Gl = GT.G[l];  // the gates were formed by the stager
-  float sv[4];
+  // the gates were formed by the stager
+  const bool split = __builtin_amdgcn_readfirstlane(GT.split) != 0;
+  const float bl = R.beta[l], Gl = GT.G[l], eg = GT.eg[l], eng = GT.eng[l];
+  float sv[4], ad[4], tv[4];
   gram_band3<CNT, DK>(kf, xr, sv);
-  // a_d(l) = -beta_l (k_l . k_{l-d}) exp(G_l - G_{l-d}), zero outside the chunk or band
-  float ad[4];
-  ad[0] = 0.f;
-  float Gm = Gl;
-#pragma unroll
-  for (int d = 1; d <= 3; ++d) {
-    Gm = lane_shr1(Gm);
-    ad[d] = (l >= d && d <= a.N) ? -bl * __expf(Gl - Gm) * sv[d] : 0.f;
-  }
-  float tv[4];
+  band_A(sv, bl, Gl, eg, eng, split, a.N, ad);
   band3_from_subdiag(ad, a.N, tv);
-  __bf16* tb = reinterpret_cast<__bf16*>(&trp[0][0][0]);
+  scatter_band(tv, trp);
+}
+
+// ---- the masked fp8 chain (N <= 3) of every chunk, ahead of the scan ------------------
+// [GEO] "Adaptation a la Quantification" with the mask: band3_fp8 on A's band, formed as
+// produce_T_band forms it (and so bit for bit the A of gdn_build_A).  One wave per chunk
+// writes (T - I)[i][i - d] of row i as bf16 in slots d = 1..3 of 8 bytes (slot 0 zero),
+// 512 bytes per chunk; the scan's T wave puts them into its row packs.  The chain's
+// serial scale reductions and divisions would otherwise sit in the scan's T wave, which
+// then sets the scan's pace.
+template <int DK>
+__global__ __launch_bounds__(256) void band_fp8_kernel(const __bf16* __restrict__ K, const float* __restrict__ beta,
+                                                       const float* __restrict__ g, int64_t n_chunks, int N,
+                                                       bf16x4* __restrict__ out, unsigned long long* stats) {
+  __shared__ float xr[4][CH][XR_LD];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+  const int64_t ch = (int64_t)blockIdx.x * 4 + wave;
+  if (ch >= n_chunks) return;
+  const int l = lane_id(), gq = l >> 4, c = l & 15;
+  const float gl = g[ch * CH + l], bl = beta[ch * CH + l];
+  const __bf16* kb = K + ch * CH * DK;
+  bf16x8 kf[CNT][DK / 32];
 #pragma unroll
-  for (int d = 1; d <= 3; ++d)
-    if (l - d >= 0) tb[trp_slot(l, l - d)] = (__bf16)tv[d];
+  for (int I = 0; I < CNT; ++I)
+#pragma unroll
+    for (int p = 0; p < DK / 32; ++p)
+      kf[I][p] = __builtin_nontemporal_load(
+          reinterpret_cast<const bf16x8*>(kb + (size_t)(16 * I + c) * DK + 32 * p + 8 * gq));
+  // the gate factors as the stager (and gdn_build_A) forms them
+  const float Gl = wave_inclusive_scan(gl);
+  const bool split = wave_min(Gl) >= -80.f;
+  const float eg = __expf(Gl), eng = __expf(-Gl);
+  float sv[4], ad[4], tv[4];
+  gram_band3<CNT, DK>(kf, xr[wave], sv);
+  band_A(sv, bl, Gl, eg, eng, split, N, ad);
+  Fp8Counts cnt{0, 0, 0, 0};
+  const bool count = stats != nullptr;
+  band3_fp8(ad, N, tv, cnt, count);
+  bf16x4 o;
+  o[0] = (__bf16)0.f;
+  o[1] = (__bf16)tv[1];
+  o[2] = (__bf16)tv[2];
+  o[3] = (__bf16)tv[3];
+  out[ch * CH + l] = o;
+  if (count) flush_counts(cnt, stats);
+}
+
+int launch_band_fp8(const BlocksArgs& a, int N, void* out, unsigned long long* stats, hipStream_t s) {
+  if (a.C != CH || a.g_cumulative) return -1;
+  const dim3 grid((unsigned)((a.n_blocks + 3) / 4)), block(4 * WAVE);
+  auto go = [&](auto dk) {
+    hipLaunchKernelGGL((band_fp8_kernel<dk.value>), grid, block, 0, s, reinterpret_cast<const __bf16*>(a.K),
+                       a.beta, a.g, a.n_blocks, N, reinterpret_cast<bf16x4*>(out), stats);
+    return 0;
+  };
+  switch (a.d_k) {
+    case 64: return go(std::integral_constant<int, 64>{});
+    case 128: return go(std::integral_constant<int, 128>{});
+    default: return -1;
+  }
 }
 
 // ---- waves 0, 1: the state scan -------------------------------------------------------
@@ -617,6 +699,34 @@ __global__ __launch_bounds__(NWAVES * WAVE, 1) void chunk_fwd_kernel(ChunkArgs a
         if (ch < nchunks) produce_T_band<DK>(a, ring(in, ch & 3), ring(buf, ch & 1).trp, ring(gr, ch & 3), xr);
         lds_barrier();
       }
+    } else if constexpr (MODE == MODE_LOADBAND) {
+      // the band pre-pass's rows of chunk ch sit at band[(bh * nchunks + ch) * 64]; loaded one
+      // iteration earlier (register ping-pong, chunk index clamped) and put into the band
+      // slots of the row packs, whose other slots were cleared once
+      const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int I = 0; I < CNT; ++I)
+#pragma unroll
+          for (int p = 0; p < 2; ++p) buf[b].trp[I][p][l] = z;
+      const bf16x4* hb = a.band + (size_t)bh * nchunks * CH + l;
+      auto clampc = [&](int ch) { return ch < last ? ch : last; };
+      auto put = [&](const bf16x4& r, bf16x8 (&trp)[CNT][2][WAVE]) {
+        const float t[4] = {0.f, (float)r[1], (float)r[2], (float)r[3]};
+        scatter_band(t, trp);
+      };
+      bf16x4 r0 = hb[0], r1;
+      lds_barrier();
+      for (int it = -1; it <= nchunks; it += 2) {
+        r1 = hb[(size_t)clampc(it + 2) * CH];
+        if (it + 1 < nchunks) put(r0, ring(buf, (it + 1) & 1).trp);
+        lds_barrier();
+        if (it + 1 > nchunks) break;
+        r0 = hb[(size_t)clampc(it + 3) * CH];
+        if (it + 2 < nchunks) put(r1, ring(buf, (it + 2) & 1).trp);
+        lds_barrier();
+      }
     } else {
       // the pre-pass's packs of chunk ch sit at packs[(bh * nchunks + ch) * 6 * 64]; chunk
       // it + 1 goes to LDS in iteration it, loaded one iteration earlier (register
@@ -732,6 +842,10 @@ bool chunk_fwd_band_path(int mode, int N, int mask, int cmp) {
   return mode == MODE_NEUMANN && mask && N <= 3 && cmp == CMP_BF16;
 }
 
+bool chunk_fwd_fp8_band(int mode, int N, int mask, int cmp) {
+  return mode == MODE_NEUMANN && mask && N <= 3 && cmp == CMP_FP8;
+}
+
 int launch_chunk_fwd(const ChunkLaunch& p, hipStream_t s) {
   ChunkArgs a;
   a.Q = reinterpret_cast<const __bf16*>(p.Q);
@@ -742,7 +856,8 @@ int launch_chunk_fwd(const ChunkLaunch& p, hipStream_t s) {
   a.S0 = p.S0;
   a.O = p.O;
   a.S_out = p.S_out;
-  a.packs = reinterpret_cast<const bf16x8*>(p.packs);
+  a.packs = p.band_rows ? nullptr : reinterpret_cast<const bf16x8*>(p.packs);
+  a.band = p.band_rows ? reinterpret_cast<const bf16x4*>(p.packs) : nullptr;
   a.T = p.T;
   a.BH = p.B * p.H;
   a.dv = p.d_v;
@@ -770,8 +885,10 @@ int launch_chunk_fwd(const ChunkLaunch& p, hipStream_t s) {
   using I3 = std::integral_constant<int, 3>;
   using MB = std::integral_constant<int, MODE_BAND>;
   using ML = std::integral_constant<int, MODE_LOAD>;
+  using MLB = std::integral_constant<int, MODE_LOADBAND>;
   auto with_dk = [&](auto dk) -> int {
     if (band) return go(dk, MB{}, I1{});
+    if (p.band_rows) return go(dk, MLB{}, I1{});
     return narrow ? go(dk, ML{}, I1{}) : go(dk, ML{}, I3{});
   };
   switch (p.d_k) {

@@ -69,7 +69,9 @@ struct ChunkLaunch {
   const float* S0;
   void* O;
   float* S_out;
-  const void* packs;  // T - I row packs from the pre-pass (NULL on the band path)
+  const void* packs;  // T - I from the pre-pass (NULL on the band path): row packs, or
+                      // with band_rows the fp8 band pre-pass's rows
+  int band_rows;
   int64_t T;
   int B, H, d_k, d_v;
   int o_bf16;
@@ -77,9 +79,15 @@ struct ChunkLaunch {
   float scale;
 };
 // chunk-wise forward, C = 64; d_k in {64, 128}; d_v a multiple of 32.  The band path
-// (Neumann, mask, N <= 3, bf16) forms T - I itself; every other variant reads the row
-// packs the pre-pass wrote (p.packs).
+// (Neumann, mask, N <= 3, bf16) forms T - I itself; the masked fp8 chain with N <= 3 reads
+// the band rows of launch_band_fp8 (p.packs, p.band_rows); every other variant reads the
+// row packs of launch_T_packs (p.packs).
 bool chunk_fwd_band_path(int mode, int N, int mask, int cmp);
+bool chunk_fwd_fp8_band(int mode, int N, int mask, int cmp);
+// the band of T - I of every 64-row chunk for the masked fp8 chain, N <= 3 (bf16 keys,
+// d_k 64 or 128, raw log-gates): 64 rows x 8 bytes per chunk; stats: its counters (or NULL)
+int launch_band_fp8(const BlocksArgs& a, int N, void* out, unsigned long long* stats, hipStream_t s);
+constexpr size_t BAND_ROW_BYTES = 64 * 8;
 int launch_chunk_fwd(const ChunkLaunch& p, hipStream_t s);
 }  // namespace gdn
 

@@ -59,17 +59,6 @@ struct BlockIn<NT, SRC_A, DK> {
   }
 };
 
-__device__ __forceinline__ void flush_counts(Fp8Counts& cnt, unsigned long long* stats) {
-  uint32_t v0 = wave_sum_u32(cnt.nonfinite), v1 = wave_sum_u32(cnt.sat_dyn);
-  uint32_t v2 = wave_sum_u32(cnt.sat_static), v3 = wave_sum_u32(cnt.underflow);
-  if (lane_id() == 0) {
-    if (v0) atomicAdd(stats + 0, (unsigned long long)v0);
-    if (v1) atomicAdd(stats + 1, (unsigned long long)v1);
-    if (v2) atomicAdd(stats + 2, (unsigned long long)v2);
-    if (v3) atomicAdd(stats + 3, (unsigned long long)v3);
-  }
-}
-
 // A alone (gdn_build_A): one block per wave, fp32 or bf16 keys.
 template <int NT, int SRC, int DK>
 __global__ __launch_bounds__(256) void build_A_kernel(BlocksArgs a, float* __restrict__ A_out) {

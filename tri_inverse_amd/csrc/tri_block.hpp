@@ -521,25 +521,38 @@ __device__ __forceinline__ long quant8(const f32x4& lo, const f32x4& hi, float i
 // count diagnostics of quantising the lower tiles of M (those within MAXD tile-diagonals
 // of the main one; the rest are zero and count nothing) under the reciprocal scales
 // inv_s (dynamic) and inv_st (static), per lane, element by element
+__device__ __forceinline__ void fp8_count1(float x, float inv_s, float inv_st, Fp8Counts& cnt) {
+  constexpr float UNDER = 0.0009765625f;  // 2^-10: half the smallest e4m3 subnormal
+  const float a = fabsf(x);
+  const bool fin = __builtin_isfinite(x);
+  cnt.nonfinite += fin ? 0u : 1u;
+  cnt.sat_dyn += (fin && a * inv_s >= FP8_SAT) ? 1u : 0u;
+  cnt.sat_static += (fin && a * inv_st >= FP8_SAT) ? 1u : 0u;
+  cnt.underflow += (fin && x != 0.f && a * inv_s <= UNDER) ? 1u : 0u;
+}
+
 template <int NT, int MAXD>
 __device__ __forceinline__ void fp8_count(const Mat<NT>& M, float inv_s, float inv_st, Fp8Counts& cnt) {
-  constexpr float UNDER = 0.0009765625f;  // 2^-10: half the smallest e4m3 subnormal
 #pragma unroll
   for (int I = 0; I < NT; ++I)
 #pragma unroll
     for (int J = 0; J <= I; ++J) {
       if (I - J > MAXD) continue;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float x = M.t[I][J][r];
-        const float a = fabsf(x);
-        const bool fin = __builtin_isfinite(x);
-        cnt.nonfinite += fin ? 0u : 1u;
-        cnt.sat_dyn += (fin && a * inv_s >= FP8_SAT) ? 1u : 0u;
-        cnt.sat_static += (fin && a * inv_st >= FP8_SAT) ? 1u : 0u;
-        cnt.underflow += (fin && x != 0.f && a * inv_s <= UNDER) ? 1u : 0u;
-      }
+      for (int r = 0; r < 4; ++r) fp8_count1(M.t[I][J][r], inv_s, inv_st, cnt);
     }
+}
+
+// the wave's counters added to stats[0..3] (one atomic per counter and wave)
+__device__ __forceinline__ void flush_counts(const Fp8Counts& cnt, unsigned long long* stats) {
+  const uint32_t v0 = wave_sum_u32(cnt.nonfinite), v1 = wave_sum_u32(cnt.sat_dyn);
+  const uint32_t v2 = wave_sum_u32(cnt.sat_static), v3 = wave_sum_u32(cnt.underflow);
+  if (lane_id() == 0) {
+    if (v0) atomicAdd(stats + 0, (unsigned long long)v0);
+    if (v1) atomicAdd(stats + 1, (unsigned long long)v1);
+    if (v2) atomicAdd(stats + 2, (unsigned long long)v2);
+    if (v3) atomicAdd(stats + 3, (unsigned long long)v3);
+  }
 }
 
 // block absmax of the lower tiles within MAXD tile-diagonals (a NaN never becomes the
@@ -620,6 +633,81 @@ __device__ __forceinline__ void fp8_roundtrip(Mat<NT>& M, float s) {
       M.t[I][J][2] = fp8_to_f32<2>(w) * s;
       M.t[I][J][3] = fp8_to_f32<3>(w) * s;
     }
+}
+
+// ---- the masked fp8 chain for N <= 3 in band form (lane i = row i of a 64-row block) --
+// [GEO] "Adaptation a la Quantification" with the band mask of Methodologie SS2.  With the
+// mask, A and every X_k live on sub-diagonals 1..N, so the chain of neumann_T_fp8 needs
+// only x_d(i) = X[i][i - d], d <= 3: the same scales (absmax / 448 over the block, here a
+// wave reduction), the same e4m3 codes and counters, and X_{k+1} = A' + s_A s_X (q(A) q(X_k))
+// with
+//   (q(A) q(X))[i][i-1] = 0,
+//   (q(A) q(X))[i][i-2] = qa_1(i) qx_1(i-1),
+//   (q(A) q(X))[i][i-3] = qa_1(i) qx_2(i-1) + qa_2(i) qx_1(i-2).
+// A product of two e4m3 values is exact in fp32, so one fused multiply-add over the exact
+// second product rounds the exact sum once: the oracle's arithmetic, bit for bit.
+
+// e4m3 code values (as fp32 numbers, before scaling back) of x1..x3 under the reciprocal
+// scale inv: clamp to +-448, then the hardware's round-to-nearest-even conversion
+__device__ __forceinline__ void fp8_code3(float x1, float x2, float x3, float inv, float& q1, float& q2,
+                                          float& q3) {
+  const float y1 = fminf(fmaxf(x1 * inv, -FP8_MAX), FP8_MAX);
+  const float y2 = fminf(fmaxf(x2 * inv, -FP8_MAX), FP8_MAX);
+  const float y3 = fminf(fmaxf(x3 * inv, -FP8_MAX), FP8_MAX);
+  const uint32_t w = cvt_fp8x2<true>(y3, 0.f, cvt_fp8x2<false>(y1, y2, 0u));
+  q1 = fp8_to_f32<0>(w);
+  q2 = fp8_to_f32<1>(w);
+  q3 = fp8_to_f32<2>(w);
+}
+
+// the scale absmax / 448 of a band tensor (x1..x3 on every lane) and, when count is set,
+// its four counters under that scale and under s_static (<= 0: its own)
+__device__ __forceinline__ float band_scale_count(float x1, float x2, float x3, float s_static, Fp8Counts& cnt,
+                                                  bool count) {
+  const float s = fp8_scale(wave_max(fmaxf(fmaxf(fabsf(x1), fabsf(x2)), fabsf(x3))));
+  if (count) {
+    const float inv_s = 1.f / s, inv_st = 1.f / (s_static > 0.f ? s_static : s);
+    fp8_count1(x1, inv_s, inv_st, cnt);
+    fp8_count1(x2, inv_s, inv_st, cnt);
+    fp8_count1(x3, inv_s, inv_st, cnt);
+  }
+  return s;
+}
+
+// ad[d] = A[i][i - d] for d = 1..3 (zero where i - d < 0 or d > N), 1 <= N <= 3 ->
+// t[d] = (T - I)[i][i - d]
+__device__ __forceinline__ void band3_fp8(const float (&ad)[4], int N, float (&t)[4], Fp8Counts& cnt, bool count) {
+  const float sA = band_scale_count(ad[1], ad[2], ad[3], 0.f, cnt, count);
+  float qa1, qa2, qa3;
+  fp8_code3(ad[1], ad[2], ad[3], 1.f / sA, qa1, qa2, qa3);
+  const float ap1 = qa1 * sA, ap2 = qa2 * sA, ap3 = qa3 * sA;  // A' = s_A q(A)
+  float x1 = ap1, x2 = ap2, x3 = ap3;                            // X_1 = A'
+  for (int k = 1; k < N; ++k) {
+    const float sX = band_scale_count(x1, x2, x3, sA, cnt, count);
+    const float sxy = sA * sX;
+    float qx1, qx2, qx3;
+    fp8_code3(x1, x2, x3, 1.f / sX, qx1, qx2, qx3);
+    const float qx1m1 = lane_shr1(qx1), qx1m2 = lane_shr1(qx1m1), qx2m1 = lane_shr1(qx2);
+    const float p2 = qa1 * qx1m1;
+    const float p3 = __builtin_fmaf(qa2, qx1m2, qa1 * qx2m1);
+    x1 = __builtin_fmaf(0.f, sxy, ap1);
+    x2 = __builtin_fmaf(p2, sxy, ap2);
+    x3 = N >= 3 ? __builtin_fmaf(p3, sxy, ap3) : 0.f;
+  }
+  // T - I = s_T q(X_N), or A' itself for N = 1
+  float t1 = ap1, t2 = 0.f, t3 = 0.f;
+  if (N >= 2) {
+    const float sT = band_scale_count(x1, x2, x3, sA, cnt, count);
+    float q1, q2, q3;
+    fp8_code3(x1, x2, x3, 1.f / sT, q1, q2, q3);
+    t1 = q1 * sT;
+    t2 = q2 * sT;
+    t3 = q3 * sT;
+  }
+  t[0] = 0.f;
+  t[1] = t1;
+  t[2] = t2;
+  t[3] = t3;
 }
 
 // ---- int8 variant: per-block power-of-two scales, int32 accumulation ----------
