@@ -178,13 +178,11 @@ __device__ __forceinline__ void write_gates(float gl, float bl, ChunkGates& GT) 
 }
 
 // ---- T wave -----------------------------------------------------------------------------
-// Band-masked sum with N <= 3: the band of T - I by band3_from_subdiag (bf16 operands:
-// the exact band of the masked sum in fp32) or by band3_fp8 (the e4m3 chain), lane i =
-// row i.  The Gram entries come from the MFMA diagonal tiles and the last four columns of
-// the tile left of each (T-form, through LDS to the row lanes); the gate factor is
-// applied as gram_to_A applies it, so A's band is bit for bit the A of the batched
-// inverse (gdn_build_A).  Only the band slots of the row packs are written: the rest of
-// both pack buffers is cleared once before the scan and stays zero.
+// Band-masked sum with N <= 3: the band of T - I by band3_from_subdiag (lane i = row i).
+// The Gram entries come from the MFMA diagonal tiles and the last four columns of the
+// tile left of each (T-form, through LDS to the row lanes).  Only the band slots of the
+// row packs are written: the rest of both pack buffers is cleared once before the scan
+// and stays zero.
 constexpr int MODE_BAND = 16;  // chunk-only codes next to the MODE_* values
 // Every other variant (the truncated sum on bf16 or fp8 operands, masked or not, and the
 // exact product) has its T - I formed by the batched pre-pass as the row packs the
@@ -204,18 +202,26 @@ __device__ __forceinline__ int trp_slot(int i, int j) {
 // lane's beta, G, exp(G), exp(-G): (-beta_l exp(G_l)) S exp(-G_{l-d}) when every exp(-G)
 // of the chunk is finite, else -beta_l exp(G_l - G_{l-d}) S (gram_to_A's two forms, in its
 // operation order); zero outside the chunk (l < d) or the band (d > N)
+// (split: wave-uniform, so only one form is evaluated)
 __device__ __forceinline__ void band_A(const float (&sv)[4], float bl, float Gl, float eg, float eng, bool split,
                                        int N, float (&ad)[4]) {
   const int l = lane_id();
-  const float rl = -bl * eg;
-  float Gm = Gl, nm = eng;
   ad[0] = 0.f;
+  if (split) {
+    const float rl = -bl * eg;
+    float nm = eng;
 #pragma unroll
-  for (int d = 1; d <= 3; ++d) {
-    Gm = lane_shr1(Gm);
-    nm = lane_shr1(nm);
-    const float v = split ? rl * sv[d] * nm : -bl * __expf(Gl - Gm) * sv[d];
-    ad[d] = (l >= d && d <= N) ? v : 0.f;
+    for (int d = 1; d <= 3; ++d) {
+      nm = lane_shr1(nm);
+      ad[d] = (l >= d && d <= N) ? rl * sv[d] * nm : 0.f;
+    }
+  } else {
+    float Gm = Gl;
+#pragma unroll
+    for (int d = 1; d <= 3; ++d) {
+      Gm = lane_shr1(Gm);
+      ad[d] = (l >= d && d <= N) ? -bl * __expf(Gl - Gm) * sv[d] : 0.f;
+    }
   }
 }
 
@@ -238,19 +244,29 @@ __device__ __forceinline__ void produce_T_band(const ChunkArgs& a, const ChunkIn
   for (int I = 0; I < CNT; ++I)
 #pragma unroll
     for (int p = 0; p < DK / 32; ++p) kf[I][p] = rowfrag_nat<DK>(R, 16 * I + c, p);
-  // the gates were formed by the stager
-  const bool split = __builtin_amdgcn_readfirstlane(GT.split) != 0;
-  const float bl = R.beta[l], Gl = GT.G[l], eg = GT.eg[l], eng = GT.eng[l];
-  float sv[4], ad[4], tv[4];
+  const float bl = R.beta[l];
+  const float Gl = GT.G[l];  // the gates were formed by the stager
+  float sv[4];
   gram_band3<CNT, DK>(kf, xr, sv);
-  band_A(sv, bl, Gl, eg, eng, split, a.N, ad);
+  // a_d(l) = -beta_l (k_l . k_{l-d}) exp(G_l - G_{l-d}), zero outside the chunk or band
+  // (the exponential of the difference: three exponentials per row measured faster here
+  // than band_A's split form, which reads two more gate rows)
+  float ad[4];
+  ad[0] = 0.f;
+  float Gm = Gl;
+#pragma unroll
+  for (int d = 1; d <= 3; ++d) {
+    Gm = lane_shr1(Gm);
+    ad[d] = (l >= d && d <= a.N) ? -bl * __expf(Gl - Gm) * sv[d] : 0.f;
+  }
+  float tv[4];
   band3_from_subdiag(ad, a.N, tv);
   scatter_band(tv, trp);
 }
 
 // ---- the masked fp8 chain (N <= 3) of every chunk, ahead of the scan ------------------
-// [GEO] "Adaptation a la Quantification" with the mask: band3_fp8 on A's band, formed as
-// produce_T_band forms it (and so bit for bit the A of gdn_build_A).  One wave per chunk
+// [GEO] "Adaptation a la Quantification" with the mask: band3_fp8 on A's band, formed by
+// band_A in gram_to_A's gate form and order (so bit for bit the A of gdn_build_A).  One wave per chunk
 // writes (T - I)[i][i - d] of row i as bf16 in slots d = 1..3 of 8 bytes (slot 0 zero),
 // 512 bytes per chunk; the scan's T wave puts them into its row packs.  The chain's
 // serial scale reductions and divisions would otherwise sit in the scan's T wave, which
@@ -266,16 +282,18 @@ __global__ __launch_bounds__(256) void band_fp8_kernel(const __bf16* __restrict_
   const int l = lane_id(), gq = l >> 4, c = l & 15;
   const float gl = g[ch * CH + l], bl = beta[ch * CH + l];
   const __bf16* kb = K + ch * CH * DK;
+  // plain loads: each instruction covers half of 16 rows' 128-byte lines and the next one
+  // the other half; with streaming (non-temporal) loads the lines were fetched twice
+  // (1.37x the key bytes, 131 against 112 us)
   bf16x8 kf[CNT][DK / 32];
 #pragma unroll
   for (int I = 0; I < CNT; ++I)
 #pragma unroll
     for (int p = 0; p < DK / 32; ++p)
-      kf[I][p] = __builtin_nontemporal_load(
-          reinterpret_cast<const bf16x8*>(kb + (size_t)(16 * I + c) * DK + 32 * p + 8 * gq));
+      kf[I][p] = *reinterpret_cast<const bf16x8*>(kb + (size_t)(16 * I + c) * DK + 32 * p + 8 * gq);
   // the gate factors as the stager (and gdn_build_A) forms them
   const float Gl = wave_inclusive_scan(gl);
-  const bool split = wave_min(Gl) >= -80.f;
+  const bool split = __builtin_amdgcn_readfirstlane(wave_min(Gl) >= -80.f ? 1 : 0) != 0;
   const float eg = __expf(Gl), eng = __expf(-Gl);
   float sv[4], ad[4], tv[4];
   gram_band3<CNT, DK>(kf, xr[wave], sv);
