@@ -29,10 +29,15 @@ struct BlockIn<NT, SRC_K_BF16, DK> {
   // Measured faster where the block's work after A is long (exact doubling, quantised
   // chains: 8-10 %; residual correction: 2-3 %) and slower for the light bf16 / fp32
   // truncated sums (3-4 %), which keep the compiler's own order.
-  template <bool GF = false>
+  // STREAM: streaming (non-temporal) key loads.  Each load instruction covers half of
+  // 16 rows' 128-byte lines and the next one the other half; over 8192 and more blocks
+  // (the chunk forward's pre-pass) streaming loads fetched lines twice (1.12-1.15x the
+  // key bytes) and plain loads are faster (bf16 products pre-pass 40 -> 34 us at 8192
+  // blocks), while the 2048-block inverses read exactly their bytes either way.
+  template <bool GF = false, bool STREAM = true>
   __device__ __forceinline__ void load(const BlocksArgs& a, int64_t blk) {
     constexpr int C = 16 * NT;
-    load_kblock<NT, DK, true, GF>(reinterpret_cast<const __bf16*>(a.K) + (size_t)blk * C * DK,
+    load_kblock<NT, DK, STREAM, GF>(reinterpret_cast<const __bf16*>(a.K) + (size_t)blk * C * DK,
                                   a.beta + (size_t)blk * C, a.g + (size_t)blk * C, k);
   }
   template <int MAXD, bool BANDED, bool GF = false>
@@ -48,7 +53,7 @@ struct BlockIn<NT, SRC_K_BF16, DK> {
 template <int NT, int DK>
 struct BlockIn<NT, SRC_A, DK> {
   ABlock<NT> ab;
-  template <bool GF = false>
+  template <bool GF = false, bool STREAM = true>
   __device__ __forceinline__ void load(const BlocksArgs& a, int64_t blk) {
     constexpr int C = 16 * NT;
     load_ablock<NT>(a.A + (size_t)blk * C * C, ab);
@@ -145,7 +150,7 @@ __global__ __launch_bounds__(256) void inverse_kernel(BlocksArgs a, int N, int m
     const int64_t blk = (int64_t)blockIdx.x * (blockDim.x / WAVE) + (threadIdx.x / WAVE);
     if (blk >= a.n_blocks) return;
     BlockIn<NT, SRC, DK> in;
-    in.template load<gates_first<CMP, MODE>()>(a, blk);
+    in.template load<gates_first<CMP, MODE>(), !PK>(a, blk);
     inverse_block<NT, SRC, DK, CMP, MODE, MAXD, PK>(a, blk, in, N, mask, T_out, t_bf16, cnt, count, S,
                                                     threadIdx.x / WAVE);
   } else {
@@ -154,10 +159,10 @@ __global__ __launch_bounds__(256) void inverse_kernel(BlocksArgs a, int N, int m
     if (first >= a.n_blocks) return;
     const int64_t stride = (int64_t)gridDim.x * (blockDim.x / WAVE);
     BlockIn<NT, SRC, DK> in;
-    in.template load<gates_first<CMP, MODE>()>(a, first);
+    in.template load<gates_first<CMP, MODE>(), !PK>(a, first);
     for (int64_t blk = first; blk < a.n_blocks; blk += stride) {
       BlockIn<NT, SRC, DK> nxt;
-      nxt.template load<gates_first<CMP, MODE>()>(a, blk + stride < a.n_blocks ? blk + stride : a.n_blocks - 1);
+      nxt.template load<gates_first<CMP, MODE>(), !PK>(a, blk + stride < a.n_blocks ? blk + stride : a.n_blocks - 1);
       inverse_block<NT, SRC, DK, CMP, MODE, MAXD, PK>(a, blk, in, N, mask, T_out, t_bf16, cnt, count, S, wave);
       in = nxt;
     }
