@@ -300,6 +300,34 @@ def test_chunk_fwd_fp8_inverse():
         assert s[0] == 0 and s[1] == 0
 
 
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 96)])
+@pytest.mark.parametrize("strong", [False, True])
+@pytest.mark.parametrize("mask", [True, False])
+def test_chunk_fwd_fp8_shapes_and_strong_gates(dk, dv, strong, mask):
+    """The fp8 inverse at d_k = 64 and an odd multiple of 32 for d_v, with ordinary gates
+    and with log-gates near -2.6 per token (G below -80 inside every chunk, so every gate
+    factor is the exponential of a difference, in the band pre-pass as well): O and S
+    against the oracle's e4m3 emulation, counters exact."""
+    B, H, T = 1, 3, 320
+    say(f"chunk fwd fp8 dk={dk} dv={dv} strong={strong} mask={mask}")
+    x = synth.prefill(29, B, H, T, dk, dv)
+    if strong:
+        x["g"] = (x["g"] - 2.5).contiguous()
+    x64 = {k: f64(v) for k, v in x.items()}
+    if strong:
+        assert x64["g"][..., :32].sum(axis=-1).max() < -80.0
+    stats = torch.zeros(4, dtype=torch.int64, device="cuda")
+    O, S = _run_chunk(x, C=64, scale=dk ** -0.5, N=3, mask=mask, compute="fp8", stats=stats,
+                      o_dtype=torch.float32)
+    assert np.isfinite(O).all() and np.isfinite(S).all()
+    Oe, Se = oracle.chunk_fwd(x64["Q"], x64["K"], x64["V"], x64["beta"], x64["g"], 64, dk ** -0.5,
+                              inv_mode=oracle.INV_FP8, N=3, mask=mask)
+    assert relF(O, Oe) <= TOL_FP8_EMU, relF(O, Oe)
+    assert relF(S, Se) <= TOL_FP8_EMU, relF(S, Se)
+    s, ref = stats.cpu().tolist(), _fp8_reference_counts(x, mask)
+    assert s == ref, (s, ref)
+
+
 def test_chunk_fwd_full_size_all_heads():
     """B=4, H=16, seq 8192, d_k = d_v = 128 (the prefill workload the bench times):
     every one of the 64 heads is recomputed by the oracle and compared."""
