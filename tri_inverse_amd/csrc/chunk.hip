@@ -27,8 +27,9 @@
 //               and 2 share one SIMD, tiles 1 and 3 another (equal shares of the
 //               triangular P).
 //   wave 5      T - I of the next chunk (beside state wave 1): formed here on the band
-//               path (N <= 3 with the mask, bf16), else streamed from the row packs a
-//               batched pre-pass wrote (every other inverse variant, fp8 included).
+//               path (N <= 3 with the mask, bf16); for the masked fp8 chain with N <= 3
+//               put together from the band rows of the fp8 band pre-pass; else streamed
+//               from the row packs a batched pre-pass wrote (every other variant).
 //   wave 4      copies K rows, V columns, log-gates and beta of the chunk after next
 //               into a 4-deep LDS ring and forms that chunk's gate factors (beside
 //               state wave 0).
