@@ -267,11 +267,11 @@ __device__ __forceinline__ void produce_T_band(const ChunkArgs& a, const ChunkIn
 
 // ---- the masked fp8 chain (N <= 3) of every chunk, ahead of the scan ------------------
 // [GEO] "Adaptation a la Quantification" with the mask: band3_fp8 on A's band, formed by
-// band_A in gram_to_A's gate form and order (so bit for bit the A of gdn_build_A).  One wave per chunk
-// writes (T - I)[i][i - d] of row i as bf16 in slots d = 1..3 of 8 bytes (slot 0 zero),
-// 512 bytes per chunk; the scan's T wave puts them into its row packs.  The chain's
-// serial scale reductions and divisions would otherwise sit in the scan's T wave, which
-// then sets the scan's pace.
+// band_A in gram_to_A's gate form and order (so bit for bit the A of gdn_build_A).  One
+// wave per chunk writes (T - I)[i][i - d] of row i as bf16 in slots d = 1..3 of 8 bytes
+// (slot 0 zero), 512 bytes per chunk; the scan's T wave puts them into its row packs.
+// The chain's serial scale reductions and divisions would otherwise sit in the scan's T
+// wave, which then sets the scan's pace.
 template <int DK>
 __global__ __launch_bounds__(256) void band_fp8_kernel(const __bf16* __restrict__ K, const float* __restrict__ beta,
                                                        const float* __restrict__ g, int64_t n_chunks, int N,
