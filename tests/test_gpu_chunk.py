@@ -260,7 +260,7 @@ def test_chunk_fwd_no_decay_follows_the_bf16_rounding_model(ab_beta, mask):
 TOL_FP8_EMU = 5e-3
 
 
-def _fp8_reference_counts(x, mask):
+def _fp8_reference_counts(x, mask, N=3):
     """The counters the chunk forward must report for the fp8 chain over every chunk of x.
     Masked (N = 3): the band pre-pass runs the chain in band form, whose sums of code
     products are exactly rounded as the oracle's are, on the A of gdn_build_A (the same Gram
@@ -271,10 +271,10 @@ def _fp8_reference_counts(x, mask):
     if mask:
         A = f64(tri.gdn_build_A(K=K, beta=beta, g=g, C=64))
         del K, beta, g
-        _, cnt, _ = oracle.neumann_fp8(A, 3, True)
+        _, cnt, _ = oracle.neumann_fp8(A, N, True)
         return [int(v) for v in cnt.sum(axis=0)]
     stats_inv = torch.zeros(4, dtype=torch.int64, device="cuda")
-    tri.gdn_tri_inverse_neumann(K=K, beta=beta, g=g, C=64, N=3, mask=False, compute="fp8", stats=stats_inv)
+    tri.gdn_tri_inverse_neumann(K=K, beta=beta, g=g, C=64, N=N, mask=False, compute="fp8", stats=stats_inv)
     torch.cuda.synchronize()
     return stats_inv.cpu().tolist()
 
@@ -325,6 +325,27 @@ def test_chunk_fwd_fp8_shapes_and_strong_gates(dk, dv, strong, mask):
     assert relF(O, Oe) <= TOL_FP8_EMU, relF(O, Oe)
     assert relF(S, Se) <= TOL_FP8_EMU, relF(S, Se)
     s, ref = stats.cpu().tolist(), _fp8_reference_counts(x, mask)
+    assert s == ref, (s, ref)
+
+
+@pytest.mark.parametrize("N", [1, 2])
+@pytest.mark.parametrize("mask", [True, False])
+def test_chunk_fwd_fp8_short_chains(N, mask):
+    """N = 1 (T - I = A') and N = 2 on the fp8 inverse: the band pre-pass's shorter chains
+    (masked) and the products pre-pass's (unmasked), against the e4m3 emulation, counters
+    exact."""
+    B, H, T, dk, dv = 1, 2, 256, 128, 64
+    say(f"chunk fwd fp8 N={N} mask={mask}")
+    x = synth.prefill(31, B, H, T, dk, dv)
+    x64 = {k: f64(v) for k, v in x.items()}
+    stats = torch.zeros(4, dtype=torch.int64, device="cuda")
+    O, S = _run_chunk(x, C=64, scale=dk ** -0.5, N=N, mask=mask, compute="fp8", stats=stats,
+                      o_dtype=torch.float32)
+    Oe, Se = oracle.chunk_fwd(x64["Q"], x64["K"], x64["V"], x64["beta"], x64["g"], 64, dk ** -0.5,
+                              inv_mode=oracle.INV_FP8, N=N, mask=mask)
+    assert relF(O, Oe) <= TOL_FP8_EMU, relF(O, Oe)
+    assert relF(S, Se) <= TOL_FP8_EMU, relF(S, Se)
+    s, ref = stats.cpu().tolist(), _fp8_reference_counts(x, mask, N)
     assert s == ref, (s, ref)
 
 
