@@ -15,7 +15,8 @@
 // the 16x16x16 bf16 MFMA: D-form of (X Y)^T = Y^T X^T, i.e. operand a = Y tile read
 // column-wise (LDS transpose read) and operand b = X tile read row-wise, which gives Z
 // in T-form directly.  Both operands come from bf16 copies of the tile matrices in LDS
-// (row-major 16x16 tiles); a matrix changes only between barriers.  In the doubling
+// (16x16 tiles, rows XOR-swizzled in 8-byte chunks); a matrix changes only between
+// barriers.  In the doubling
 // product A^(2^q) vanishes on subdiagonals below 2^q, and the tiles that lie entirely
 // there are skipped.
 #include "gdn_kernels.hpp"
@@ -49,23 +50,26 @@ struct alignas(16) LTiles {
   __bf16 t[NT * (NT + 1) / 2][16][16];
 };
 
+// Each tile row holds four 8-byte chunks; chunk q of row r sits at chunk position
+// q ^ (r / 4) (rows r and r + 4 would otherwise start on the same banks).
 // lane (g,c): M(I,J)[c][4g .. 4g+3]
 template <int NT>
 __device__ __forceinline__ bf16x4 rowfrag(const LTiles<NT>& M, int I, int J) {
   const int l = lane_id(), g = l >> 4, c = l & 15;
-  return *reinterpret_cast<const bf16x4*>(&M.t[tri_idx(I, J)][c][4 * g]);
+  return *reinterpret_cast<const bf16x4*>(&M.t[tri_idx(I, J)][c][4 * (g ^ (c >> 2))]);
 }
-// lane (g,c): M(I,J)[4g .. 4g+3][c] (transpose read)
+// lane (g,c): M(I,J)[4g .. 4g+3][c] (transpose read; lane (g, j) addresses row
+// 4g + j / 4, chunk j % 4)
 template <int NT>
 __device__ __forceinline__ bf16x4 colfrag(const LTiles<NT>& M, int I, int J) {
   const int l = lane_id(), g = l >> 4, j = l & 15;
-  return lds_read_tr4(&M.t[tri_idx(I, J)][4 * g + (j >> 2)][4 * (j & 3)]);
+  return lds_read_tr4(&M.t[tri_idx(I, J)][4 * g + (j >> 2)][4 * ((j & 3) ^ g)]);
 }
 // store a T-form tile
 template <int NT>
 __device__ __forceinline__ void put_tile(LTiles<NT>& M, int I, int J, const f32x4& v) {
   const int l = lane_id(), g = l >> 4, c = l & 15;
-  *reinterpret_cast<bf16x4*>(&M.t[tri_idx(I, J)][c][4 * g]) = pack4(v);
+  *reinterpret_cast<bf16x4*>(&M.t[tri_idx(I, J)][c][4 * (g ^ (c >> 2))]) = pack4(v);
 }
 
 // the two tile rows a wave owns: row I0 = w (at most NT/2 tiles), row I1 = NT-1-w
