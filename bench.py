@@ -5,16 +5,20 @@ seq 8192 -> 2048 blocks, bf16 keys (d_k = 128), fp32 beta and log-gates, A built
 the kernel, T = band-masked truncated Neumann sum with N = 3 (the pages' method),
 T written as fp32.  value = 64x64 blocks per second.
 
-The same JSON line also carries the other inverse variants of that workload and, when
-the library has it, the full chunk-wise prefill forward (B=4, H=16, seq 8192,
-d_k = d_v = 128, C = 64) in tokens per second, each with its roofline.
+The same JSON line also carries the other inverse variants of that workload, the
+chunk-wise prefill forward (B=4, H=16, seq 8192, d_k = d_v = 128, C = 64) in tokens per
+second with its roofline, the forward-substitution comparison, the decode step, the WY
+chunk-size sweep, the fp8 prefill at seq 32768, the oracle's CPU baseline and the
+accuracy report.
 
 Inputs are seeded synthetic tensors (see synth/), resident in HBM before timing.
 Eight input/output buffer sets are rotated so that successive launches do not hit
 the 256 MB Infinity Cache.  Kernel durations come from HIP events recorded on the
 stream the kernels are launched on.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only c1|c3]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+                       [--only all|c3|fs|decode|c2|c4] [--profile-launches n --only LEG]
+(the headline always runs; --only limits the other legs)
 """
 from __future__ import annotations
 
