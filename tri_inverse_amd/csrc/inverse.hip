@@ -34,10 +34,10 @@ struct BlockIn<NT, SRC_K_BF16, DK> {
   // (the chunk forward's pre-pass) streaming loads fetched lines twice (1.12-1.15x the
   // key bytes) and plain loads are faster (bf16 products pre-pass 40 -> 34 us at 8192
   // blocks), while the 2048-block inverses read exactly their bytes either way.
-  template <bool GF = false, bool STREAM = true>
+  template <bool GF = false, bool STREAM = true, bool ORDERED = false>
   __device__ __forceinline__ void load(const BlocksArgs& a, int64_t blk) {
     constexpr int C = 16 * NT;
-    load_kblock<NT, DK, STREAM, GF>(reinterpret_cast<const __bf16*>(a.K) + (size_t)blk * C * DK,
+    load_kblock<NT, DK, STREAM, GF, ORDERED>(reinterpret_cast<const __bf16*>(a.K) + (size_t)blk * C * DK,
                                   a.beta + (size_t)blk * C, a.g + (size_t)blk * C, k);
   }
   template <int MAXD, bool BANDED, bool GF = false>
@@ -53,7 +53,7 @@ struct BlockIn<NT, SRC_K_BF16, DK> {
 template <int NT, int DK>
 struct BlockIn<NT, SRC_A, DK> {
   ABlock<NT> ab;
-  template <bool GF = false, bool STREAM = true>
+  template <bool GF = false, bool STREAM = true, bool ORDERED = false>
   __device__ __forceinline__ void load(const BlocksArgs& a, int64_t blk) {
     constexpr int C = 16 * NT;
     load_ablock<NT>(a.A + (size_t)blk * C * C, ab);
@@ -134,6 +134,44 @@ __device__ __forceinline__ void inverse_block(const BlocksArgs& a, int64_t blk, 
   }
 }
 
+// The band-masked sum with N = 2 or 3 of a 64 x 64 block from bf16 keys, T in bf16, in
+// two halves of rows.  With the mask (N <= 16) A, every Horner iterate and T reach one
+// tile-diagonal below the main one, so their tile rows 0-1 need only the key rows 0-31:
+// that half is formed and its T rows stored while the key rows 32-63 still arrive (the
+// gate inputs and the keys load in that order, and loads complete in order).  Rows 2-3
+// follow and read the first half's tile row 1 of each iterate.  Every tile is formed by
+// the same MFMAs on the same operands as in neumann_T, so T is bit-identical.
+template <int DK>
+__device__ __forceinline__ void neumann_rows_in_halves(const BlocksArgs& a, int64_t blk,
+                                                       const BlockIn<4, SRC_K_BF16, DK>& in, int N,
+                                                       void* T_out) {
+  constexpr int C = 64, MAXD = 1;
+  Gates<4> gt;
+  gates_from_lanes<4>(in.k.gl, in.k.bl, a.g_cumulative != 0, gt);
+  Mat<4> S, AD, AT, H1, H2, TT;
+  const f32x4 eye = eye_tile();
+  auto half = [&](auto lo) {
+    constexpr int ILO = decltype(lo)::value, IHI = ILO + 1;
+    gram_from_frags<4, DK, MAXD, ILO, IHI>(in.k, S);
+    gram_to_A<4, MAXD, false, ILO, IHI>(S, gt, -1, AD, AT);
+#pragma unroll
+    for (int I = ILO; I <= IHI; ++I)
+#pragma unroll
+      for (int J = 0; J <= I; ++J) H1.t[I][J] = (I == J) ? AD.t[I][J] + eye : AD.t[I][J];  // H_1 = I + A
+    if (N == 3) {
+      lmul_bf16<4, false, MAXD, true, ILO, IHI>(AT, H1, H2);  // H_2 = I + A H_1
+      lmul_bf16<4, true, MAXD, true, ILO, IHI>(AT, H2, TT);   // T = I + A H_2
+    } else {
+      lmul_bf16<4, true, MAXD, true, ILO, IHI>(AT, H1, TT);   // T = I + A H_1
+    }
+    mask_T<4, ILO, IHI>(TT, N);
+    store_T_rows_bf16<4, MAXD, ILO, IHI>(reinterpret_cast<__bf16*>(T_out) + (size_t)blk * C * C, TT);
+  };
+  half(std::integral_constant<int, 0>{});
+  __builtin_amdgcn_sched_barrier(0);  // keep the second half's work behind the first's stores
+  half(std::integral_constant<int, 2>{});
+}
+
 // The batched inverse.  PF = false: one wave per block.  PF = true: fewer waves than
 // blocks, each walking the blocks with the grid's stride; while it forms and stores T
 // of one block, the next block's raw inputs are already on their way into registers
@@ -150,6 +188,16 @@ __global__ __launch_bounds__(256) void inverse_kernel(BlocksArgs a, int N, int m
     const int64_t blk = (int64_t)blockIdx.x * (blockDim.x / WAVE) + (threadIdx.x / WAVE);
     if (blk >= a.n_blocks) return;
     BlockIn<NT, SRC, DK> in;
+    if constexpr (NT == 4 && SRC == SRC_K_BF16 && CMP == CMP_BF16 && MODE == MODE_NEUMANN && MAXD == 1 && !PK) {
+      // bf16 T only: with fp32 T (twice the store bytes) the first half's stores, mixed
+      // into the second half's key reads, made the launch slower (13.2 -> 14.2 us),
+      // while bf16 T gained (12.7 -> 12.2 us)
+      if ((N == 2 || N == 3) && t_bf16) {
+        in.template load<true, true, true>(a, blk);
+        neumann_rows_in_halves<DK>(a, blk, in, N, T_out);
+        return;
+      }
+    }
     in.template load<gates_first<CMP, MODE>(), !PK>(a, blk);
     inverse_block<NT, SRC, DK, CMP, MODE, MAXD, PK>(a, blk, in, N, mask, T_out, t_bf16, cnt, count, S,
                                                     threadIdx.x / WAVE);

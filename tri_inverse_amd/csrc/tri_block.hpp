@@ -158,7 +158,9 @@ struct KBlock {
 
 // GATES_FIRST: the gate inputs are loaded before the key rows (loads complete in order),
 // so the gate factors can be formed while the keys are still arriving
-template <int NT, int DK, bool NT_LOAD = false, bool GATES_FIRST = false>
+// ORDERED: the loads are issued in program order (gates, then key row tile 0, 1, ...),
+// for a consumer that starts on the first row tiles while the rest still arrive
+template <int NT, int DK, bool NT_LOAD = false, bool GATES_FIRST = false, bool ORDERED = false>
 __device__ __forceinline__ void load_kblock(const __bf16* __restrict__ K,
                                             const float* __restrict__ beta,
                                             const float* __restrict__ g, KBlock<NT, DK>& kb) {
@@ -167,9 +169,10 @@ __device__ __forceinline__ void load_kblock(const __bf16* __restrict__ K,
   if constexpr (GATES_FIRST) {
     kb.gl = (l < C) ? g[l] : 0.f;
     kb.bl = (l < C) ? beta[l] : 0.f;
+    if constexpr (ORDERED) __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
-  for (int I = 0; I < NT; ++I)
+  for (int I = 0; I < NT; ++I) {
 #pragma unroll
     for (int s = 0; s < DK / 32; ++s)
       {
@@ -177,6 +180,8 @@ __device__ __forceinline__ void load_kblock(const __bf16* __restrict__ K,
         // streaming (non-temporal) when nothing reads these rows again
         kb.kf[I][s] = NT_LOAD ? __builtin_nontemporal_load(src) : *src;
       }
+    if constexpr (ORDERED) __builtin_amdgcn_sched_barrier(0);
+  }
   if constexpr (!GATES_FIRST) {
     kb.gl = (l < C) ? g[l] : 0.f;
     kb.bl = (l < C) ? beta[l] : 0.f;
@@ -191,17 +196,21 @@ __device__ __forceinline__ void gates_from_lanes(float gl, float bl, bool g_cumu
   gather_gates<NT>(Gl, bl, gt);
 }
 
-// Gram tiles from preloaded fragments (D-form), only tiles with |I - J| <= MAXD
-template <int NT, int DK, int MAXD = NT - 1>
+// Gram tiles from preloaded fragments (D-form), only tiles with |I - J| <= MAXD, and of
+// those only the ones A's rows ILO .. IHI are formed from
+template <int NT, int DK, int MAXD = NT - 1, int ILO = 0, int IHI = NT - 1>
 __device__ __forceinline__ void gram_from_frags(const KBlock<NT, DK>& kb, Mat<NT>& S) {
+  constexpr bool ALL = ILO == 0 && IHI == NT - 1;
 #pragma unroll
   for (int I = 0; I < NT; ++I)
 #pragma unroll
     for (int J = 0; J < NT; ++J) {
       if (I - J > MAXD || J - I > MAXD) {
-        S.t[I][J] = zero4();
+        if constexpr (ALL) S.t[I][J] = zero4();
         continue;
       }
+      const int row = I > J ? I : J;  // tile (I, J) and its mirror serve A's row `row`
+      if (row < ILO || row > IHI) continue;
       f32x4 acc = zero4();
 #pragma unroll
       for (int s = 0; s < DK / 32; ++s) acc = mma_bf16(kb.kf[I][s], kb.kf[J][s], acc);
@@ -344,14 +353,14 @@ __device__ __forceinline__ void gram_band3(const bf16x8 (&kf)[NT][DK / 32], floa
 // the band mask (keep i - j <= band, band < 0 = none) is applied too.  The gate factor
 // is split as exp(G_i - G_j) = exp(G_i) exp(-G_j) when every exp(-G) of the block is
 // finite (G >= -80); otherwise each element takes exp of the difference.
-template <int NT, int MAXD = NT - 1, bool BANDED = false>
+template <int NT, int MAXD = NT - 1, bool BANDED = false, int ILO = 0, int IHI = NT - 1>
 __device__ __forceinline__ void gram_to_A(const Mat<NT>& S, const Gates<NT>& gt, int band,
                                           Mat<NT>& AD, Mat<NT>& AT) {
   const int hi = band < 0 ? (1 << 30) : band;
   const bool split = gt.split;
   const int lane = lane_id(), grp = lane >> 4, cl = lane & 15;
 #pragma unroll
-  for (int I = 0; I < NT; ++I)
+  for (int I = ILO; I <= IHI; ++I)
 #pragma unroll
     for (int J = 0; J <= I; ++J) {
       if (I - J > MAXD || (BANDED && 16 * (I - J) - 15 > hi)) {  // tile outside (uniform)
@@ -403,10 +412,10 @@ __device__ __forceinline__ void mask_D(Mat<NT>& M, int band) {
       M.t[I][J] = band_select_D<NT>(M.t[I][J], I - J, -(1 << 30), band);
     }
 }
-template <int NT>
+template <int NT, int ILO = 0, int IHI = NT - 1>
 __device__ __forceinline__ void mask_T(Mat<NT>& M, int band) {
 #pragma unroll
-  for (int I = 0; I < NT; ++I)
+  for (int I = ILO; I <= IHI; ++I)
 #pragma unroll
     for (int J = 0; J <= I; ++J) {
       if (16 * (I - J) + 15 <= band) continue;
@@ -438,7 +447,7 @@ __device__ __forceinline__ f32x4 tile_init(int I, int J, bool eye) {
   return (eye && I == J) ? eye_tile() : zero4();
 }
 
-template <int NT, bool TFORM, int MAXD, bool EYE>
+template <int NT, bool TFORM, int MAXD, bool EYE, int ILO = 0, int IHI = NT - 1>
 __device__ __forceinline__ void lmul_bf16(const Mat<NT>& XT, const Mat<NT>& YD, Mat<NT>& Z) {
   constexpr int NP = (NT + 1) / 2;
   bf16x8 rp[NT][NP], cp[NP][NT];
@@ -454,8 +463,9 @@ __device__ __forceinline__ void lmul_bf16(const Mat<NT>& XT, const Mat<NT>& YD, 
     for (int J = 0; J < NT; ++J)
       if (J <= 2 * p + 1 && 2 * p - J <= MAXD)
         cp[p][J] = pack8(tile_or_zero(YD, 2 * p, J), tile_or_zero(YD, 2 * p + 1, J));
+  // output rows ILO .. IHI only (the packs no such row reads are never formed)
 #pragma unroll
-  for (int I = 0; I < NT; ++I)
+  for (int I = ILO; I <= IHI; ++I)
 #pragma unroll
     for (int J = 0; J <= I; ++J) {
       if (I - J > MAXD) {
@@ -1278,12 +1288,12 @@ __device__ __forceinline__ f32x4 tile_kept(const Mat<NT>& M, int I, int J) {
 }
 
 // fp32: tile pairs through store_rows_f32x2 (a pair is 128 bytes of a row)
-template <int NT, int MAXD>
+template <int NT, int MAXD, int ILO = 0, int IHI = NT - 1>
 __device__ __forceinline__ void store_T_rows_f32(float* __restrict__ out, const Mat<NT>& M) {
   static_assert(NT == 2 || NT == 4, "32 x 32 or 64 x 64 blocks");
   constexpr int C = 16 * NT;
 #pragma unroll
-  for (int I = 0; I < NT; ++I)
+  for (int I = ILO; I <= IHI; ++I)
 #pragma unroll
     for (int J = 0; J < NT; J += 2)
       store_rows_f32x2<true>(out + (size_t)16 * I * C + 16 * J, C, tile_kept<NT, MAXD>(M, I, J),
@@ -1292,13 +1302,13 @@ __device__ __forceinline__ void store_T_rows_f32(float* __restrict__ out, const 
 
 // bf16: at C = 64 four tiles through store_rows_bf16x4; at C = 32 a row is 64 bytes and
 // one tile pair through store_pair_bf16 writes 16 contiguous rows
-template <int NT, int MAXD>
+template <int NT, int MAXD, int ILO = 0, int IHI = NT - 1>
 __device__ __forceinline__ void store_T_rows_bf16(__bf16* __restrict__ out, const Mat<NT>& M) {
   static_assert(NT == 2 || NT == 4, "32 x 32 or 64 x 64 blocks");
   constexpr int C = 16 * NT;
   const int c = lane_id() & 15;
 #pragma unroll
-  for (int I = 0; I < NT; ++I) {
+  for (int I = ILO; I <= IHI; ++I) {
     if constexpr (NT == 4) {
       const f32x4 t[4] = {tile_kept<NT, MAXD>(M, I, 0), tile_kept<NT, MAXD>(M, I, 1),
                           tile_kept<NT, MAXD>(M, I, 2), tile_kept<NT, MAXD>(M, I, 3)};
