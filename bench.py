@@ -66,14 +66,19 @@ def load_traffic(kernel_key: str):
     return ent.get("hbm_bytes_per_launch")
 
 
-def time_launches(torch, launch, n_sets, steps, warmup, repeats=7):
+_GPU_WARM = [False]
+
+
+def time_launches(torch, launch, n_sets, steps, warmup, repeats=7, warm_ms=20.0):
     """Run `launch(set_index)` `warmup` times eagerly, then capture exactly `steps`
-    launches (rotating buffer sets) in one HIP graph.  The graph is replayed once
-    untimed, then `repeats` times, each replay timed on its own with HIP events on the
-    replay stream (each timed region holds exactly `steps` launches).  Returns the
-    median ms per launch and the list of all repeats.  Replaying a graph keeps Python's
-    per-call overhead out of the timed region, so back-to-back kernels run without
-    host-induced gaps; the median of several replays keeps clock ramps and one-off
+    launches (rotating buffer sets) in one HIP graph.  The graph is replayed untimed for
+    at least `warm_ms` milliseconds (the first leg of a process: 500 ms, because for the
+    first few milliseconds of sustained load the GPU's clocks are still settling and a
+    replay drifted by up to 10 %), then `repeats` times, each replay timed on its own
+    with HIP events on the replay stream (each timed region holds exactly `steps`
+    launches).  Returns the median ms per launch and the list of all repeats.  Replaying
+    a graph keeps Python's per-call overhead out of the timed region, so back-to-back
+    kernels run without host-induced gaps; the median of several replays keeps one-off
     stalls out of the figure."""
     for i in range(warmup):
         launch(i % n_sets)
@@ -82,8 +87,15 @@ def time_launches(torch, launch, n_sets, steps, warmup, repeats=7):
     with torch.cuda.graph(graph):
         for k in range(steps):
             launch(k % n_sets)
-    graph.replay()  # untimed: first replay uploads the graph
-    torch.cuda.synchronize()
+    if not _GPU_WARM[0]:
+        warm_ms = max(warm_ms, 500.0)
+        _GPU_WARM[0] = True
+    t_end = time.perf_counter() + warm_ms * 1e-3
+    while True:  # untimed; the first replay also uploads the graph
+        graph.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() >= t_end:
+            break
     stream = torch.cuda.current_stream()
     per = []
     for _ in range(repeats):
