@@ -198,7 +198,12 @@ __global__ __launch_bounds__(256) void inverse_kernel(BlocksArgs a, int N, int m
         return;
       }
     }
-    in.template load<gates_first<CMP, MODE>(), !PK>(a, blk);
+    // loads issued in program order (gates as gates_first says, then key row tiles 0..3),
+    // so the Gram products of the first row tiles start while the last ones arrive; the
+    // compiler's own interleaving of the loads made most of them wait for nearly all
+    // keys.  Measured 3-9 % faster on the 2048-block inverses and 3-4 % on the chunk
+    // forward's pre-passes.
+    in.template load<gates_first<CMP, MODE>(), !PK, true>(a, blk);
     inverse_block<NT, SRC, DK, CMP, MODE, MAXD, PK>(a, blk, in, N, mask, T_out, t_bf16, cnt, count, S,
                                                     threadIdx.x / WAVE);
   } else {
