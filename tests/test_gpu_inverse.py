@@ -248,6 +248,24 @@ def test_bf16_output_is_the_rounded_fp32_output(N, strong):
     assert torch.equal(T16, T32.to(torch.bfloat16))
 
 
+@pytest.mark.parametrize("dk", [64, 128])
+@pytest.mark.parametrize("strong", [False, True])
+def test_exact_bf16_output_is_the_rounded_fp32_output(dk, strong):
+    """Exact doubling from bf16 keys: T in bf16 (formed in two halves of rows, the first
+    stored while the second half's keys still arrive, the second reading the first
+    half's rows of every square) must be exactly the bf16 rounding of T in fp32 (formed
+    in one piece); ordinary gates and gates that force the exponential-of-difference
+    form; 3000 blocks, so the grid ends in a part-filled workgroup."""
+    say(f"exact bf16 vs fp32 output dk={dk} strong={strong}")
+    inp = synth.blocks(9, 3000, 64, dk, k_dtype="bf16")
+    g = inp["g"] * 4.0 - 1.0 if strong else inp["g"]
+    K, beta, gg = cuda(inp["K"]), cuda(inp["beta"]), cuda(g)
+    T32 = tri.gdn_tri_inverse_exact(K=K, beta=beta, g=gg, C=64, t_dtype=torch.float32)
+    T16 = tri.gdn_tri_inverse_exact(K=K, beta=beta, g=gg, C=64, t_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(T16, T32.to(torch.bfloat16))
+
+
 def test_empty_batch_is_a_noop():
     K = torch.zeros(0, 64, 128, dtype=torch.bfloat16, device="cuda")
     b = torch.zeros(0, 64, device="cuda")
