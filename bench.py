@@ -653,7 +653,7 @@ def main():
         return
     c1 = bench_c1(torch, tri, synth, args.steps, args.warmup)
     head = c1["N3_masked_Tf32"]
-    traffic = load_traffic("inverse_kernel<4,1,128,1,0,1,false,false>")
+    traffic = load_traffic("inverse_kernel<4,1,128,1,0,1,false,false,2>")
     roofline = {
         "bound": "hbm",
         "achieved": head["bytes"] / (head["ms_kernel"] * 1e-3) / 1e9,

@@ -94,7 +94,7 @@ constexpr bool gates_first() {
 // The inverse of one block by the current wave.  MAXD is the largest tile distance
 // I - J kept (NT - 1 in general, 1 for the band-masked sum with N <= 16).
 // PK: write T - I as the chunk forward's row packs (store_T_packs) instead of T.
-template <int NT, int SRC, int DK, int CMP, int MODE, int MAXD, bool PK>
+template <int NT, int SRC, int DK, int CMP, int MODE, int MAXD, bool PK, int WPG>
 __device__ __forceinline__ void inverse_block(const BlocksArgs& a, int64_t blk, const BlockIn<NT, SRC, DK>& in,
                                               int N, int mask, void* T_out, int t_bf16, Fp8Counts& cnt,
                                               bool count, int S, int wave) {
@@ -106,7 +106,7 @@ __device__ __forceinline__ void inverse_block(const BlocksArgs& a, int64_t blk, 
   Mat<NT> AD, AT, TT;
   in.template to_A<MAXD, BANDED, gates_first<CMP, MODE>()>(a, BANDED ? band : -1, AD, AT);
   if constexpr (MODE == MODE_EXACT && NT == 4 && CMP == CMP_BF16) {
-    __shared__ __bf16 xt[4][64][XT_LD];  // per wave: X^T for the transpose read
+    __shared__ __bf16 xt[WPG][64][XT_LD];  // per wave: X^T for the transpose read
     doubling_T_lds(AD, AT, TT, xt[wave]);
   } else if constexpr (MODE == MODE_EXACT)
     doubling_T<NT, CMP>(AD, AT, TT);
@@ -172,20 +172,21 @@ __device__ __forceinline__ void neumann_rows_in_halves(const BlocksArgs& a, int6
   half(std::integral_constant<int, 2>{});
 }
 
-// The batched inverse.  PF = false: one wave per block.  PF = true: fewer waves than
+// The batched inverse.  WPG: waves per workgroup (the launch's block size, 2 or 4).
+// PF = false: one wave per block.  PF = true: fewer waves than
 // blocks, each walking the blocks with the grid's stride; while it forms and stores T
 // of one block, the next block's raw inputs are already on their way into registers
 // (the index is clamped, so the load is unconditional and the wait before the next
 // block covers only those loads).  That overlap pays where the per-block work is long
 // next to its loads (the unmasked fp8 chain over many blocks); with fewer blocks or
 // lighter work, independent waves hide the loads better, so PF stays off there.
-template <int NT, int SRC, int DK, int CMP, int MODE, int MAXD, bool PK = false, bool PF = false>
+template <int NT, int SRC, int DK, int CMP, int MODE, int MAXD, bool PK = false, bool PF = false, int WPG = 4>
 __global__ __launch_bounds__(256) void inverse_kernel(BlocksArgs a, int N, int mask, void* T_out,
                                                       int t_bf16, unsigned long long* stats, int S) {
   Fp8Counts cnt{0, 0, 0, 0};
   const bool count = (CMP == CMP_FP8) && stats != nullptr;
   if constexpr (!PF) {
-    const int64_t blk = (int64_t)blockIdx.x * (blockDim.x / WAVE) + (threadIdx.x / WAVE);
+    const int64_t blk = (int64_t)blockIdx.x * WPG + (threadIdx.x / WAVE);
     if (blk >= a.n_blocks) return;
     BlockIn<NT, SRC, DK> in;
     if constexpr (NT == 4 && SRC == SRC_K_BF16 && CMP == CMP_BF16 && MODE == MODE_NEUMANN && MAXD == 1 && !PK) {
@@ -204,19 +205,19 @@ __global__ __launch_bounds__(256) void inverse_kernel(BlocksArgs a, int N, int m
     // keys.  Measured 3-9 % faster on the 2048-block inverses and 3-4 % on the chunk
     // forward's pre-passes.
     in.template load<gates_first<CMP, MODE>(), !PK, true>(a, blk);
-    inverse_block<NT, SRC, DK, CMP, MODE, MAXD, PK>(a, blk, in, N, mask, T_out, t_bf16, cnt, count, S,
-                                                    threadIdx.x / WAVE);
+    inverse_block<NT, SRC, DK, CMP, MODE, MAXD, PK, WPG>(a, blk, in, N, mask, T_out, t_bf16, cnt, count, S,
+                                                         threadIdx.x / WAVE);
   } else {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
-    const int64_t first = (int64_t)blockIdx.x * (blockDim.x / WAVE) + wave;
+    const int64_t first = (int64_t)blockIdx.x * WPG + wave;
     if (first >= a.n_blocks) return;
-    const int64_t stride = (int64_t)gridDim.x * (blockDim.x / WAVE);
+    const int64_t stride = (int64_t)gridDim.x * WPG;
     BlockIn<NT, SRC, DK> in;
     in.template load<gates_first<CMP, MODE>(), !PK>(a, first);
     for (int64_t blk = first; blk < a.n_blocks; blk += stride) {
       BlockIn<NT, SRC, DK> nxt;
       nxt.template load<gates_first<CMP, MODE>(), !PK>(a, blk + stride < a.n_blocks ? blk + stride : a.n_blocks - 1);
-      inverse_block<NT, SRC, DK, CMP, MODE, MAXD, PK>(a, blk, in, N, mask, T_out, t_bf16, cnt, count, S, wave);
+      inverse_block<NT, SRC, DK, CMP, MODE, MAXD, PK, WPG>(a, blk, in, N, mask, T_out, t_bf16, cnt, count, S, wave);
       in = nxt;
     }
   }
@@ -276,8 +277,32 @@ __global__ void zero_u64_kernel(unsigned long long* p, int n) {
 
 static constexpr int WAVES_PER_WG = 4;
 
-static dim3 grid_for(int64_t n_blocks) {
-  return dim3((unsigned)((n_blocks + WAVES_PER_WG - 1) / WAVES_PER_WG));
+static dim3 grid_for(int64_t n_blocks, int wpg = WAVES_PER_WG) {
+  return dim3((unsigned)((n_blocks + wpg - 1) / wpg));
+}
+
+// One launch of the batched inverse (T out, one wave per block).  The truncated sums on
+// blocks of 32 x 32 and 64 x 64 go two waves to a workgroup: twice as many workgroups
+// spread over the CUs more evenly.  Same-box A/Bs over 2048 blocks of 64 x 64, two boxes:
+// unmasked N = 3 12.41-12.61 -> 11.98-12.20 us, int8 12.9 -> 12.4 us, int16 17.45 ->
+// 16.9 us, masked N = 3 with T fp32 12.26-12.31 -> 11.86-12.32 us (a gain on one box,
+// level on the other).  The exact product (T bf16 11.24 -> 11.64 us on one box), the
+// residual correction (level) and the masked sum with bf16 T in two halves of rows
+// (11.28-11.33 against 11.43 us) keep four waves.
+template <int NT, int SRC, int DK, int CMP, int MODE, int MAXD>
+static void launch_inverse(const BlocksArgs& a, int N, int mask, void* T_out, int t_bf16,
+                           unsigned long long* stats, int S, hipStream_t s) {
+  const bool halves = NT == 4 && SRC == SRC_K_BF16 && CMP == CMP_BF16 && MODE == MODE_NEUMANN && MAXD == 1 &&
+                      t_bf16 && (N == 2 || N == 3);
+  if constexpr (NT >= 2 && MODE == MODE_NEUMANN) {
+    if (!halves) {
+      hipLaunchKernelGGL((inverse_kernel<NT, SRC, DK, CMP, MODE, MAXD, false, false, 2>), grid_for(a.n_blocks, 2),
+                         dim3(WAVE * 2), 0, s, a, N, mask, T_out, t_bf16, stats, S);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((inverse_kernel<NT, SRC, DK, CMP, MODE, MAXD>), grid_for(a.n_blocks),
+                     dim3(WAVE * WAVES_PER_WG), 0, s, a, N, mask, T_out, t_bf16, stats, S);
 }
 
 // Waves of the persistent fp8 pre-pass: two per SIMD of the 256 CUs.  It is used for the
@@ -357,13 +382,10 @@ int launch_neumann(const BlocksArgs& a, int src, int N, int mask, int cmp, void*
       constexpr int NTv = nt.value;
       // band-masked with N <= 16: tiles two or more tile-diagonals down stay zero
       if (mask && N <= 16 && NTv > 2) {
-        hipLaunchKernelGGL((inverse_kernel<NTv, sc.value, dk.value, cm.value, MODE_NEUMANN, 1>),
-                           grid_for(a.n_blocks), dim3(WAVE * WAVES_PER_WG), 0, s, a, N, mask,
-                           T_out, t_bf16, stats, 0);
+        launch_inverse<NTv, sc.value, dk.value, cm.value, MODE_NEUMANN, 1>(a, N, mask, T_out, t_bf16, stats, 0, s);
       } else {
-        hipLaunchKernelGGL((inverse_kernel<NTv, sc.value, dk.value, cm.value, MODE_NEUMANN, NTv - 1>),
-                           grid_for(a.n_blocks), dim3(WAVE * WAVES_PER_WG), 0, s, a, N, mask,
-                           T_out, t_bf16, stats, 0);
+        launch_inverse<NTv, sc.value, dk.value, cm.value, MODE_NEUMANN, NTv - 1>(a, N, mask, T_out, t_bf16, stats,
+                                                                                 0, s);
       }
       return 0;
     };
@@ -381,10 +403,8 @@ int launch_neumann(const BlocksArgs& a, int src, int N, int mask, int cmp, void*
 int launch_exact(const BlocksArgs& a, int src, int cmp, void* T_out, int t_bf16, hipStream_t s) {
   return dispatch_nt_src_dk(a.C, src, a.d_k, [&](auto nt, auto sc, auto dk) -> int {
     auto go = [&](auto cm) {
-      hipLaunchKernelGGL((inverse_kernel<nt.value, sc.value, dk.value, cm.value, MODE_EXACT,
-                                         nt.value - 1>),
-                         grid_for(a.n_blocks), dim3(WAVE * WAVES_PER_WG), 0, s, a, 0, 0,
-                         T_out, t_bf16, (unsigned long long*)nullptr, 0);
+      launch_inverse<nt.value, sc.value, dk.value, cm.value, MODE_EXACT, nt.value - 1>(
+          a, 0, 0, T_out, t_bf16, (unsigned long long*)nullptr, 0, s);
       return 0;
     };
     switch (cmp) {
@@ -440,9 +460,8 @@ int launch_T_packs(const BlocksArgs& a, int mode, int N, int mask, int cmp, void
 int launch_residual(const BlocksArgs& a, int src, int N, int mask, int S, void* T_out, int t_bf16,
                     hipStream_t s) {
   return dispatch_nt_src_dk(a.C, src, a.d_k, [&](auto nt, auto sc, auto dk) -> int {
-    hipLaunchKernelGGL((inverse_kernel<nt.value, sc.value, dk.value, CMP_F32, MODE_RESIDUAL, nt.value - 1>),
-                       grid_for(a.n_blocks), dim3(WAVE * WAVES_PER_WG), 0, s, a, N, mask, T_out, t_bf16,
-                       (unsigned long long*)nullptr, S);
+    launch_inverse<nt.value, sc.value, dk.value, CMP_F32, MODE_RESIDUAL, nt.value - 1>(
+        a, N, mask, T_out, t_bf16, (unsigned long long*)nullptr, S, s);
     return 0;
   });
 }
