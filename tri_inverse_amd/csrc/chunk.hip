@@ -24,8 +24,8 @@
 //               They hand S^T (bf16) and U' (hi/lo) to the output waves.
 //   waves 2, 3, 6, 7  output waves for row tiles 0, 1, 2, 3, one chunk behind: P and
 //               O = scale (e^G Q S + P U') for their 16 rows, all 32 columns.  Tiles 0
-//               and 2 share one SIMD, tiles 1 and 3 another (equal shares of the
-//               triangular P).
+//               and 2 share one SIMD, tiles 1 and 3 another (measured as fast as the
+//               pairing 0 and 3, 1 and 2, which evens the two SIMDs' MFMA counts).
 //   wave 5      T - I of the next chunk (beside state wave 1): formed here on the band
 //               path (N <= 3 with the mask, bf16); for the masked fp8 chain with N <= 3
 //               put together from the band rows of the fp8 band pre-pass; else streamed
