@@ -107,6 +107,52 @@ __device__ __forceinline__ void row_product(const LTiles<NT>& X, const LTiles<NT
   }
 }
 
+// The squarings X <- X X of the doubling product feed only the bf16 copy in LDS, so their
+// output tiles need not follow row ownership.  A tile (I, J) of a product of lower-
+// triangular tile matrices sums I - J + 1 tile products, so the owner pairs (w, NT-1-w)
+// carry from (NT/2)(NT/2 + 1) to NT/2 + NT(NT + 1)/2 of them: 81 to 137 at NT = 16, with
+// every barrier waiting for the heaviest.  The squarings are dealt out instead as row
+// halves (column tiles 0 .. NT/2-1, "left", and NT/2 .. NT-1, "right"), assigned by
+// longest-first greedy packing: at most 103 (NT = 16) and 31 (NT = 8) tile products per
+// wave for the unskipped squarings, against a mean of 102 and 30.
+template <int NT>
+__device__ __forceinline__ int sq_left_row(int w, int s) {  // -1: none
+  static constexpr int L8[4][3] = {{7, 1, -1}, {6, 2, -1}, {5, 0, -1}, {4, 3, -1}};
+  static constexpr int L16[8][3] = {{15, 0, -1}, {14, -1, -1}, {13, 4, -1}, {12, 5, -1},
+                                    {11, 2, -1}, {10, 6, -1}, {9, 3, 1},   {8, 7, -1}};
+  if constexpr (NT == 8) return L8[w][s];
+  else return L16[w][s];
+}
+template <int NT>
+__device__ __forceinline__ int sq_right_row(int w) {
+  static constexpr int R8[4] = {4, 5, 7, 6};
+  static constexpr int R16[8] = {8, 11, 9, 10, 14, 12, 15, 13};
+  if constexpr (NT == 8) return R8[w];
+  else return R16[w];
+}
+
+// wave w's share of X^2 (the tiles of A^(2n) that vanish skipped through d) into out
+template <int NT>
+__device__ __forceinline__ void square_share(const LTiles<NT>& X, LTiles<NT>& out, int w, int d) {
+  static_assert(NT == 8 || NT == 16, "C = 128 or 256");
+  auto half = [&](int I, auto j0) {
+    constexpr int J0 = decltype(j0)::value;
+    f32x4 z[NT / 2];
+    static_for<NT / 2>([&](auto jc) { z[decltype(jc)::value] = zero4(); });
+    row_product<NT, NT / 2, J0>(X, X, I, d, d, z);
+    static_for<NT / 2>([&](auto jc) {
+      constexpr int J = J0 + decltype(jc)::value;
+      if (J <= I) put_tile<NT>(out, I, J, z[J - J0]);
+    });
+  };
+  for (int s = 0; s < 3; ++s) {
+    const int I = sq_left_row<NT>(w, s);
+    if (I < 0) break;
+    half(I, std::integral_constant<int, 0>{});
+  }
+  half(sq_right_row<NT>(w), std::integral_constant<int, NT / 2>{});
+}
+
 // T = I + A on the owned rows
 template <int NT>
 __device__ __forceinline__ void init_eye_plus(const OwnRows<NT>& A, OwnRows<NT>& T, int I0, int I1,
@@ -265,25 +311,7 @@ __global__ __launch_bounds__(NT * WAVE / 2, 1) void dense_kernel(DenseArgs p) {
         // i.e. below tile-subdiagonal n / 16 (n a power of two)
         const int dprev = (1 << (q - 1)) / 16, dq = (1 << q) / 16;
         __syncthreads();  // X = A^(2^(q-1)) complete in *xb; *ob no longer read
-        {
-          f32x4 z[NT / 2];
-          static_for<NT / 2>([&](auto Jc) { z[decltype(Jc)::value] = zero4(); });
-          row_product<NT, NT / 2>(*xb, *xb, I0, dprev, dprev, z);
-          static_for<NT / 2>([&](auto Jc) {
-            constexpr int J = decltype(Jc)::value;
-            if (J <= I0) put_tile<NT>(*ob, I0, J, z[J]);
-          });
-        }
-        static_for<2>([&](auto hc) {  // the long row in two halves of NT/2 output tiles
-          constexpr int J0 = decltype(hc)::value * (NT / 2);
-          f32x4 z[NT / 2];
-          static_for<NT / 2>([&](auto jc) { z[decltype(jc)::value] = zero4(); });
-          row_product<NT, NT / 2, J0>(*xb, *xb, I1, dprev, dprev, z);
-          static_for<NT / 2>([&](auto jc) {
-            constexpr int J = J0 + decltype(jc)::value;
-            if (J <= I1) put_tile<NT>(*ob, I1, J, z[J - J0]);
-          });
-        });
+        square_share<NT>(*xb, *ob, w, dprev);
         __syncthreads();  // X^2 complete in *ob; the old X is dead
         for_owned<NT>(T, I0, I1, [&](int I, int J, f32x4& t) { put_tile<NT>(*xb, I, J, t); });  // P (old)
         __syncthreads();
