@@ -107,7 +107,7 @@ __device__ __forceinline__ void inverse_block(const BlocksArgs& a, int64_t blk, 
   in.template to_A<MAXD, BANDED, gates_first<CMP, MODE>()>(a, BANDED ? band : -1, AD, AT);
   if constexpr (MODE == MODE_EXACT && NT == 4 && CMP == CMP_BF16) {
     __shared__ __bf16 xt[WPG][64][XT_LD];  // per wave: X^T for the transpose read
-    doubling_T_lds(AD, AT, TT, xt[wave]);
+    doubling_T_lds<SRC == SRC_K_BF16>(AD, AT, TT, xt[wave]);
   } else if constexpr (MODE == MODE_EXACT)
     doubling_T<NT, CMP>(AD, AT, TT);
   else if constexpr (MODE == MODE_RESIDUAL)

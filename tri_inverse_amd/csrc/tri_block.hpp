@@ -1170,6 +1170,11 @@ __device__ __forceinline__ constexpr int tile_kmax(int I, int kl) { return I - k
 // smallest tile distance I - J at which A^d can be non-zero (entries only at i - j >= d)
 __device__ __forceinline__ constexpr int tile_dist(int d) { return d <= 15 ? 0 : (d - 15 + 15) / 16; }
 
+// AD_FROM_AT: A's column packs are not formed from AD (which the caller then need not
+// build, nor the Gram tiles below the diagonal that only AD reads) but read back from a
+// bf16 copy of A's rows through the same transpose read, as the squares' row packs are:
+// the column packs of A are the row packs of A^T.
+template <bool AD_FROM_AT = false>
 __device__ __forceinline__ void doubling_T_lds(const Mat<4>& AD, const Mat<4>& AT, Mat<4>& PT,
                                                __bf16 (*xt)[XT_LD]) {
   constexpr int NT = 4, NP = 2;
@@ -1179,10 +1184,30 @@ __device__ __forceinline__ void doubling_T_lds(const Mat<4>& AD, const Mat<4>& A
   for (int I = 0; I < NT; ++I)
 #pragma unroll
     for (int p = 0; p < NP; ++p) xr[I][p] = pack8(tile_or_zero(AT, I, 2 * p), tile_or_zero(AT, I, 2 * p + 1));
+  if constexpr (AD_FROM_AT) {
+    // A's rows 16I + c, columns 32p + 16h + 4g .. +3 into the scratch (every pack, the
+    // zero ones above the diagonal included), then A^T's row packs back transposed
 #pragma unroll
-  for (int p = 0; p < NP; ++p)
+    for (int I = 0; I < NT; ++I)
 #pragma unroll
-    for (int J = 0; J < NT; ++J) xc[p][J] = pack8(tile_or_zero(AD, 2 * p, J), tile_or_zero(AD, 2 * p + 1, J));
+      for (int p = 0; p < NP; ++p) {
+        const u32x4 w = __builtin_bit_cast(u32x4, xr[I][p]);
+        *reinterpret_cast<u32x2*>(&xt[16 * I + c][32 * p + 4 * g]) = u32x2{w[0], w[1]};
+        *reinterpret_cast<u32x2*>(&xt[16 * I + c][32 * p + 16 + 4 * g]) = u32x2{w[2], w[3]};
+      }
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int J = 0; J < NT; ++J) {
+        const __bf16* b0 = &xt[32 * p + 4 * g + (c >> 2)][16 * J + 4 * (c & 3)];
+        xc[p][J] = join8(lds_read_tr4(b0), lds_read_tr4(b0 + 16 * XT_LD));
+      }
+  } else {
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int J = 0; J < NT; ++J) xc[p][J] = pack8(tile_or_zero(AD, 2 * p, J), tile_or_zero(AD, 2 * p + 1, J));
+  }
   PT = AT;
   add_eye(PT);
 #pragma unroll
